@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Benchmark one scheduler step of paged-KV attention on one MI355X.
+
+A step is the whole hot path over one synthetic batch: ``paged_kv_append`` of
+the step's new K/V rows, then ``paged_attn_step`` (decode partitions, split
+reduce, prefill-chunk rows).  Inputs are resident in HBM before the timed
+region.  Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_7b]
+
+value = algorithmic KV bytes of the step (each distinct physical token row of
+K and V once, fp8 scales included) / wall time of a step, in GB/s (1e9 B/s).
+"""
+import argparse
+import hashlib
+import glob
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+METRIC = "paged decode attention: KV-read GB/s (% of HBM peak), batch-steps/s"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "paged_kv_cache_286_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs, if still current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, seconds):
+    """Time the CPU oracle on a bounded prefix of the step's sequences (single BLAS thread)."""
+    import numpy as np
+    import oracle
+    from paged_kv_cache_286_amd import workloads as W
+    from threadpoolctl import threadpool_limits
+    p, cfg = wl.plan, wl.cfg
+    per_tok = W.kv_bytes_per_token(cfg)
+    done, t_used, toks = [], 0.0, 0
+    with threadpool_limits(limits=1):
+        for i in range(p.num_seqs):
+            t0 = time.perf_counter()
+            oracle.paged_attention(wl.q, wl.k, wl.v, p.block_tables, p.context_lens, p.query_lens,
+                                   wl.scale, cfg.block_size, cfg.kv_dtype, cfg.q_dtype,
+                                   wl.k_scale, wl.v_scale, seqs=[i])
+            t_used += time.perf_counter() - t0
+            done.append(i)
+            toks += int(p.context_lens[i])
+            if t_used >= seconds:
+                break
+    gbs = toks * per_tok / t_used / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 numpy oracle, attention of the first {len(done)} of {p.num_seqs} "
+                      f"sequences ({toks} context tokens, {toks * per_tok} KV bytes) in "
+                      f"{t_used:.1f} s on 1 thread of {platform.processor() or platform.machine()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_7b")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="time the steps without per-kernel events")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the paged attention step here runs on a single "
+              "MI355X (no sharding or collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_cache_286_amd import pagedkv as pk          # raises if the library is not built
+    from paged_kv_cache_286_amd import workloads as W
+    from paged_kv_cache_286_amd.device import DeviceStep
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    log(f"generating workload {args.workload}")
+    t0 = time.time()
+    wl = W.generate(W.make_plan(args.workload))
+    p, cfg = wl.plan, wl.cfg
+    alg = W.algorithmic_kv_bytes(p)
+    log(f"generated in {time.time() - t0:.1f} s; uploading")
+    ds = DeviceStep(wl, "cuda:0")
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        ds.step(stream)
+    torch.cuda.synchronize()
+
+    if not args.no_kernel_timing:
+        pk.pkv_timing_enable(4 * args.steps + 64)
+    log(f"timing {args.steps} steps")
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        ds.step(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    kernels = {}
+    if not args.no_kernel_timing:
+        dropped = pk.pkv_timing_collect()
+        for kind in range(pk.PKV_KERNEL_KINDS):
+            ms, n = pk.pkv_timing_get(kind)
+            if n:
+                kernels[pk.pkv_kernel_name(kind)] = {"avg_us": round(1000 * ms / n, 3), "launches": n}
+        pk.pkv_timing_disable()
+        if dropped:
+            log(f"warning: {dropped} launches were not timed")
+
+    value = alg["unique"] / (ms_per_step / 1e3) / 1e9
+    roofline = None
+    dom = pk.pkv_kernel_name(pk.PKV_KERNEL_DECODE)
+    if dom in kernels:
+        achieved = alg["unique"] / (kernels[dom]["avg_us"] / 1e6) / 1e9
+        traffic = measured_traffic(args.workload, dom)
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic, "algorithmic_bytes_per_launch": alg["unique"]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f16": "f16", "bf16": "bf16", "fp8_e4m3": "fp8_e4m3"}[cfg.kv_dtype],
+        "data": "synthetic (seeded N(0,1) q/K/V, seeded block placement)",
+        "config": {
+            "workload": args.workload,
+            "description": cfg.description,
+            "num_seqs": p.num_seqs,
+            "query_rows": p.total_q_tokens,
+            "num_q_heads": cfg.num_q_heads,
+            "num_kv_heads": cfg.num_kv_heads,
+            "head_dim": cfg.head_dim,
+            "block_size": cfg.block_size,
+            "kv_dtype": cfg.kv_dtype,
+            "context_tokens": alg["logical_tokens"],
+            "algorithmic_kv_bytes": alg["unique"],
+            "appended_rows": int(len(wl.slot_mapping)),
+        },
+        "batch_steps_per_s": round(1000.0 / ms_per_step, 2),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: one scheduler step of attention over a
+ * paged KV cache on an AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes is defined on the page "Serving LLMs with vLLM:
+ * Continuous Batching and PagedAttention Explained":
+ *   - section "Blocks and Block Tables": the KV cache is cut into fixed-size
+ *     blocks in one shared physical pool; each sequence owns a block table that
+ *     lists the physical block holding each of its logical blocks, and the
+ *     blocks need not be neighbours;
+ *   - section "Growing During Decode": every decode step writes the new token's
+ *     key and value into the next slot of the sequence's last block
+ *     (paged_kv_append);
+ *   - section "Attention Over Scattered Blocks": attention reads each block
+ *     through the table from wherever it lies, and the result is ordinary
+ *     softmax attention of the query over the whole history (paged_attn_step);
+ *   - sections "Prefill Versus Decode" and "Chunked Prefill": one step mixes
+ *     decoding sequences (one query row each) with a chunk of a long prompt
+ *     (several query rows, causal within the history);
+ *   - section "Shared Prefixes": several tables may name the same physical
+ *     blocks; nothing here writes to them.
+ * The 8-bit KV cache ("Why a Second Kind of Engine", section "The memory that
+ * concurrency actually costs") is stored as OCP FP8 E4M3FN bytes with one
+ * float32 scale per (block, kv head).
+ *
+ * Conventions for every entry point
+ *   Pointers are DEVICE memory owned by the caller unless marked "host".
+ *   The library never allocates, frees or synchronises: it validates the host
+ *   arguments, enqueues kernels on `stream` (a hipStream_t; NULL = the null
+ *   stream) and returns.  Results are valid once the stream has passed the
+ *   work; the caller keeps every buffer alive until then.
+ *   Return value: a pkv_status (0 = PKV_OK).  Validation failures return before
+ *   anything is enqueued.  A failed launch returns PKV_ERR_HIP.  No exception or
+ *   abort crosses the ABI.
+ *   Device-resident metadata is the caller's contract and is not read back:
+ *   block ids in [0, num_blocks), context_lens[i] >= 1 and
+ *   <= max_blocks_per_seq * block_size, 1 <= query_lens[i] <= context_lens[i],
+ *   append slots distinct.  Kernels skip any address that would fall outside
+ *   the pools (so a violation gives wrong numbers, not a memory fault).
+ *   Calls are reentrant; calls that share output buffers on concurrent streams
+ *   race.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+typedef enum pkv_dtype {
+  PKV_F16 = 0,       /* IEEE binary16 */
+  PKV_BF16 = 1,      /* bfloat16 */
+  PKV_FP8_E4M3 = 2   /* OCP E4M3FN byte, value = e4m3(byte) * scale[block][kv_head] */
+} pkv_dtype;
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,         /* a required pointer is NULL */
+  PKV_ERR_SHAPE = 2,        /* a size is out of range or inconsistent */
+  PKV_ERR_DTYPE = 3,        /* dtype code unknown or combination not allowed */
+  PKV_ERR_WORKSPACE = 4,    /* workspace missing or smaller than paged_attn_workspace_bytes */
+  PKV_ERR_UNSUPPORTED = 5,  /* valid request this build has no kernel for */
+  PKV_ERR_HIP = 6           /* the HIP runtime refused a launch */
+} pkv_status;
+
+/* Shape of one layer's K and V pools (host struct).
+ * Layout of each pool: [num_blocks][num_kv_heads][block_size][head_dim], elements of
+ * kv_dtype, row-major, so one (block, kv head) is one contiguous run of
+ * block_size * head_dim elements.
+ * Supported: block_size == 16, head_dim in {64, 128}, num_kv_heads >= 1. */
+typedef struct pkv_pool {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t kv_dtype;         /* pkv_dtype */
+} pkv_pool;
+
+/* paged_kv_append -- write this step's new K/V rows into their slots
+ * ("Growing During Decode").
+ *   pool           host; shape of the pools.
+ *   k_pool, v_pool pools to write into (see pkv_pool for the layout).
+ *   k_new, v_new   [num_tokens][num_kv_heads][head_dim] rows, elements of new_dtype.
+ *   new_dtype      must equal pool->kv_dtype (rows are copied bit for bit; for fp8
+ *                  pools the caller has quantised them with the block's scale).
+ *   slot_mapping   [num_tokens] int32; slot = block * block_size + offset; a negative
+ *                  slot skips its row; slots >= num_blocks * block_size are skipped.
+ *   num_tokens     >= 0 (0 enqueues nothing).
+ * Bytes of the pools outside the named slots are left untouched.  Must be
+ * enqueued before the paged_attn_step that reads the rows (same stream). */
+int paged_kv_append(const pkv_pool* pool, void* k_pool, void* v_pool,
+                    const void* k_new, const void* v_new, int32_t new_dtype,
+                    const int32_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/* paged_attn_workspace_bytes -- device scratch paged_attn_step needs for these
+ * host scalars (split-context partial results and query row offsets).  Returns 0
+ * if the arguments are invalid. */
+size_t paged_attn_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t total_q_tokens, int32_t max_context_len,
+                                  int32_t max_query_len);
+
+/* paged_attn_step -- attention of every query row of the step over its
+ * sequence's paged history ("Attention Over Scattered Blocks").
+ *   pool            host; shape of the pools.
+ *   q               [total_q_tokens][num_q_heads][head_dim], q_dtype (PKV_F16 or PKV_BF16);
+ *                   the query_lens[i] rows of sequence i follow those of sequence i-1.
+ *   num_q_heads     multiple of pool->num_kv_heads; query head h reads kv head
+ *                   h / (num_q_heads / num_kv_heads).
+ *   k_pool, v_pool  the pools, already holding this step's appended rows.
+ *   k_scale, v_scale  [num_blocks][num_kv_heads] float32, required iff kv_dtype is
+ *                   PKV_FP8_E4M3 (else ignored, may be NULL).
+ *   block_tables    [num_seqs][max_blocks_per_seq] int32 physical block ids; entries past
+ *                   ceil(context_lens[i] / block_size) are never read.
+ *   context_lens    [num_seqs] int32: tokens sequence i attends over, counting the rows
+ *                   appended this step.
+ *   query_lens      [num_seqs] int32: query rows of sequence i (1 = decode).  Row r sits at
+ *                   position context_lens[i] - query_lens[i] + r and attends to keys
+ *                   0 .. that position (causal).
+ *   num_seqs, total_q_tokens, max_context_len, max_query_len  host copies of
+ *                   len(context_lens), sum(query_lens), max(context_lens), max(query_lens);
+ *                   they size the launch grids and must bound the device values.
+ *   scale           softmax scale (typically 1/sqrt(head_dim)).
+ *   out             [total_q_tokens][num_q_heads][head_dim], q_dtype, rounded to nearest even.
+ *   workspace       device scratch of at least paged_attn_workspace_bytes(...) bytes
+ *                   (may be NULL when that is 0); clobbered.
+ * Slots of a block past context_lens[i] are never mixed into the result, whatever
+ * they hold (they are masked by selection, not by multiplying with zero). */
+int paged_attn_step(const pkv_pool* pool,
+                    const void* q, int32_t q_dtype, int32_t num_q_heads,
+                    const void* k_pool, const void* v_pool,
+                    const float* k_scale, const float* v_scale,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, const int32_t* query_lens,
+                    int32_t num_seqs, int32_t total_q_tokens,
+                    int32_t max_context_len, int32_t max_query_len,
+                    float scale, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* pkv_status_string -- static text for a status code (never NULL). */
+const char* pkv_status_string(int status);
+
+/* ---- kernel timing (measurement support, not part of the computation) ----
+ * While enabled, every kernel the library enqueues is bracketed by a pair of
+ * hipEvents on its own stream.  pkv_timing_enable(capacity) creates `capacity`
+ * event pairs up front (host call, allocates) and clears the totals;
+ * pkv_timing_disable() destroys them.  pkv_timing_collect() waits for the
+ * recorded events, adds their durations to per-kernel totals and recycles the
+ * events; pkv_timing_get() returns the total milliseconds and launch count of
+ * one kernel kind.  Launches beyond capacity between two collects are not
+ * timed (pkv_timing_collect returns how many were dropped). */
+typedef enum pkv_kernel_kind {
+  PKV_KERNEL_APPEND = 0,
+  PKV_KERNEL_PROLOGUE = 1,
+  PKV_KERNEL_DECODE = 2,
+  PKV_KERNEL_REDUCE = 3,
+  PKV_KERNEL_CHUNK = 4,
+  PKV_KERNEL_KINDS = 5
+} pkv_kernel_kind;
+
+int pkv_timing_enable(int32_t capacity);
+int pkv_timing_disable(void);
+int pkv_timing_collect(int64_t* dropped /* host, may be NULL */);
+int pkv_timing_get(int32_t kind, double* total_ms /* host */, int64_t* launches /* host */);
+
+/* pkv_kernel_name -- static name of a pkv_kernel_kind's kernel (never NULL). */
+const char* pkv_kernel_name(int32_t kind);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDKV_H */

@@ -1,0 +1,346 @@
+// C ABI of libpagedkv: argument validation, the launch plan of a step, the
+// workspace carve-up and optional per-kernel event timing.  See
+// include/pagedkv.h for the contract of every entry point.
+#include <stdlib.h>
+
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
+#include "../../include/pagedkv.h"
+#include "pkv_launch.h"
+
+namespace {
+
+using pkv::StepParams;
+using pkv::StepPlan;
+
+constexpr int kNumKinds = PKV_KERNEL_KINDS;
+
+int elem_bytes(int dtype) { return dtype == PKV_FP8_E4M3 ? 1 : 2; }
+bool known_dtype(int d) { return d == PKV_F16 || d == PKV_BF16 || d == PKV_FP8_E4M3; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int check_pool(const pkv_pool* pool) {
+  if (pool == nullptr) return PKV_ERR_NULL;
+  if (!known_dtype(pool->kv_dtype)) return PKV_ERR_DTYPE;
+  if (pool->num_blocks < 1 || pool->num_kv_heads < 1 || pool->block_size < 1 || pool->head_dim < 1)
+    return PKV_ERR_SHAPE;
+  if ((int64_t)pool->num_blocks * pool->block_size > INT32_MAX) return PKV_ERR_SHAPE;
+  if (pool->block_size != 16) return PKV_ERR_UNSUPPORTED;
+  if (pool->head_dim != 64 && pool->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// kernel timing
+// ---------------------------------------------------------------------------
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> start, stop;
+  std::vector<int> pending_kind;   // kind of each recorded pair, in order
+  int64_t dropped = 0;
+  double total_ms[kNumKinds] = {};
+  int64_t launches[kNumKinds] = {};
+};
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+template <class F>
+hipError_t timed_launch(int kind, hipStream_t stream, F&& launch) {
+  Timing& t = timing();
+  int slot = -1;
+  {
+    std::lock_guard<std::mutex> g(t.mu);
+    if (t.on) {
+      if (t.pending_kind.size() < t.start.size()) {
+        slot = (int)t.pending_kind.size();
+        t.pending_kind.push_back(kind);
+      } else {
+        ++t.dropped;
+      }
+    }
+  }
+  if (slot >= 0 && hipEventRecord(t.start[slot], stream) != hipSuccess) return hipErrorUnknown;
+  const hipError_t e = launch();
+  if (slot >= 0 && hipEventRecord(t.stop[slot], stream) != hipSuccess) return hipErrorUnknown;
+  return e;
+}
+
+// ---------------------------------------------------------------------------
+// the plan of a step
+// ---------------------------------------------------------------------------
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  if (s == nullptr || *s == 0) return dflt;
+  return atoi(s);
+}
+
+// Tokens per split-context partition: about 256 KiB of K+V per workgroup,
+// halved while a step of few, long rows would leave the chip under-filled.
+int32_t part_tokens_for(const pkv_pool* pool, int32_t rows, int32_t wg_per_row, int32_t max_ctx) {
+  const int forced = env_int("PKV_PART_TOKENS", 0);
+  if (forced >= 16 && forced <= 4096 && forced % 16 == 0) return forced;
+  const int32_t bytes_per_token = 2 * pool->head_dim * elem_bytes(pool->kv_dtype);
+  int32_t pt = 256 * 1024 / bytes_per_token;
+  pt = std::min(4096, std::max(16, pt));
+  while (pt > 64) {
+    const int64_t wgs = (int64_t)rows * wg_per_row * ((max_ctx + pt - 1) / pt);
+    if (wgs >= 4 * 256) break;
+    pt /= 2;
+  }
+  return pt;
+}
+
+struct Layout {
+  size_t q_start_off = 0, row_seq_off = 0, ml_off = 0, o_off = 0, total = 0;
+  int32_t part_tokens = 0, max_parts = 0, heads_per_wg = 1;
+};
+
+int32_t heads_per_wg_for(int32_t group) {
+  for (int g : {8, 4, 2, 1})
+    if (group % g == 0) return g;
+  return 1;
+}
+
+Layout layout_for(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
+                  int32_t max_ctx, int32_t max_q) {
+  Layout lay;
+  const int32_t group = num_q_heads / pool->num_kv_heads;
+  lay.heads_per_wg = heads_per_wg_for(group);
+  lay.part_tokens = part_tokens_for(pool, total_q, num_q_heads / lay.heads_per_wg, max_ctx);
+  lay.max_parts = (max_ctx + lay.part_tokens - 1) / lay.part_tokens;
+  size_t off = 0;
+  if (max_q > 1) {
+    lay.q_start_off = off;
+    off = round_up(off + sizeof(int32_t) * ((size_t)num_seqs + 1), 256);
+    lay.row_seq_off = off;
+    off = round_up(off + sizeof(int32_t) * (size_t)total_q, 256);
+  }
+  if (lay.max_parts > 1) {
+    const size_t entries = (size_t)total_q * num_q_heads * lay.max_parts;
+    lay.ml_off = off;
+    off = round_up(off + entries * 2 * sizeof(float), 256);
+    lay.o_off = off;
+    off = round_up(off + entries * pool->head_dim * sizeof(float), 256);
+  }
+  lay.total = off;
+  return lay;
+}
+
+int check_step_scalars(const pkv_pool* pool, int32_t q_dtype, int32_t num_q_heads,
+                       int32_t max_blocks, int32_t num_seqs, int32_t total_q, int32_t max_ctx,
+                       int32_t max_q) {
+  const int st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (q_dtype != PKV_F16 && q_dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  if (pool->kv_dtype != q_dtype && pool->kv_dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+  if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (num_seqs < 0 || total_q < num_seqs || max_blocks < 1) return PKV_ERR_SHAPE;
+  if (num_seqs > 0 && (max_ctx < 1 || max_q < 1 || max_q > max_ctx || max_q > total_q))
+    return PKV_ERR_SHAPE;
+  if ((int64_t)max_ctx > (int64_t)max_blocks * pool->block_size) return PKV_ERR_SHAPE;
+  if (num_seqs > 0 && max_q == 1 && total_q != num_seqs) return PKV_ERR_SHAPE;
+  if (num_seqs > 0 && max_q > 1 && (int64_t)total_q < (int64_t)num_seqs + max_q - 1) return PKV_ERR_SHAPE;
+  if (total_q > 65535) return PKV_ERR_UNSUPPORTED;   // grid z limit of the decode kernel
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case PKV_ERR_DTYPE: return "unknown dtype or dtype combination not allowed";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_UNSUPPORTED: return "no kernel for this shape in this build";
+    case PKV_ERR_HIP: return "the HIP runtime refused a launch";
+    default: return "unknown status";
+  }
+}
+
+const char* pkv_kernel_name(int32_t kind) {
+  switch (kind) {
+    case PKV_KERNEL_APPEND: return "kv_append_kernel";
+    case PKV_KERNEL_PROLOGUE: return "step_prologue_kernel";
+    case PKV_KERNEL_DECODE: return "decode_valu_kernel";
+    case PKV_KERNEL_REDUCE: return "split_reduce_kernel";
+    case PKV_KERNEL_CHUNK: return "chunk_prefill_kernel";
+    default: return "unknown";
+  }
+}
+
+int paged_kv_append(const pkv_pool* pool, void* k_pool, void* v_pool, const void* k_new,
+                    const void* v_new, int32_t new_dtype, const int32_t* slot_mapping,
+                    int32_t num_tokens, void* stream) {
+  const int st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) return PKV_ERR_SHAPE;
+  if (!known_dtype(new_dtype)) return PKV_ERR_DTYPE;
+  if (new_dtype != pool->kv_dtype) return PKV_ERR_DTYPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PKV_ERR_NULL;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
+    return PKV_ERR_SHAPE;
+  pkv::AppendArgs a;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.elem_bytes = elem_bytes(pool->kv_dtype);
+  a.block_size = pool->block_size;
+  a.num_blocks = pool->num_blocks;
+  const hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = timed_launch(PKV_KERNEL_APPEND, s, [&] { return pkv::launch_append(a, s); });
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+size_t paged_attn_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t total_q_tokens, int32_t max_context_len,
+                                  int32_t max_query_len) {
+  if (check_pool(pool) != PKV_OK) return 0;
+  if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads != 0) return 0;
+  if (num_seqs < 1 || total_q_tokens < num_seqs || max_context_len < 1 || max_query_len < 1) return 0;
+  return layout_for(pool, num_seqs, num_q_heads, total_q_tokens, max_context_len, max_query_len).total;
+}
+
+int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_t num_q_heads,
+                    const void* k_pool, const void* v_pool, const float* k_scale,
+                    const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, const int32_t* query_lens, int32_t num_seqs,
+                    int32_t total_q_tokens, int32_t max_context_len, int32_t max_query_len,
+                    float scale, void* out, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  int st = check_step_scalars(pool, q_dtype, num_q_heads, max_blocks_per_seq, num_seqs,
+                              total_q_tokens, max_context_len, max_query_len);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_lens || !out)
+    return PKV_ERR_NULL;
+  if (pool->kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_SHAPE;
+
+  const Layout lay = layout_for(pool, num_seqs, num_q_heads, total_q_tokens, max_context_len,
+                                max_query_len);
+  if (lay.total > 0 && (workspace == nullptr || workspace_bytes < lay.total)) return PKV_ERR_WORKSPACE;
+
+  StepPlan plan;
+  plan.kv_dtype = pool->kv_dtype;
+  plan.q_dtype = q_dtype;
+  plan.head_dim = pool->head_dim;
+  plan.group = num_q_heads / pool->num_kv_heads;
+  plan.heads_per_wg = lay.heads_per_wg;
+  plan.max_query_len = max_query_len;
+  plan.num_rows_grid = total_q_tokens;
+  plan.use_chunk = false;
+  if (!pkv::decode_supported(plan)) return PKV_ERR_UNSUPPORTED;
+
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  StepParams p;
+  p.q = q;
+  p.out = out;
+  p.k_pool = reinterpret_cast<const uint8_t*>(k_pool);
+  p.v_pool = reinterpret_cast<const uint8_t*>(v_pool);
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.tables = block_tables;
+  p.ctx_lens = context_lens;
+  p.q_lens = query_lens;
+  p.q_start = max_query_len > 1 ? reinterpret_cast<const int32_t*>(ws + lay.q_start_off) : nullptr;
+  p.row_seq = max_query_len > 1 ? reinterpret_cast<const int32_t*>(ws + lay.row_seq_off) : nullptr;
+  p.part_ml = lay.max_parts > 1 ? reinterpret_cast<float*>(ws + lay.ml_off) : nullptr;
+  p.part_o = lay.max_parts > 1 ? reinterpret_cast<float*>(ws + lay.o_off) : nullptr;
+  p.num_blocks = pool->num_blocks;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.num_q_heads = num_q_heads;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_seqs = num_seqs;
+  p.total_q = total_q_tokens;
+  p.max_parts = lay.max_parts;
+  p.part_tokens = lay.part_tokens;
+  p.skip_multi_row = plan.use_chunk ? 1 : 0;
+  p.scale_log2 = scale * pkv::kLog2e;
+
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (max_query_len > 1)
+    e = timed_launch(PKV_KERNEL_PROLOGUE, s, [&] { return pkv::launch_prologue(p, s); });
+  if (e == hipSuccess)
+    e = timed_launch(PKV_KERNEL_DECODE, s, [&] { return pkv::launch_decode(p, plan, s); });
+  if (e == hipSuccess && lay.max_parts > 1)
+    e = timed_launch(PKV_KERNEL_REDUCE, s, [&] { return pkv::launch_reduce(p, plan, s); });
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_timing_enable(int32_t capacity) {
+  if (capacity < 1 || capacity > (1 << 20)) return PKV_ERR_SHAPE;
+  pkv_timing_disable();
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.start.resize(capacity);
+  t.stop.resize(capacity);
+  for (int i = 0; i < capacity; ++i) {
+    if (hipEventCreate(&t.start[i]) != hipSuccess || hipEventCreate(&t.stop[i]) != hipSuccess) {
+      t.start.resize(i);
+      t.stop.resize(i);
+      return PKV_ERR_HIP;
+    }
+  }
+  t.pending_kind.clear();
+  t.dropped = 0;
+  for (int k = 0; k < kNumKinds; ++k) { t.total_ms[k] = 0; t.launches[k] = 0; }
+  t.on = true;
+  return PKV_OK;
+}
+
+int pkv_timing_collect(int64_t* dropped) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  for (size_t i = 0; i < t.pending_kind.size(); ++i) {
+    if (hipEventSynchronize(t.stop[i]) != hipSuccess) return PKV_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, t.start[i], t.stop[i]) != hipSuccess) return PKV_ERR_HIP;
+    t.total_ms[t.pending_kind[i]] += ms;
+    t.launches[t.pending_kind[i]] += 1;
+  }
+  t.pending_kind.clear();
+  if (dropped) *dropped = t.dropped;
+  t.dropped = 0;
+  return PKV_OK;
+}
+
+int pkv_timing_disable(void) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  for (auto ev : t.start) (void)hipEventDestroy(ev);
+  for (auto ev : t.stop) (void)hipEventDestroy(ev);
+  t.start.clear();
+  t.stop.clear();
+  t.pending_kind.clear();
+  t.on = false;
+  return PKV_OK;
+}
+
+int pkv_timing_get(int32_t kind, double* total_ms, int64_t* launches) {
+  if (kind < 0 || kind >= kNumKinds) return PKV_ERR_SHAPE;
+  if (!total_ms || !launches) return PKV_ERR_NULL;
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  *total_ms = t.total_ms[kind];
+  *launches = t.launches[kind];
+  return PKV_OK;
+}
+
+}  // extern "C"

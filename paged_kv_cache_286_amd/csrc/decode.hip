@@ -1,0 +1,381 @@
+// Paged decode attention for gfx950: block-table walk, 16-byte coalesced KV
+// loads, fp32 online softmax with DPP reductions, split-context partials.
+//
+// Page "Serving LLMs with vLLM: Continuous Batching and PagedAttention
+// Explained", section "Attention Over Scattered Blocks": the kernel reads the
+// block table, fetches each block from its physical place and scores block by
+// block; the result is ordinary softmax attention over the whole history.
+// Section "Blocks and Block Tables" fixes the addressing: token t of a
+// sequence sits in block table[t / 16] at offset t % 16.
+//
+// Work decomposition (one workgroup = NW wave64s):
+//   grid.x  split-context partition of part_tokens tokens,
+//   grid.y  group of `GB` query heads that share one kv head,
+//   grid.z  query row (one row per decoding sequence; every row of a prefill
+//           chunk is its own causal "decode" over positions 0..pos unless the
+//           chunk kernel owns it).
+// Inside a workgroup wave w takes blocks w, w+NW, ... of the partition.  A
+// (block, kv head) of K is block_size * head_dim contiguous elements, so one
+// wave-wide 16-byte load covers RPL whole token rows with no gaps: lane l
+// holds EPL consecutive head dims of token j*RPL + l/LPR.  Each group of LPR
+// lanes owning a token row keeps its own running max / sum / accumulator, so
+// the per-block softmax needs no cross-row traffic; rows, then waves (through
+// LDS), are merged once at the end.  A sequence longer than one partition
+// writes (max, sum, unnormalised output) per partition and the reduce kernel
+// merges them with the log-sum-exp rule.
+#include "pkv_launch.h"
+
+namespace pkv {
+
+constexpr int kWaves = 4;
+
+template <int KV, int QT, int D, int GB>
+__global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) {
+  constexpr int ELT = (KV == kFP8) ? 1 : 2;     // bytes per KV element
+  constexpr int ROWB = D * ELT;                  // bytes of one token row of one head
+  constexpr int LPR = ROWB / 16;                 // lanes per token row
+  constexpr int RPL = 64 / LPR;                  // token rows per wave-wide load
+  constexpr int NL = 16 / RPL;                   // loads per 16-token block
+  constexpr int EPL = 16 / ELT;                  // elements per lane per load
+  constexpr int BLKB = 16 * ROWB;                // bytes of one (block, head)
+  static_assert(LPR >= 1 && LPR <= 16 && NL >= 1, "unsupported shape");
+
+  const int part = blockIdx.x;
+  const int row = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int group = p.num_q_heads / p.num_kv_heads;
+  const int h0 = blockIdx.y * GB;                // first query head of this workgroup
+  const int kvh = h0 / group;
+
+  int seq = row;
+  int L;
+  if (p.row_seq != nullptr) {
+    seq = p.row_seq[row];
+    if ((unsigned)seq >= (unsigned)p.num_seqs) return;
+    const int qlen = p.q_lens[seq];
+    if (p.skip_multi_row && qlen > 1) return;
+    L = p.ctx_lens[seq] - qlen + (row - p.q_start[seq]) + 1;
+  } else {
+    L = p.ctx_lens[seq];
+  }
+  const int tok0 = part * p.part_tokens;
+  // rows whose length breaks the host scalars' promises are left unwritten
+  if (tok0 >= L || L > p.max_blocks * 16 || L > p.max_parts * p.part_tokens) return;
+  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+  const int blk_begin = tok0 >> 4;
+  const int blk_end = min((L + 15) >> 4, (tok0 + p.part_tokens) >> 4);
+
+  // this lane's slice of the GB query vectors, pre-scaled into log2 units
+  const int dim0 = (lane % LPR) * EPL;
+  float qf[GB][EPL];
+#pragma unroll
+  for (int g = 0; g < GB; ++g) {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
+                           ((size_t)row * p.num_q_heads + h0 + g) * D + dim0;
+#pragma unroll
+    for (int c = 0; c < EPL / 8; ++c) {
+      const uint4 r = reinterpret_cast<const uint4*>(qrow)[c];
+      float f[8];
+      if constexpr (QT == kBF16) unpack16<kBF16>(r, f);
+      else unpack16<kF16>(r, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[g][c * 8 + e] = f[e] * p.scale_log2;
+    }
+  }
+
+  float m[GB], l[GB], acc[GB][EPL];
+#pragma unroll
+  for (int g = 0; g < GB; ++g) {
+    m[g] = kMaxSeed;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+  }
+
+  const int rg = lane / LPR;                     // token row group of this lane
+  const int32_t* trow = p.tables + (size_t)seq * p.max_blocks;
+  const int nb = blk_end - blk_begin;
+  const int cnt = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;   // <= 64 by construction
+  const int my_tbl = lane < cnt ? trow[blk_begin + wave + kWaves * lane] : -1;
+
+  for (int i = 0; i < cnt; ++i) {
+    const int b = blk_begin + wave + kWaves * i;
+    const int phys = __builtin_amdgcn_readlane(my_tbl, i);
+    if ((unsigned)phys >= (unsigned)p.num_blocks) continue;
+    const size_t boff = ((size_t)phys * p.num_kv_heads + kvh) * BLKB;
+    const uint4* kb = reinterpret_cast<const uint4*>(p.k_pool + boff);
+    const uint4* vb = reinterpret_cast<const uint4*>(p.v_pool + boff);
+    uint4 kr[NL], vr[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) kr[j] = kb[j * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) vr[j] = vb[j * 64 + lane];
+    float ksc = 1.f, vsc = 1.f;
+    if constexpr (KV == kFP8) {
+      ksc = p.k_scale[(size_t)phys * p.num_kv_heads + kvh];
+      vsc = p.v_scale[(size_t)phys * p.num_kv_heads + kvh];
+    }
+
+    // scores of this lane's token rows (one per load)
+    float s[GB][NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      float kf[EPL];
+      unpack16<KV>(kr[j], kf);
+#pragma unroll
+      for (int g = 0; g < GB; ++g) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) a = __builtin_fmaf(qf[g][e], kf[e], a);
+        s[g][j] = group_sum<LPR>(a) * ksc;
+      }
+    }
+
+    const bool full = b * 16 + 16 <= L;
+    bool valid[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) valid[j] = full || (b * 16 + j * RPL + rg < L);
+
+    float pw[GB][NL];
+#pragma unroll
+    for (int g = 0; g < GB; ++g) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int j = 0; j < NL; ++j) mx = fmaxf(mx, valid[j] ? s[g][j] : -__builtin_inff());
+      const float mn = fmaxf(m[g], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m[g] - mn);
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        pw[g][j] = valid[j] ? __builtin_amdgcn_exp2f(s[g][j] - mn) : 0.f;
+        ps += pw[g][j];
+      }
+      l[g] = l[g] * alpha + ps;
+      m[g] = mn;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+    }
+
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      float vf[EPL];
+      unpack16<KV>(vr[j], vf);
+      if (!full) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[e] = valid[j] ? vf[e] : 0.f;   // select: tail slots may hold NaN
+      }
+#pragma unroll
+      for (int g = 0; g < GB; ++g) {
+        const float pv = pw[g][j] * vsc;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = __builtin_fmaf(pv, vf[e], acc[g][e]);
+      }
+    }
+  }
+
+  // merge the RPL token-row groups of this wave
+#pragma unroll
+  for (int g = 0; g < GB; ++g) {
+    float M = m[g];
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, shfl_xor_f(M, off));
+    const float f = __builtin_amdgcn_exp2f(m[g] - M);
+    l[g] *= f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] *= f;
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+      l[g] += shfl_xor_f(l[g], off);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] += shfl_xor_f(acc[g][e], off);
+    }
+    m[g] = M;
+  }
+
+  // merge the waves through LDS
+  __shared__ float sm_o[kWaves][GB][D];
+  __shared__ float sm_m[kWaves][GB];
+  __shared__ float sm_l[kWaves][GB];
+  if (rg == 0) {
+#pragma unroll
+    for (int g = 0; g < GB; ++g)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sm_o[wave][g][dim0 + e] = acc[g][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < GB; ++g) { sm_m[wave][g] = m[g]; sm_l[wave][g] = l[g]; }
+  }
+  __syncthreads();
+
+  for (int t = threadIdx.x; t < GB * D; t += kWaves * 64) {
+    const int g = t / D;
+    const int d = t - g * D;
+    float M = sm_m[0][g];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][g]);
+    float ls = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = __builtin_amdgcn_exp2f(sm_m[w][g] - M);
+      ls = __builtin_fmaf(sm_l[w][g], f, ls);
+      o = __builtin_fmaf(sm_o[w][g][d], f, o);
+    }
+    const size_t rh = (size_t)row * p.num_q_heads + h0 + g;
+    if (nparts == 1) {
+      reinterpret_cast<uint16_t*>(p.out)[rh * D + d] = to_out_bits<QT>(o / ls);
+    } else {
+      const size_t idx = rh * p.max_parts + part;
+      p.part_o[idx * D + d] = o;
+      if (d == 0) {
+        p.part_ml[idx * 2] = M;
+        p.part_ml[idx * 2 + 1] = ls;
+      }
+    }
+  }
+}
+
+// Merge the partitions of every (row, query head) whose sequence was split.
+template <int QT, int D>
+__global__ __launch_bounds__(64) void split_reduce_kernel(StepParams p) {
+  const int h = blockIdx.x;
+  const int row = blockIdx.y;
+  int L;
+  if (p.row_seq != nullptr) {
+    const int seq = p.row_seq[row];
+    if ((unsigned)seq >= (unsigned)p.num_seqs) return;
+    const int qlen = p.q_lens[seq];
+    if (p.skip_multi_row && qlen > 1) return;
+    L = p.ctx_lens[seq] - qlen + (row - p.q_start[seq]) + 1;
+  } else {
+    L = p.ctx_lens[row];
+  }
+  if (L < 1 || L > p.max_blocks * 16 || L > p.max_parts * p.part_tokens) return;
+  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+  if (nparts <= 1) return;
+  const size_t rh = (size_t)row * p.num_q_heads + h;
+  const float* ml = p.part_ml + rh * p.max_parts * 2;
+  const float* po = p.part_o + rh * p.max_parts * D;
+  float M = -__builtin_inff();
+  for (int q = 0; q < nparts; ++q) M = fmaxf(M, ml[2 * q]);
+  float ls = 0.f;
+  float o[D / 64];
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c) o[c] = 0.f;
+  for (int q = 0; q < nparts; ++q) {
+    const float f = __builtin_amdgcn_exp2f(ml[2 * q] - M);
+    ls = __builtin_fmaf(ml[2 * q + 1], f, ls);
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c)
+      o[c] = __builtin_fmaf(po[(size_t)q * D + c * 64 + threadIdx.x], f, o[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c)
+    reinterpret_cast<uint16_t*>(p.out)[rh * D + c * 64 + threadIdx.x] = to_out_bits<QT>(o[c] / ls);
+}
+
+// Row offsets of every sequence (exclusive scan of query_lens) and the owning
+// sequence of every query row.  One workgroup; only launched when some
+// sequence has more than one query row.
+__global__ __launch_bounds__(1024) void step_prologue_kernel(const int32_t* __restrict__ q_lens,
+                                                             int32_t num_seqs, int32_t total_q,
+                                                             int32_t* __restrict__ q_start,
+                                                             int32_t* __restrict__ row_seq) {
+  __shared__ int32_t wave_tot[16];
+  __shared__ int32_t carry_s;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < num_seqs; base += 1024) {
+    const int i = base + tid;
+    const int v = i < num_seqs ? q_lens[i] : 0;
+    int x = v;   // inclusive scan inside the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) wave_tot[wave] = x;
+    __syncthreads();
+    int before = carry_s;
+    for (int w = 0; w < wave; ++w) before += wave_tot[w];
+    const int start = before + x - v;
+    if (i < num_seqs) {
+      q_start[i] = start;
+      const int stop = min(start + v, total_q);
+      for (int r = max(start, 0); r < stop; ++r) row_seq[r] = i;
+    }
+    __syncthreads();
+    if (tid == 1023) carry_s = before + x;
+    __syncthreads();
+  }
+  if (tid == 0) q_start[num_seqs] = carry_s;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_prologue(const StepParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(step_prologue_kernel, dim3(1), dim3(1024), 0, stream, p.q_lens, p.num_seqs,
+                     p.total_q, const_cast<int32_t*>(p.q_start), const_cast<int32_t*>(p.row_seq));
+  return hipGetLastError();
+}
+
+template <int KV, int QT, int D>
+static hipError_t decode_by_group(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
+  const dim3 grid((uint32_t)p.max_parts, (uint32_t)(p.num_q_heads / plan.heads_per_wg),
+                  (uint32_t)plan.num_rows_grid);
+  const dim3 block(kWaves * 64);
+  switch (plan.heads_per_wg) {
+    case 1: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 1>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 2>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 4>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 8>), grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int KV, int QT>
+static hipError_t decode_by_dim(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
+  if (plan.head_dim == 128) return decode_by_group<KV, QT, 128>(p, plan, stream);
+  if (plan.head_dim == 64) return decode_by_group<KV, QT, 64>(p, plan, stream);
+  return hipErrorInvalidValue;
+}
+
+bool decode_supported(const StepPlan& plan) {
+  const bool dim_ok = plan.head_dim == 64 || plan.head_dim == 128;
+  const bool gb_ok = plan.heads_per_wg == 1 || plan.heads_per_wg == 2 || plan.heads_per_wg == 4 ||
+                     plan.heads_per_wg == 8;
+  const bool q_ok = plan.q_dtype == kF16 || plan.q_dtype == kBF16;
+  const bool kv_ok = plan.kv_dtype == plan.q_dtype || plan.kv_dtype == kFP8;
+  return dim_ok && gb_ok && q_ok && kv_ok;
+}
+
+hipError_t launch_decode(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
+  if (plan.q_dtype == kBF16) {
+    if (plan.kv_dtype == kBF16) return decode_by_dim<kBF16, kBF16>(p, plan, stream);
+    if (plan.kv_dtype == kFP8) return decode_by_dim<kFP8, kBF16>(p, plan, stream);
+  } else if (plan.q_dtype == kF16) {
+    if (plan.kv_dtype == kF16) return decode_by_dim<kF16, kF16>(p, plan, stream);
+    if (plan.kv_dtype == kFP8) return decode_by_dim<kFP8, kF16>(p, plan, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_reduce(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
+  const dim3 grid((uint32_t)p.num_q_heads, (uint32_t)plan.num_rows_grid);
+  if (plan.q_dtype == kBF16) {
+    if (plan.head_dim == 128) hipLaunchKernelGGL((split_reduce_kernel<kBF16, 128>), grid, dim3(64), 0, stream, p);
+    else hipLaunchKernelGGL((split_reduce_kernel<kBF16, 64>), grid, dim3(64), 0, stream, p);
+  } else {
+    if (plan.head_dim == 128) hipLaunchKernelGGL((split_reduce_kernel<kF16, 128>), grid, dim3(64), 0, stream, p);
+    else hipLaunchKernelGGL((split_reduce_kernel<kF16, 64>), grid, dim3(64), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,139 @@
+// Device-side helpers shared by the gfx950 kernels of libpagedkv.
+// Element conversions, wave64 reductions and the parameter block of one step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// element type codes (same values as pkv_dtype)
+constexpr int kF16 = 0;
+constexpr int kBF16 = 1;
+constexpr int kFP8 = 2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+// running-max seed: finite, far below any real score, so exp2(seed - seed) = 1 and
+// exp2(seed - real) = 0 without ever forming inf - inf
+constexpr float kMaxSeed = -1.0e30f;
+
+// ---------------------------------------------------------------------------
+// parameters of one paged_attn_step, as the kernels see them
+// ---------------------------------------------------------------------------
+struct StepParams {
+  const void* q;             // [Tq][Hq][D]
+  void* out;                 // [Tq][Hq][D]
+  const uint8_t* k_pool;     // [NB][Hkv][bs][D]
+  const uint8_t* v_pool;
+  const float* k_scale;      // [NB][Hkv] (fp8 only)
+  const float* v_scale;
+  const int32_t* tables;     // [S][max_blocks]
+  const int32_t* ctx_lens;   // [S]
+  const int32_t* q_lens;     // [S]
+  const int32_t* q_start;    // [S + 1] row offsets (NULL when every query_len is 1)
+  const int32_t* row_seq;    // [Tq] sequence of each row (NULL when every query_len is 1)
+  float* part_ml;            // [Tq][Hq][max_parts][2]  (m in log2 units, l)
+  float* part_o;             // [Tq][Hq][max_parts][D]  unnormalised
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t max_blocks;
+  int32_t num_seqs;
+  int32_t total_q;
+  int32_t max_parts;
+  int32_t part_tokens;       // tokens per split-context partition (multiple of 16)
+  int32_t skip_multi_row;    // 1: rows of sequences with query_len > 1 are left to the chunk kernel
+  float scale_log2;          // softmax scale * log2(e)
+};
+
+// ---------------------------------------------------------------------------
+// conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// two OCP E4M3FN bytes (the low or high 16 bits of w) -> two floats, hardware convert
+template <bool HI>
+__device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& a, float& b) {
+  auto v = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  a = v[0];
+  b = v[1];
+}
+
+// unpack a 16-byte load of KV elements into floats (8 for 16-bit types, 16 for fp8)
+template <int KV>
+__device__ __forceinline__ void unpack16(const uint4& r, float* f) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+  if constexpr (KV == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_lo(w[i]); f[2 * i + 1] = bf16_hi(w[i]); }
+  } else if constexpr (KV == kF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[2 * i] = f16_lo(w[i]); f[2 * i + 1] = f16_hi(w[i]); }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fp8x2_to_f32<false>(w[i], f[4 * i], f[4 * i + 1]);
+      fp8x2_to_f32<true>(w[i], f[4 * i + 2], f[4 * i + 3]);
+    }
+  }
+}
+
+// 16-bit query/output element <-> float
+template <int T>
+__device__ __forceinline__ float load_q(const void* base, size_t idx) {
+  const uint16_t u = reinterpret_cast<const uint16_t*>(base)[idx];
+  if constexpr (T == kBF16) return __uint_as_float((uint32_t)u << 16);
+  else return (float)__builtin_bit_cast(_Float16, u);
+}
+
+// float -> bfloat16 bits, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <int T>
+__device__ __forceinline__ uint16_t to_out_bits(float f) {
+  if constexpr (T == kBF16) return f32_to_bf16_rne(f);
+  else return __builtin_bit_cast(uint16_t, (_Float16)f);   // v_cvt_f16_f32, RNE
+}
+
+// ---------------------------------------------------------------------------
+// wave64 cross-lane reductions
+// ---------------------------------------------------------------------------
+// DPP controls (gfx9): quad_perm, row_half_mirror, row_mirror
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// sum over aligned groups of N lanes (N in {1,2,4,8,16}); every lane gets its group's sum
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp_f<kDppQuadXor1>(v);
+  if constexpr (N >= 4) v += dpp_f<kDppQuadXor2>(v);
+  if constexpr (N >= 8) v += dpp_f<kDppRowHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp_f<kDppRowMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace pkv

@@ -1,0 +1,157 @@
+"""ctypes binding of libpagedkv.so: the C ABI of include/pagedkv.h, same names.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  Pointer arguments accept an ``int`` device address,
+``None`` (NULL) or any object with ``data_ptr()`` (a torch tensor); stream
+arguments accept an ``int`` hipStream_t, ``None`` or an object with a
+``cuda_stream`` attribute (a torch stream).  A non-zero status raises
+:class:`PagedKVError`.
+
+Importing this module raises ``ImportError`` when the library has not been
+built (``python -m paged_kv_cache_286_amd.build_lib``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run `python -m paged_kv_cache_286_amd.build_lib`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+DTYPE_CODES = {"f16": PKV_F16, "bf16": PKV_BF16, "fp8_e4m3": PKV_FP8_E4M3}
+(PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_WORKSPACE,
+ PKV_ERR_UNSUPPORTED, PKV_ERR_HIP) = range(7)
+(PKV_KERNEL_APPEND, PKV_KERNEL_PROLOGUE, PKV_KERNEL_DECODE, PKV_KERNEL_REDUCE,
+ PKV_KERNEL_CHUNK, PKV_KERNEL_KINDS) = range(6)
+
+# every symbol include/pagedkv.h declares
+EXPORTS = ("paged_kv_append", "paged_attn_workspace_bytes", "paged_attn_step",
+           "pkv_status_string", "pkv_timing_enable", "pkv_timing_disable",
+           "pkv_timing_collect", "pkv_timing_get", "pkv_kernel_name")
+
+
+class PkvPool(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32)]
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {pkv_status_string(status)} (status {status})")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_POOLP = ctypes.POINTER(PkvPool)
+
+_lib.paged_kv_append.argtypes = [_POOLP, _P, _P, _P, _P, _I, _P, _I, _P]
+_lib.paged_kv_append.restype = ctypes.c_int
+_lib.paged_attn_workspace_bytes.argtypes = [_POOLP, _I, _I, _I, _I, _I]
+_lib.paged_attn_workspace_bytes.restype = ctypes.c_size_t
+_lib.paged_attn_step.argtypes = [_POOLP, _P, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I,
+                                 _I, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+_lib.paged_attn_step.restype = ctypes.c_int
+_lib.pkv_status_string.argtypes = [ctypes.c_int]
+_lib.pkv_status_string.restype = ctypes.c_char_p
+_lib.pkv_kernel_name.argtypes = [_I]
+_lib.pkv_kernel_name.restype = ctypes.c_char_p
+_lib.pkv_timing_enable.argtypes = [_I]
+_lib.pkv_timing_enable.restype = ctypes.c_int
+_lib.pkv_timing_disable.argtypes = []
+_lib.pkv_timing_disable.restype = ctypes.c_int
+_lib.pkv_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int64)]
+_lib.pkv_timing_collect.restype = ctypes.c_int
+_lib.pkv_timing_get.argtypes = [_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+_lib.pkv_timing_get.restype = ctypes.c_int
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(s) -> Optional[int]:
+    if s is None or isinstance(s, int):
+        return s
+    return int(s.cuda_stream)
+
+
+def _poolref(pool: Optional[PkvPool]):
+    return None if pool is None else ctypes.byref(pool)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != PKV_OK:
+        raise PagedKVError(fn, status)
+
+
+def make_pool(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
+              kv_dtype) -> PkvPool:
+    code = DTYPE_CODES[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
+    return PkvPool(num_blocks, block_size, num_kv_heads, head_dim, code)
+
+
+def pkv_status_string(status: int) -> str:
+    return _lib.pkv_status_string(int(status)).decode()
+
+
+def pkv_kernel_name(kind: int) -> str:
+    return _lib.pkv_kernel_name(int(kind)).decode()
+
+
+def paged_kv_append(pool: PkvPool, k_pool, v_pool, k_new, v_new, new_dtype: int,
+                    slot_mapping, num_tokens: int, stream=None) -> None:
+    _check("paged_kv_append", _lib.paged_kv_append(
+        _poolref(pool), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), int(new_dtype),
+        _ptr(slot_mapping), int(num_tokens), _stream(stream)))
+
+
+def paged_attn_workspace_bytes(pool: PkvPool, num_seqs: int, num_q_heads: int,
+                               total_q_tokens: int, max_context_len: int,
+                               max_query_len: int) -> int:
+    return int(_lib.paged_attn_workspace_bytes(_poolref(pool), int(num_seqs), int(num_q_heads),
+                                               int(total_q_tokens), int(max_context_len),
+                                               int(max_query_len)))
+
+
+def paged_attn_step(pool: PkvPool, q, q_dtype: int, num_q_heads: int, k_pool, v_pool,
+                    k_scale, v_scale, block_tables, max_blocks_per_seq: int, context_lens,
+                    query_lens, num_seqs: int, total_q_tokens: int, max_context_len: int,
+                    max_query_len: int, scale: float, out, workspace, workspace_bytes: int,
+                    stream=None) -> None:
+    _check("paged_attn_step", _lib.paged_attn_step(
+        _poolref(pool), _ptr(q), int(q_dtype), int(num_q_heads), _ptr(k_pool), _ptr(v_pool),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), int(max_blocks_per_seq),
+        _ptr(context_lens), _ptr(query_lens), int(num_seqs), int(total_q_tokens),
+        int(max_context_len), int(max_query_len), float(scale), _ptr(out), _ptr(workspace),
+        int(workspace_bytes), _stream(stream)))
+
+
+def pkv_timing_enable(capacity: int) -> None:
+    _check("pkv_timing_enable", _lib.pkv_timing_enable(int(capacity)))
+
+
+def pkv_timing_disable() -> None:
+    _check("pkv_timing_disable", _lib.pkv_timing_disable())
+
+
+def pkv_timing_collect() -> int:
+    dropped = ctypes.c_int64(0)
+    _check("pkv_timing_collect", _lib.pkv_timing_collect(ctypes.byref(dropped)))
+    return int(dropped.value)
+
+
+def pkv_timing_get(kind: int) -> Tuple[float, int]:
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    _check("pkv_timing_get", _lib.pkv_timing_get(int(kind), ctypes.byref(ms), ctypes.byref(n)))
+    return float(ms.value), int(n.value)
