@@ -143,6 +143,12 @@ int paged_attn_step(const pkv_pool* pool,
 /* pkv_status_string -- static text for a status code (never NULL). */
 const char* pkv_status_string(int status);
 
+/* pkv_last_hip_error / pkv_last_hip_error_string -- the hipError_t (and its name)
+ * behind the most recent PKV_ERR_HIP returned on the calling thread; 0 / "hipSuccess"
+ * if there was none.  The string is static. */
+int pkv_last_hip_error(void);
+const char* pkv_last_hip_error_string(void);
+
 /* ---- kernel timing (measurement support, not part of the computation) ----
  * While enabled, every kernel the library enqueues is bracketed by a pair of
  * hipEvents on its own stream.  pkv_timing_enable(capacity) creates `capacity`

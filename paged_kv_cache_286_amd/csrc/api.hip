@@ -17,6 +17,15 @@ using pkv::StepPlan;
 
 constexpr int kNumKinds = PKV_KERNEL_KINDS;
 
+// HIP error behind the most recent PKV_ERR_HIP of this thread
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return PKV_OK;
+  g_last_hip_error = e;
+  return PKV_ERR_HIP;
+}
+
 int elem_bytes(int dtype) { return dtype == PKV_FP8_E4M3 ? 1 : 2; }
 bool known_dtype(int d) { return d == PKV_F16 || d == PKV_BF16 || d == PKV_FP8_E4M3; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -203,8 +212,7 @@ int paged_kv_append(const pkv_pool* pool, void* k_pool, void* v_pool, const void
   a.block_size = pool->block_size;
   a.num_blocks = pool->num_blocks;
   const hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = timed_launch(PKV_KERNEL_APPEND, s, [&] { return pkv::launch_append(a, s); });
-  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  return hip_status(timed_launch(PKV_KERNEL_APPEND, s, [&] { return pkv::launch_append(a, s); }));
 }
 
 size_t paged_attn_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
@@ -281,7 +289,7 @@ int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_
     e = timed_launch(PKV_KERNEL_DECODE, s, [&] { return pkv::launch_decode(p, plan, s); });
   if (e == hipSuccess && lay.max_parts > 1)
     e = timed_launch(PKV_KERNEL_REDUCE, s, [&] { return pkv::launch_reduce(p, plan, s); });
-  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  return hip_status(e);
 }
 
 int pkv_timing_enable(int32_t capacity) {
@@ -295,7 +303,7 @@ int pkv_timing_enable(int32_t capacity) {
     if (hipEventCreate(&t.start[i]) != hipSuccess || hipEventCreate(&t.stop[i]) != hipSuccess) {
       t.start.resize(i);
       t.stop.resize(i);
-      return PKV_ERR_HIP;
+      return hip_status(hipErrorOutOfMemory);
     }
   }
   t.pending_kind.clear();
@@ -309,9 +317,11 @@ int pkv_timing_collect(int64_t* dropped) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
   for (size_t i = 0; i < t.pending_kind.size(); ++i) {
-    if (hipEventSynchronize(t.stop[i]) != hipSuccess) return PKV_ERR_HIP;
+    hipError_t e = hipEventSynchronize(t.stop[i]);
+    if (e != hipSuccess) return hip_status(e);
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, t.start[i], t.stop[i]) != hipSuccess) return PKV_ERR_HIP;
+    e = hipEventElapsedTime(&ms, t.start[i], t.stop[i]);
+    if (e != hipSuccess) return hip_status(e);
     t.total_ms[t.pending_kind[i]] += ms;
     t.launches[t.pending_kind[i]] += 1;
   }
@@ -332,6 +342,10 @@ int pkv_timing_disable(void) {
   t.on = false;
   return PKV_OK;
 }
+
+int pkv_last_hip_error(void) { return (int)g_last_hip_error; }
+
+const char* pkv_last_hip_error_string(void) { return hipGetErrorName(g_last_hip_error); }
 
 int pkv_timing_get(int32_t kind, double* total_ms, int64_t* launches) {
   if (kind < 0 || kind >= kNumKinds) return PKV_ERR_SHAPE;

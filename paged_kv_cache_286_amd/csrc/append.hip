@@ -44,6 +44,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   const int64_t threads = 2LL * a.num_tokens * a.num_kv_heads * pieces;
   if (threads == 0) return hipSuccess;
   const int64_t blocks = (threads + 255) / 256;
+  (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
   hipLaunchKernelGGL(kv_append_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
                      (uint8_t*)a.k_pool, (uint8_t*)a.v_pool, (const uint8_t*)a.k_new,
                      (const uint8_t*)a.v_new, a.slots, a.num_tokens, a.num_kv_heads, pieces,

@@ -319,6 +319,7 @@ __global__ __launch_bounds__(1024) void step_prologue_kernel(const int32_t* __re
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_prologue(const StepParams& p, hipStream_t stream) {
+  (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
   hipLaunchKernelGGL(step_prologue_kernel, dim3(1), dim3(1024), 0, stream, p.q_lens, p.num_seqs,
                      p.total_q, const_cast<int32_t*>(p.q_start), const_cast<int32_t*>(p.row_seq));
   return hipGetLastError();
@@ -329,6 +330,7 @@ static hipError_t decode_by_group(const StepParams& p, const StepPlan& plan, hip
   const dim3 grid((uint32_t)p.max_parts, (uint32_t)(p.num_q_heads / plan.heads_per_wg),
                   (uint32_t)plan.num_rows_grid);
   const dim3 block(kWaves * 64);
+  (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
   switch (plan.heads_per_wg) {
     case 1: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 1>), grid, block, 0, stream, p); break;
     case 2: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 2>), grid, block, 0, stream, p); break;
@@ -368,6 +370,7 @@ hipError_t launch_decode(const StepParams& p, const StepPlan& plan, hipStream_t 
 
 hipError_t launch_reduce(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
   const dim3 grid((uint32_t)p.num_q_heads, (uint32_t)plan.num_rows_grid);
+  (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
   if (plan.q_dtype == kBF16) {
     if (plan.head_dim == 128) hipLaunchKernelGGL((split_reduce_kernel<kBF16, 128>), grid, dim3(64), 0, stream, p);
     else hipLaunchKernelGGL((split_reduce_kernel<kBF16, 64>), grid, dim3(64), 0, stream, p);

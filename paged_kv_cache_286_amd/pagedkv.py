@@ -16,6 +16,15 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
+# One process may hold only one HIP runtime.  PyTorch ships its own
+# libamdhip64.so.7; loading it first makes the dynamic loader bind this
+# library's libamdhip64.so.7 dependency to that same copy (same soname), so
+# the library and torch share devices, streams and memory.
+try:
+    import torch  # noqa: F401
+except ImportError:  # pragma: no cover - a C-only user links the system runtime
+    pass
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run `python -m paged_kv_cache_286_amd.build_lib`")
@@ -31,7 +40,8 @@ DTYPE_CODES = {"f16": PKV_F16, "bf16": PKV_BF16, "fp8_e4m3": PKV_FP8_E4M3}
 # every symbol include/pagedkv.h declares
 EXPORTS = ("paged_kv_append", "paged_attn_workspace_bytes", "paged_attn_step",
            "pkv_status_string", "pkv_timing_enable", "pkv_timing_disable",
-           "pkv_timing_collect", "pkv_timing_get", "pkv_kernel_name")
+           "pkv_timing_collect", "pkv_timing_get", "pkv_kernel_name", "pkv_last_hip_error",
+           "pkv_last_hip_error_string")
 
 
 class PkvPool(ctypes.Structure):
@@ -42,7 +52,10 @@ class PkvPool(ctypes.Structure):
 
 class PagedKVError(RuntimeError):
     def __init__(self, fn: str, status: int):
-        super().__init__(f"{fn}: {pkv_status_string(status)} (status {status})")
+        msg = f"{fn}: {pkv_status_string(status)} (status {status})"
+        if status == PKV_ERR_HIP:
+            msg += f": {pkv_last_hip_error_string()} ({pkv_last_hip_error()})"
+        super().__init__(msg)
         self.status = status
 
 
@@ -61,6 +74,10 @@ _lib.pkv_status_string.argtypes = [ctypes.c_int]
 _lib.pkv_status_string.restype = ctypes.c_char_p
 _lib.pkv_kernel_name.argtypes = [_I]
 _lib.pkv_kernel_name.restype = ctypes.c_char_p
+_lib.pkv_last_hip_error.argtypes = []
+_lib.pkv_last_hip_error.restype = ctypes.c_int
+_lib.pkv_last_hip_error_string.argtypes = []
+_lib.pkv_last_hip_error_string.restype = ctypes.c_char_p
 _lib.pkv_timing_enable.argtypes = [_I]
 _lib.pkv_timing_enable.restype = ctypes.c_int
 _lib.pkv_timing_disable.argtypes = []
@@ -134,6 +151,14 @@ def paged_attn_step(pool: PkvPool, q, q_dtype: int, num_q_heads: int, k_pool, v_
         _ptr(context_lens), _ptr(query_lens), int(num_seqs), int(total_q_tokens),
         int(max_context_len), int(max_query_len), float(scale), _ptr(out), _ptr(workspace),
         int(workspace_bytes), _stream(stream)))
+
+
+def pkv_last_hip_error() -> int:
+    return int(_lib.pkv_last_hip_error())
+
+
+def pkv_last_hip_error_string() -> str:
+    return _lib.pkv_last_hip_error_string().decode()
 
 
 def pkv_timing_enable(capacity: int) -> None:

@@ -122,3 +122,11 @@ def test_timing_argument_checks():
         pk.pkv_timing_get(pk.PKV_KERNEL_KINDS)
     ms, n = pk.pkv_timing_get(pk.PKV_KERNEL_DECODE)
     assert n >= 0 and ms >= 0
+
+
+def test_library_shares_torchs_hip_runtime():
+    # the binding loads torch first, so exactly one libamdhip64 is mapped in this process
+    import torch  # noqa: F401
+    maps = open("/proc/self/maps").read()
+    hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(hip) == 1, hip
