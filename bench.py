@@ -90,6 +90,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the steps without per-kernel events")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB --steps times (scales the "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -105,6 +108,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": args.steps}), flush=True)
+        return
     log(f"generating workload {args.workload}")
     t0 = time.time()
     wl = W.generate(W.make_plan(args.workload))
@@ -119,8 +132,6 @@ def main():
         ds.step(stream)
     torch.cuda.synchronize()
 
-    if not args.no_kernel_timing:
-        pk.pkv_timing_enable(4 * args.steps + 64)
     log(f"timing {args.steps} steps")
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -131,8 +142,17 @@ def main():
     stop.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(stop) / args.steps
+
+    # Per-kernel durations: the same number of steps again, every library launch
+    # bracketed by a pair of hipEvents on the launch stream.  Kept out of the
+    # region above because the markers themselves add ~20 us to a step.
     kernels = {}
     if not args.no_kernel_timing:
+        log(f"timing {args.steps} steps per kernel")
+        pk.pkv_timing_enable(4 * args.steps + 64)
+        for _ in range(args.steps):
+            ds.step(stream)
+        torch.cuda.synchronize()
         dropped = pk.pkv_timing_collect()
         for kind in range(pk.PKV_KERNEL_KINDS):
             ms, n = pk.pkv_timing_get(kind)

@@ -89,13 +89,13 @@ int env_int(const char* name, int dflt) {
   return atoi(s);
 }
 
-// Tokens per split-context partition: about 256 KiB of K+V per workgroup,
+// Tokens per split-context partition: about 512 KiB of K+V per workgroup,
 // halved while a step of few, long rows would leave the chip under-filled.
 int32_t part_tokens_for(const pkv_pool* pool, int32_t rows, int32_t wg_per_row, int32_t max_ctx) {
   const int forced = env_int("PKV_PART_TOKENS", 0);
   if (forced >= 16 && forced <= 4096 && forced % 16 == 0) return forced;
   const int32_t bytes_per_token = 2 * pool->head_dim * elem_bytes(pool->kv_dtype);
-  int32_t pt = 256 * 1024 / bytes_per_token;
+  int32_t pt = 512 * 1024 / bytes_per_token;
   pt = std::min(4096, std::max(16, pt));
   while (pt > 64) {
     const int64_t wgs = (int64_t)rows * wg_per_row * ((max_ctx + pt - 1) / pt);
@@ -155,7 +155,7 @@ int check_step_scalars(const pkv_pool* pool, int32_t q_dtype, int32_t num_q_head
   if ((int64_t)max_ctx > (int64_t)max_blocks * pool->block_size) return PKV_ERR_SHAPE;
   if (num_seqs > 0 && max_q == 1 && total_q != num_seqs) return PKV_ERR_SHAPE;
   if (num_seqs > 0 && max_q > 1 && (int64_t)total_q < (int64_t)num_seqs + max_q - 1) return PKV_ERR_SHAPE;
-  if (total_q > 65535) return PKV_ERR_UNSUPPORTED;   // grid z limit of the decode kernel
+  if (total_q > 65535) return PKV_ERR_UNSUPPORTED;   // grid y limit of the decode kernel
   return PKV_OK;
 }
 

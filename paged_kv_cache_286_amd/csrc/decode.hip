@@ -9,11 +9,16 @@
 // sequence sits in block table[t / 16] at offset t % 16.
 //
 // Work decomposition (one workgroup = NW wave64s):
-//   grid.x  split-context partition of part_tokens tokens,
-//   grid.y  group of `GB` query heads that share one kv head,
-//   grid.z  query row (one row per decoding sequence; every row of a prefill
+//   grid.x  group of `GB` query heads that share one kv head,
+//   grid.y  query row (one row per decoding sequence; every row of a prefill
 //           chunk is its own causal "decode" over positions 0..pos unless the
-//           chunk kernel owns it).
+//           chunk kernel owns it),
+//   grid.z  split-context partition of part_tokens tokens.
+// The hardware deals workgroups to the 8 XCDs round-robin by linear id, so the
+// fastest grid dimension must not be one along which the work per workgroup
+// changes: heads (equal work) go first and partitions (the last ones are often
+// empty) go last, which also dispatches every row's heavy first partitions
+// before the light tail ones.
 // Inside a workgroup wave w takes blocks w, w+NW, ... of the partition.  A
 // (block, kv head) of K is block_size * head_dim contiguous elements, so one
 // wave-wide 16-byte load covers RPL whole token rows with no gaps: lane l
@@ -29,23 +34,119 @@ namespace pkv {
 
 constexpr int kWaves = 4;
 
+// Shape constants of the register layout for one (KV type, head_dim).
+template <int KV, int D>
+struct Lay {
+  static constexpr int ELT = (KV == kFP8) ? 1 : 2;   // bytes per KV element
+  static constexpr int ROWB = D * ELT;                // bytes of one token row of one head
+  static constexpr int LPR = ROWB / 16;               // lanes per token row
+  static constexpr int RPL = 64 / LPR;                // token rows per wave-wide load
+  static constexpr int NL = 16 / RPL;                 // loads per 16-token block
+  static constexpr int EPL = 16 / ELT;                // elements per lane per load
+  static constexpr int BLKB = 16 * ROWB;              // bytes of one (block, head)
+  // 16-bit K is multiplied pairwise with v_dot2 against 16-bit q; fp8 K goes through fp32
+  static constexpr bool DOT2 = KV != kFP8;
+};
+
+// Scores, online-softmax update and value accumulation for one 16-token block.
+// kr / vr hold this lane's slice of the block's K and V rows; `limit` is the
+// number of the block's tokens that belong to the sequence (16 for all but the
+// last block; 0 for a block whose table entry is out of range).
+template <int KV, int QT, int D, int GB>
+__device__ __forceinline__ void attend_block(const uint4 (&kr)[Lay<KV, D>::NL],
+                                             const uint4 (&vr)[Lay<KV, D>::NL], float ksc,
+                                             float vsc, int limit, int rg,
+                                             const uint32_t (&qp)[GB][Lay<KV, D>::EPL / 2],
+                                             const float (&qf)[GB][Lay<KV, D>::EPL],
+                                             float score_mul, float (&m)[GB], float (&l)[GB],
+                                             float (&acc)[GB][Lay<KV, D>::EPL]) {
+  using T = Lay<KV, D>;
+  float s[GB][T::NL];
+#pragma unroll
+  for (int j = 0; j < T::NL; ++j) {
+    if constexpr (T::DOT2) {
+      const uint32_t w[4] = {kr[j].x, kr[j].y, kr[j].z, kr[j].w};
+#pragma unroll
+      for (int g = 0; g < GB; ++g) {
+        float a = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if constexpr (KV == kBF16)
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qp[g][c]),
+                                                __builtin_bit_cast(bf16x2, w[c]), a, false);
+          else
+            a = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qp[g][c]),
+                                       __builtin_bit_cast(f16x2, w[c]), a, false);
+        }
+        s[g][j] = group_sum<T::LPR>(a) * score_mul;
+      }
+    } else {
+      float kf[T::EPL];
+      unpack16<KV>(kr[j], kf);
+#pragma unroll
+      for (int g = 0; g < GB; ++g) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < T::EPL; ++e) a = __builtin_fmaf(qf[g][e], kf[e], a);
+        s[g][j] = group_sum<T::LPR>(a) * ksc;
+      }
+    }
+  }
+
+  const bool full = limit >= 16;
+  bool valid[T::NL];
+#pragma unroll
+  for (int j = 0; j < T::NL; ++j) valid[j] = full || (j * T::RPL + rg < limit);
+
+  float pw[GB][T::NL];
+#pragma unroll
+  for (int g = 0; g < GB; ++g) {
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < T::NL; ++j) mx = fmaxf(mx, valid[j] ? s[g][j] : -__builtin_inff());
+    const float mn = fmaxf(m[g], mx);
+    const float alpha = __builtin_amdgcn_exp2f(m[g] - mn);
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < T::NL; ++j) {
+      pw[g][j] = valid[j] ? __builtin_amdgcn_exp2f(s[g][j] - mn) : 0.f;
+      ps += pw[g][j];
+    }
+    l[g] = l[g] * alpha + ps;
+    m[g] = mn;
+#pragma unroll
+    for (int e = 0; e < T::EPL; ++e) acc[g][e] *= alpha;
+  }
+
+#pragma unroll
+  for (int j = 0; j < T::NL; ++j) {
+    float vf[T::EPL];
+    unpack16<KV>(vr[j], vf);
+    if (!full) {
+#pragma unroll
+      for (int e = 0; e < T::EPL; ++e) vf[e] = valid[j] ? vf[e] : 0.f;   // select: tail slots may hold NaN
+    }
+#pragma unroll
+    for (int g = 0; g < GB; ++g) {
+      const float pv = pw[g][j] * vsc;
+#pragma unroll
+      for (int e = 0; e < T::EPL; ++e) acc[g][e] = __builtin_fmaf(pv, vf[e], acc[g][e]);
+    }
+  }
+}
+
 template <int KV, int QT, int D, int GB>
 __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) {
-  constexpr int ELT = (KV == kFP8) ? 1 : 2;     // bytes per KV element
-  constexpr int ROWB = D * ELT;                  // bytes of one token row of one head
-  constexpr int LPR = ROWB / 16;                 // lanes per token row
-  constexpr int RPL = 64 / LPR;                  // token rows per wave-wide load
-  constexpr int NL = 16 / RPL;                   // loads per 16-token block
-  constexpr int EPL = 16 / ELT;                  // elements per lane per load
-  constexpr int BLKB = 16 * ROWB;                // bytes of one (block, head)
-  static_assert(LPR >= 1 && LPR <= 16 && NL >= 1, "unsupported shape");
+  using T = Lay<KV, D>;
+  static_assert(T::LPR >= 1 && T::LPR <= 16 && T::NL >= 1, "unsupported shape");
+  static_assert(!T::DOT2 || KV == QT, "16-bit KV is read with q of the same type");
 
-  const int part = blockIdx.x;
-  const int row = blockIdx.z;
+  const int part = blockIdx.z;
+  const int row = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int group = p.num_q_heads / p.num_kv_heads;
-  const int h0 = blockIdx.y * GB;                // first query head of this workgroup
+  const int h0 = blockIdx.x * GB;                // first query head of this workgroup
   const int kvh = h0 / group;
 
   int seq = row;
@@ -66,111 +167,79 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) 
   const int blk_begin = tok0 >> 4;
   const int blk_end = min((L + 15) >> 4, (tok0 + p.part_tokens) >> 4);
 
-  // this lane's slice of the GB query vectors, pre-scaled into log2 units
-  const int dim0 = (lane % LPR) * EPL;
-  float qf[GB][EPL];
-#pragma unroll
-  for (int g = 0; g < GB; ++g) {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
-                           ((size_t)row * p.num_q_heads + h0 + g) * D + dim0;
-#pragma unroll
-    for (int c = 0; c < EPL / 8; ++c) {
-      const uint4 r = reinterpret_cast<const uint4*>(qrow)[c];
-      float f[8];
-      if constexpr (QT == kBF16) unpack16<kBF16>(r, f);
-      else unpack16<kF16>(r, f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[g][c * 8 + e] = f[e] * p.scale_log2;
-    }
-  }
-
-  float m[GB], l[GB], acc[GB][EPL];
-#pragma unroll
-  for (int g = 0; g < GB; ++g) {
-    m[g] = kMaxSeed;
-    l[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
-  }
-
-  const int rg = lane / LPR;                     // token row group of this lane
+  // block table entries of this wave's blocks (blk_begin + wave + kWaves * i)
   const int32_t* trow = p.tables + (size_t)seq * p.max_blocks;
   const int nb = blk_end - blk_begin;
   const int cnt = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;   // <= 64 by construction
   const int my_tbl = lane < cnt ? trow[blk_begin + wave + kWaves * lane] : -1;
 
-  for (int i = 0; i < cnt; ++i) {
+  // this lane's slice of the GB query vectors: raw 16-bit pairs for the dot2
+  // path (the score is scaled afterwards), fp32 pre-scaled into log2 units otherwise
+  const int dim0 = (lane % T::LPR) * T::EPL;
+  uint32_t qp[GB][T::EPL / 2];
+  float qf[GB][T::EPL];
+#pragma unroll
+  for (int g = 0; g < GB; ++g) {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
+                           ((size_t)row * p.num_q_heads + h0 + g) * D + dim0;
+#pragma unroll
+    for (int c = 0; c < T::EPL / 8; ++c) {
+      const uint4 r = reinterpret_cast<const uint4*>(qrow)[c];
+      if constexpr (T::DOT2) {
+        qp[g][4 * c + 0] = r.x;
+        qp[g][4 * c + 1] = r.y;
+        qp[g][4 * c + 2] = r.z;
+        qp[g][4 * c + 3] = r.w;
+      } else {
+        float f[8];
+        if constexpr (QT == kBF16) unpack16<kBF16>(r, f);
+        else unpack16<kF16>(r, f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[g][c * 8 + e] = f[e] * p.scale_log2;
+      }
+    }
+  }
+
+  float m[GB], l[GB], acc[GB][T::EPL];
+#pragma unroll
+  for (int g = 0; g < GB; ++g) {
+    m[g] = kMaxSeed;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < T::EPL; ++e) acc[g][e] = 0.f;
+  }
+
+  const int rg = lane / T::LPR;                  // token row group of this lane
+  // Two register buffers: the loads of block i+1 are in flight while block i is
+  // scored.  An out-of-range table entry reads block 0 and counts no tokens.
+  uint4 kA[T::NL], vA[T::NL], kB[T::NL], vB[T::NL];
+  float kscA = 1.f, vscA = 1.f, kscB = 1.f, vscB = 1.f;
+  int limA = 0, limB = 0;
+  auto issue = [&](int i, uint4 (&kr)[T::NL], uint4 (&vr)[T::NL], float& ks, float& vs, int& lim) {
     const int b = blk_begin + wave + kWaves * i;
-    const int phys = __builtin_amdgcn_readlane(my_tbl, i);
-    if ((unsigned)phys >= (unsigned)p.num_blocks) continue;
-    const size_t boff = ((size_t)phys * p.num_kv_heads + kvh) * BLKB;
+    int phys = __builtin_amdgcn_readlane(my_tbl, i);
+    lim = min(16, L - b * 16);
+    if ((unsigned)phys >= (unsigned)p.num_blocks) { phys = 0; lim = 0; }
+    const size_t boff = ((size_t)phys * p.num_kv_heads + kvh) * T::BLKB;
     const uint4* kb = reinterpret_cast<const uint4*>(p.k_pool + boff);
     const uint4* vb = reinterpret_cast<const uint4*>(p.v_pool + boff);
-    uint4 kr[NL], vr[NL];
 #pragma unroll
-    for (int j = 0; j < NL; ++j) kr[j] = kb[j * 64 + lane];
+    for (int j = 0; j < T::NL; ++j) kr[j] = kb[j * 64 + lane];
 #pragma unroll
-    for (int j = 0; j < NL; ++j) vr[j] = vb[j * 64 + lane];
-    float ksc = 1.f, vsc = 1.f;
+    for (int j = 0; j < T::NL; ++j) vr[j] = vb[j * 64 + lane];
     if constexpr (KV == kFP8) {
-      ksc = p.k_scale[(size_t)phys * p.num_kv_heads + kvh];
-      vsc = p.v_scale[(size_t)phys * p.num_kv_heads + kvh];
+      ks = p.k_scale[(size_t)phys * p.num_kv_heads + kvh];
+      vs = p.v_scale[(size_t)phys * p.num_kv_heads + kvh];
     }
+  };
 
-    // scores of this lane's token rows (one per load)
-    float s[GB][NL];
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      float kf[EPL];
-      unpack16<KV>(kr[j], kf);
-#pragma unroll
-      for (int g = 0; g < GB; ++g) {
-        float a = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) a = __builtin_fmaf(qf[g][e], kf[e], a);
-        s[g][j] = group_sum<LPR>(a) * ksc;
-      }
-    }
-
-    const bool full = b * 16 + 16 <= L;
-    bool valid[NL];
-#pragma unroll
-    for (int j = 0; j < NL; ++j) valid[j] = full || (b * 16 + j * RPL + rg < L);
-
-    float pw[GB][NL];
-#pragma unroll
-    for (int g = 0; g < GB; ++g) {
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int j = 0; j < NL; ++j) mx = fmaxf(mx, valid[j] ? s[g][j] : -__builtin_inff());
-      const float mn = fmaxf(m[g], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m[g] - mn);
-      float ps = 0.f;
-#pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        pw[g][j] = valid[j] ? __builtin_amdgcn_exp2f(s[g][j] - mn) : 0.f;
-        ps += pw[g][j];
-      }
-      l[g] = l[g] * alpha + ps;
-      m[g] = mn;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
-    }
-
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      float vf[EPL];
-      unpack16<KV>(vr[j], vf);
-      if (!full) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) vf[e] = valid[j] ? vf[e] : 0.f;   // select: tail slots may hold NaN
-      }
-#pragma unroll
-      for (int g = 0; g < GB; ++g) {
-        const float pv = pw[g][j] * vsc;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] = __builtin_fmaf(pv, vf[e], acc[g][e]);
-      }
+  if (cnt > 0) issue(0, kA, vA, kscA, vscA, limA);
+  for (int i = 0; i < cnt; i += 2) {
+    if (i + 1 < cnt) issue(i + 1, kB, vB, kscB, vscB, limB);
+    attend_block<KV, QT, D, GB>(kA, vA, kscA, vscA, limA, rg, qp, qf, p.scale_log2, m, l, acc);
+    if (i + 1 < cnt) {
+      if (i + 2 < cnt) issue(i + 2, kA, vA, kscA, vscA, limA);
+      attend_block<KV, QT, D, GB>(kB, vB, kscB, vscB, limB, rg, qp, qf, p.scale_log2, m, l, acc);
     }
   }
 
@@ -179,16 +248,16 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) 
   for (int g = 0; g < GB; ++g) {
     float M = m[g];
 #pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, shfl_xor_f(M, off));
+    for (int off = T::LPR; off < 64; off <<= 1) M = fmaxf(M, shfl_xor_f(M, off));
     const float f = __builtin_amdgcn_exp2f(m[g] - M);
     l[g] *= f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] *= f;
+    for (int e = 0; e < T::EPL; ++e) acc[g][e] *= f;
 #pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) {
+    for (int off = T::LPR; off < 64; off <<= 1) {
       l[g] += shfl_xor_f(l[g], off);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] += shfl_xor_f(acc[g][e], off);
+      for (int e = 0; e < T::EPL; ++e) acc[g][e] += shfl_xor_f(acc[g][e], off);
     }
     m[g] = M;
   }
@@ -201,7 +270,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) 
 #pragma unroll
     for (int g = 0; g < GB; ++g)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_o[wave][g][dim0 + e] = acc[g][e];
+      for (int e = 0; e < T::EPL; ++e) sm_o[wave][g][dim0 + e] = acc[g][e];
   }
   if (lane == 0) {
 #pragma unroll
@@ -327,8 +396,8 @@ hipError_t launch_prologue(const StepParams& p, hipStream_t stream) {
 
 template <int KV, int QT, int D>
 static hipError_t decode_by_group(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
-  const dim3 grid((uint32_t)p.max_parts, (uint32_t)(p.num_q_heads / plan.heads_per_wg),
-                  (uint32_t)plan.num_rows_grid);
+  const dim3 grid((uint32_t)(p.num_q_heads / plan.heads_per_wg), (uint32_t)plan.num_rows_grid,
+                  (uint32_t)p.max_parts);
   const dim3 block(kWaves * 64);
   (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
   switch (plan.heads_per_wg) {

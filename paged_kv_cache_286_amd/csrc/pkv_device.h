@@ -12,6 +12,9 @@ constexpr int kF16 = 0;
 constexpr int kBF16 = 1;
 constexpr int kFP8 = 2;
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 constexpr float kLog2e = 1.4426950408889634f;
 // running-max seed: finite, far below any real score, so exp2(seed - seed) = 1 and
 // exp2(seed - real) = 0 without ever forming inf - inf
