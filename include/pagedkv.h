@@ -159,12 +159,13 @@ const char* pkv_last_hip_error_string(void);
  * one kernel kind.  Launches beyond capacity between two collects are not
  * timed (pkv_timing_collect returns how many were dropped). */
 typedef enum pkv_kernel_kind {
-  PKV_KERNEL_APPEND = 0,
-  PKV_KERNEL_PROLOGUE = 1,
-  PKV_KERNEL_DECODE = 2,
-  PKV_KERNEL_REDUCE = 3,
-  PKV_KERNEL_CHUNK = 4,
-  PKV_KERNEL_KINDS = 5
+  PKV_KERNEL_APPEND = 0,       /* kv_append_kernel */
+  PKV_KERNEL_PROLOGUE = 1,     /* step_prologue_kernel: row offsets, prefill tile list */
+  PKV_KERNEL_DECODE = 2,       /* decode_valu_kernel: decode rows, 16-bit KV, <= 2 heads per kv head */
+  PKV_KERNEL_REDUCE = 3,       /* split_reduce_kernel */
+  PKV_KERNEL_CHUNK = 4,        /* chunk_mfma_kernel: rows of prefill chunks */
+  PKV_KERNEL_DECODE_MFMA = 5,  /* decode_mfma_kernel: grouped-query or fp8 decode rows */
+  PKV_KERNEL_KINDS = 6
 } pkv_kernel_kind;
 
 int pkv_timing_enable(int32_t capacity);

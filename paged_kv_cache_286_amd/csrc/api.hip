@@ -106,8 +106,11 @@ int32_t part_tokens_for(const pkv_pool* pool, int32_t rows, int32_t wg_per_row, 
 }
 
 struct Layout {
-  size_t q_start_off = 0, row_seq_off = 0, ml_off = 0, o_off = 0, total = 0;
-  int32_t part_tokens = 0, max_parts = 0, heads_per_wg = 1;
+  size_t q_start_off = 0, row_seq_off = 0, chunk_count_off = 0, chunk_entries_off = 0;
+  size_t ml_off = 0, o_off = 0, total = 0;
+  int32_t part_tokens = 0, chunk_part_tokens = 0, max_parts = 0, chunk_max_parts = 0;
+  int32_t chunk_capacity = 0, heads_per_wg = 1;
+  bool decode_on_mfma = false;
 };
 
 int32_t heads_per_wg_for(int32_t group) {
@@ -116,19 +119,56 @@ int32_t heads_per_wg_for(int32_t group) {
   return 1;
 }
 
+// Decode rows of 16-bit KV with at most two query heads per kv head run on the
+// VALU kernel (one token row per 16-lane group, nothing padded); grouped-query
+// and fp8 decode rows run on the MFMA tile kernel, where the group's heads fill
+// the columns of a 16x16 tile and K/V are read once for all of them.
+bool decode_on_mfma_for(const pkv_pool* pool, int32_t group) {
+  const int forced = env_int("PKV_DECODE_MFMA", -1);
+  if (forced == 0 || forced == 1) return forced == 1;
+  return pool->kv_dtype == PKV_FP8_E4M3 || group > 2;
+}
+
+int32_t round16(int64_t x) { return (int32_t)((x + 15) / 16 * 16); }
+
+// Tokens per partition of a prefill-chunk row: no split when the chunk's
+// column tiles already give >= 512 work items, otherwise enough partitions to
+// reach ~1024 items.  At most 4096 (64 blocks per wave).
+int32_t chunk_part_tokens_for(int32_t group, int32_t num_kv_heads, int32_t max_ctx, int32_t max_q) {
+  const int forced = env_int("PKV_CHUNK_PART_TOKENS", 0);
+  if (forced >= 16 && forced <= 4096 && forced % 16 == 0) return forced;
+  const int64_t tiles = ((int64_t)max_q * group + 15) / 16;
+  const int64_t items = tiles * num_kv_heads;
+  int64_t parts = items >= 512 ? 1 : (1024 + items - 1) / items;
+  int32_t pt = round16((max_ctx + parts - 1) / parts);
+  return std::min(4096, std::max(64, pt));
+}
+
 Layout layout_for(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
                   int32_t max_ctx, int32_t max_q) {
   Layout lay;
   const int32_t group = num_q_heads / pool->num_kv_heads;
+  lay.decode_on_mfma = decode_on_mfma_for(pool, group);
   lay.heads_per_wg = heads_per_wg_for(group);
-  lay.part_tokens = part_tokens_for(pool, total_q, num_q_heads / lay.heads_per_wg, max_ctx);
+  const int32_t wg_per_row =
+      lay.decode_on_mfma ? pool->num_kv_heads * ((group + 15) / 16) : num_q_heads / lay.heads_per_wg;
+  lay.part_tokens = part_tokens_for(pool, num_seqs, wg_per_row, max_ctx);
   lay.max_parts = (max_ctx + lay.part_tokens - 1) / lay.part_tokens;
   size_t off = 0;
   if (max_q > 1) {
+    lay.chunk_part_tokens = chunk_part_tokens_for(group, pool->num_kv_heads, max_ctx, max_q);
+    lay.chunk_max_parts = (max_ctx + lay.chunk_part_tokens - 1) / lay.chunk_part_tokens;
+    lay.max_parts = std::max(lay.max_parts, lay.chunk_max_parts);
+    // sum over sequences with q > 1 of ceil(q * group / 16) <= total_q * group / 16 + num_seqs
+    lay.chunk_capacity = (int32_t)(((int64_t)total_q * group + 15) / 16 + num_seqs);
     lay.q_start_off = off;
     off = round_up(off + sizeof(int32_t) * ((size_t)num_seqs + 1), 256);
     lay.row_seq_off = off;
     off = round_up(off + sizeof(int32_t) * (size_t)total_q, 256);
+    lay.chunk_count_off = off;
+    off = round_up(off + sizeof(int32_t), 256);
+    lay.chunk_entries_off = off;
+    off = round_up(off + 2 * sizeof(int32_t) * (size_t)lay.chunk_capacity, 256);
   }
   if (lay.max_parts > 1) {
     const size_t entries = (size_t)total_q * num_q_heads * lay.max_parts;
@@ -181,8 +221,9 @@ const char* pkv_kernel_name(int32_t kind) {
     case PKV_KERNEL_APPEND: return "kv_append_kernel";
     case PKV_KERNEL_PROLOGUE: return "step_prologue_kernel";
     case PKV_KERNEL_DECODE: return "decode_valu_kernel";
+    case PKV_KERNEL_DECODE_MFMA: return "decode_mfma_kernel";
     case PKV_KERNEL_REDUCE: return "split_reduce_kernel";
-    case PKV_KERNEL_CHUNK: return "chunk_prefill_kernel";
+    case PKV_KERNEL_CHUNK: return "chunk_mfma_kernel";
     default: return "unknown";
   }
 }
@@ -250,12 +291,12 @@ int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_
   plan.head_dim = pool->head_dim;
   plan.group = num_q_heads / pool->num_kv_heads;
   plan.heads_per_wg = lay.heads_per_wg;
-  plan.max_query_len = max_query_len;
-  plan.num_rows_grid = total_q_tokens;
-  plan.use_chunk = false;
+  plan.decode_on_mfma = lay.decode_on_mfma;
+  plan.chunk_grid = 0;
   if (!pkv::decode_supported(plan)) return PKV_ERR_UNSUPPORTED;
 
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  const bool multi = max_query_len > 1;
   StepParams p;
   p.q = q;
   p.out = out;
@@ -266,8 +307,10 @@ int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_
   p.tables = block_tables;
   p.ctx_lens = context_lens;
   p.q_lens = query_lens;
-  p.q_start = max_query_len > 1 ? reinterpret_cast<const int32_t*>(ws + lay.q_start_off) : nullptr;
-  p.row_seq = max_query_len > 1 ? reinterpret_cast<const int32_t*>(ws + lay.row_seq_off) : nullptr;
+  p.q_start = multi ? reinterpret_cast<const int32_t*>(ws + lay.q_start_off) : nullptr;
+  p.row_seq = multi ? reinterpret_cast<const int32_t*>(ws + lay.row_seq_off) : nullptr;
+  p.chunk_count = multi ? reinterpret_cast<const int32_t*>(ws + lay.chunk_count_off) : nullptr;
+  p.chunk_entries = multi ? reinterpret_cast<const int32_t*>(ws + lay.chunk_entries_off) : nullptr;
   p.part_ml = lay.max_parts > 1 ? reinterpret_cast<float*>(ws + lay.ml_off) : nullptr;
   p.part_o = lay.max_parts > 1 ? reinterpret_cast<float*>(ws + lay.o_off) : nullptr;
   p.num_blocks = pool->num_blocks;
@@ -278,15 +321,25 @@ int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_
   p.total_q = total_q_tokens;
   p.max_parts = lay.max_parts;
   p.part_tokens = lay.part_tokens;
-  p.skip_multi_row = plan.use_chunk ? 1 : 0;
+  p.chunk_part_tokens = multi ? lay.chunk_part_tokens : lay.part_tokens;
+  p.chunk_max_parts = lay.chunk_max_parts;
+  p.chunk_capacity = lay.chunk_capacity;
   p.scale_log2 = scale * pkv::kLog2e;
+  if (multi) {
+    const int64_t items = (int64_t)lay.chunk_capacity * pool->num_kv_heads * lay.chunk_max_parts;
+    plan.chunk_grid = (int32_t)std::min<int64_t>(items, 2048);
+  }
 
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
-  if (max_query_len > 1)
+  if (multi)
     e = timed_launch(PKV_KERNEL_PROLOGUE, s, [&] { return pkv::launch_prologue(p, s); });
   if (e == hipSuccess)
-    e = timed_launch(PKV_KERNEL_DECODE, s, [&] { return pkv::launch_decode(p, plan, s); });
+    e = plan.decode_on_mfma
+            ? timed_launch(PKV_KERNEL_DECODE_MFMA, s, [&] { return pkv::launch_decode_mfma(p, plan, s); })
+            : timed_launch(PKV_KERNEL_DECODE, s, [&] { return pkv::launch_decode(p, plan, s); });
+  if (e == hipSuccess && multi)
+    e = timed_launch(PKV_KERNEL_CHUNK, s, [&] { return pkv::launch_chunk(p, plan, s); });
   if (e == hipSuccess && lay.max_parts > 1)
     e = timed_launch(PKV_KERNEL_REDUCE, s, [&] { return pkv::launch_reduce(p, plan, s); });
   return hip_status(e);

@@ -10,9 +10,8 @@
 //
 // Work decomposition (one workgroup = NW wave64s):
 //   grid.x  group of `GB` query heads that share one kv head,
-//   grid.y  query row (one row per decoding sequence; every row of a prefill
-//           chunk is its own causal "decode" over positions 0..pos unless the
-//           chunk kernel owns it),
+//   grid.y  sequence (only sequences with one query row; prefill chunks go to
+//           the MFMA chunk kernel),
 //   grid.z  split-context partition of part_tokens tokens.
 // The hardware deals workgroups to the 8 XCDs round-robin by linear id, so the
 // fastest grid dimension must not be one along which the work per workgroup
@@ -142,24 +141,20 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) 
   static_assert(!T::DOT2 || KV == QT, "16-bit KV is read with q of the same type");
 
   const int part = blockIdx.z;
-  const int row = blockIdx.y;
+  const int seq = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int group = p.num_q_heads / p.num_kv_heads;
   const int h0 = blockIdx.x * GB;                // first query head of this workgroup
   const int kvh = h0 / group;
 
-  int seq = row;
-  int L;
-  if (p.row_seq != nullptr) {
-    seq = p.row_seq[row];
-    if ((unsigned)seq >= (unsigned)p.num_seqs) return;
-    const int qlen = p.q_lens[seq];
-    if (p.skip_multi_row && qlen > 1) return;
-    L = p.ctx_lens[seq] - qlen + (row - p.q_start[seq]) + 1;
-  } else {
-    L = p.ctx_lens[seq];
+  int row = seq;
+  if (p.q_start != nullptr) {
+    if (p.q_lens[seq] != 1) return;              // prefill chunks go to the chunk kernel
+    row = p.q_start[seq];
+    if (row < 0 || row >= p.total_q) return;
   }
+  const int L = p.ctx_lens[seq];
   const int tok0 = part * p.part_tokens;
   // rows whose length breaks the host scalars' promises are left unwritten
   if (tok0 >= L || L > p.max_blocks * 16 || L > p.max_parts * p.part_tokens) return;
@@ -305,23 +300,26 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) 
   }
 }
 
-// Merge the partitions of every (row, query head) whose sequence was split.
+// Merge the partitions of every (row, query head) whose context was split.
+// A row of a prefill chunk sees keys 0..its position, split by the chunk
+// kernel's partition size; a decode row sees the whole context.
 template <int QT, int D>
 __global__ __launch_bounds__(64) void split_reduce_kernel(StepParams p) {
   const int h = blockIdx.x;
   const int row = blockIdx.y;
-  int L;
+  int L, pt;
   if (p.row_seq != nullptr) {
     const int seq = p.row_seq[row];
     if ((unsigned)seq >= (unsigned)p.num_seqs) return;
     const int qlen = p.q_lens[seq];
-    if (p.skip_multi_row && qlen > 1) return;
     L = p.ctx_lens[seq] - qlen + (row - p.q_start[seq]) + 1;
+    pt = qlen > 1 ? p.chunk_part_tokens : p.part_tokens;
   } else {
     L = p.ctx_lens[row];
+    pt = p.part_tokens;
   }
-  if (L < 1 || L > p.max_blocks * 16 || L > p.max_parts * p.part_tokens) return;
-  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+  if (L < 1 || L > p.max_blocks * 16 || L > p.max_parts * pt) return;
+  const int nparts = (L + pt - 1) / pt;
   if (nparts <= 1) return;
   const size_t rh = (size_t)row * p.num_q_heads + h;
   const float* ml = p.part_ml + rh * p.max_parts * 2;
@@ -344,44 +342,62 @@ __global__ __launch_bounds__(64) void split_reduce_kernel(StepParams p) {
     reinterpret_cast<uint16_t*>(p.out)[rh * D + c * 64 + threadIdx.x] = to_out_bits<QT>(o[c] / ls);
 }
 
-// Row offsets of every sequence (exclusive scan of query_lens) and the owning
-// sequence of every query row.  One workgroup; only launched when some
-// sequence has more than one query row.
-__global__ __launch_bounds__(1024) void step_prologue_kernel(const int32_t* __restrict__ q_lens,
-                                                             int32_t num_seqs, int32_t total_q,
-                                                             int32_t* __restrict__ q_start,
-                                                             int32_t* __restrict__ row_seq) {
-  __shared__ int32_t wave_tot[16];
-  __shared__ int32_t carry_s;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  if (tid == 0) carry_s = 0;
-  __syncthreads();
-  for (int base = 0; base < num_seqs; base += 1024) {
-    const int i = base + tid;
-    const int v = i < num_seqs ? q_lens[i] : 0;
-    int x = v;   // inclusive scan inside the wave
+// inclusive scan of v over the 1024 threads of the workgroup
+__device__ __forceinline__ int block_scan_1024(int v, int32_t* wave_tot) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int x = v;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
-    }
-    if (lane == 63) wave_tot[wave] = x;
-    __syncthreads();
-    int before = carry_s;
-    for (int w = 0; w < wave; ++w) before += wave_tot[w];
-    const int start = before + x - v;
-    if (i < num_seqs) {
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wave_tot[wave] = x;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) x += wave_tot[w];
+  __syncthreads();
+  return x;
+}
+
+// Row offsets of every sequence (exclusive scan of query_lens), the owning
+// sequence of every query row, and the list of (sequence, first column) tiles
+// of 16 (row, head) columns of every sequence with more than one query row.
+// One workgroup; only launched when some sequence has more than one row.
+__global__ __launch_bounds__(1024) void step_prologue_kernel(StepParams p) {
+  __shared__ int32_t wave_tot[16];
+  __shared__ int32_t carry_rows, carry_tiles;
+  int32_t* q_start = const_cast<int32_t*>(p.q_start);
+  int32_t* row_seq = const_cast<int32_t*>(p.row_seq);
+  int32_t* entries = const_cast<int32_t*>(p.chunk_entries);
+  const int group = p.num_q_heads / p.num_kv_heads;
+  const int tid = threadIdx.x;
+  if (tid == 0) { carry_rows = 0; carry_tiles = 0; }
+  __syncthreads();
+  for (int base = 0; base < p.num_seqs; base += 1024) {
+    const int i = base + tid;
+    const int q = i < p.num_seqs ? max(p.q_lens[i], 0) : 0;
+    const int tiles = q > 1 ? (q * group + 15) / 16 : 0;
+    const int r_incl = block_scan_1024(q, wave_tot);
+    const int t_incl = block_scan_1024(tiles, wave_tot);
+    const int start = carry_rows + r_incl - q;
+    const int tstart = carry_tiles + t_incl - tiles;
+    if (i < p.num_seqs) {
       q_start[i] = start;
-      const int stop = min(start + v, total_q);
+      const int stop = min(start + q, p.total_q);
       for (int r = max(start, 0); r < stop; ++r) row_seq[r] = i;
+      for (int t = 0; t < tiles && tstart + t < p.chunk_capacity; ++t) {
+        entries[2 * (tstart + t)] = i;
+        entries[2 * (tstart + t) + 1] = 16 * t;
+      }
     }
     __syncthreads();
-    if (tid == 1023) carry_s = before + x;
+    if (tid == 1023) { carry_rows += r_incl; carry_tiles += t_incl; }
     __syncthreads();
   }
-  if (tid == 0) q_start[num_seqs] = carry_s;
+  if (tid == 0) {
+    q_start[p.num_seqs] = carry_rows;
+    *const_cast<int32_t*>(p.chunk_count) = min(carry_tiles, p.chunk_capacity);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -389,14 +405,13 @@ __global__ __launch_bounds__(1024) void step_prologue_kernel(const int32_t* __re
 // ---------------------------------------------------------------------------
 hipError_t launch_prologue(const StepParams& p, hipStream_t stream) {
   (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
-  hipLaunchKernelGGL(step_prologue_kernel, dim3(1), dim3(1024), 0, stream, p.q_lens, p.num_seqs,
-                     p.total_q, const_cast<int32_t*>(p.q_start), const_cast<int32_t*>(p.row_seq));
+  hipLaunchKernelGGL(step_prologue_kernel, dim3(1), dim3(1024), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int KV, int QT, int D>
 static hipError_t decode_by_group(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
-  const dim3 grid((uint32_t)(p.num_q_heads / plan.heads_per_wg), (uint32_t)plan.num_rows_grid,
+  const dim3 grid((uint32_t)(p.num_q_heads / plan.heads_per_wg), (uint32_t)p.num_seqs,
                   (uint32_t)p.max_parts);
   const dim3 block(kWaves * 64);
   (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
@@ -438,7 +453,7 @@ hipError_t launch_decode(const StepParams& p, const StepPlan& plan, hipStream_t 
 }
 
 hipError_t launch_reduce(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
-  const dim3 grid((uint32_t)p.num_q_heads, (uint32_t)plan.num_rows_grid);
+  const dim3 grid((uint32_t)p.num_q_heads, (uint32_t)p.total_q);
   (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
   if (plan.q_dtype == kBF16) {
     if (plan.head_dim == 128) hipLaunchKernelGGL((split_reduce_kernel<kBF16, 128>), grid, dim3(64), 0, stream, p);

@@ -37,15 +37,19 @@ struct StepParams {
   const int32_t* row_seq;    // [Tq] sequence of each row (NULL when every query_len is 1)
   float* part_ml;            // [Tq][Hq][max_parts][2]  (m in log2 units, l)
   float* part_o;             // [Tq][Hq][max_parts][D]  unnormalised
+  const int32_t* chunk_entries;  // [chunk_capacity][2] (sequence, first column) of prefill tiles
+  const int32_t* chunk_count;    // number of valid chunk entries (written by the prologue)
   int32_t num_blocks;
   int32_t num_kv_heads;
   int32_t num_q_heads;
   int32_t max_blocks;
   int32_t num_seqs;
   int32_t total_q;
-  int32_t max_parts;
-  int32_t part_tokens;       // tokens per split-context partition (multiple of 16)
-  int32_t skip_multi_row;    // 1: rows of sequences with query_len > 1 are left to the chunk kernel
+  int32_t max_parts;         // partition slots per (row, head) in the partial buffers
+  int32_t part_tokens;       // tokens per split-context partition of a decode row (multiple of 16)
+  int32_t chunk_part_tokens; // tokens per partition of a prefill-chunk row (multiple of 16)
+  int32_t chunk_max_parts;   // partitions the chunk kernel walks per entry and kv head
+  int32_t chunk_capacity;    // room for chunk entries in the workspace
   float scale_log2;          // softmax scale * log2(e)
 };
 

@@ -28,15 +28,16 @@ struct StepPlan {
   int32_t q_dtype;
   int32_t head_dim;
   int32_t group;          // query heads per kv head
-  int32_t heads_per_wg;   // query heads one decode workgroup handles
-  int32_t max_query_len;
-  int32_t num_rows_grid;  // grid z of the decode kernel (query rows)
-  bool use_chunk;         // sequences with query_len > 1 go to the chunk kernel
+  int32_t heads_per_wg;   // query heads one VALU decode workgroup handles
+  bool decode_on_mfma;    // decode rows run on the MFMA tile kernel instead of the VALU kernel
+  int32_t chunk_grid;     // workgroups of the chunk kernel (0: no sequence has query_len > 1)
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_prologue(const StepParams& p, hipStream_t stream);
 hipError_t launch_decode(const StepParams& p, const StepPlan& plan, hipStream_t stream);
+hipError_t launch_decode_mfma(const StepParams& p, const StepPlan& plan, hipStream_t stream);
+hipError_t launch_chunk(const StepParams& p, const StepPlan& plan, hipStream_t stream);
 hipError_t launch_reduce(const StepParams& p, const StepPlan& plan, hipStream_t stream);
 bool decode_supported(const StepPlan& plan);
 

@@ -1,0 +1,460 @@
+// MFMA attention tiles over paged KV for gfx950: the chunked-prefill tile and
+// the grouped-query / fp8 decode.
+//
+// Page "Serving LLMs with vLLM: Continuous Batching and PagedAttention
+// Explained", sections "Chunked Prefill" and "Prefill Versus Decode": a step
+// mixes decoding sequences with a chunk of a long prompt whose rows attend
+// causally to the sequence's paged history; section "Attention Over Scattered
+// Blocks": the keys and values are fetched block by block through the table.
+//
+// A work item is (sequence, kv head, column tile, split-context partition).
+// Its 16 columns are (query row, query head) pairs that read the same kv head:
+// column c of the sequence is row c / G, head c % G (G = query heads per kv
+// head), so a decode row with G = 8 fills 8 columns and a prefill chunk of an
+// MHA model fills 16 rows.  Every 16-token block of the partition is one
+// 16x16x16 MFMA step in each direction:
+//   S^T[token][col] = K[token][:] . Q[col][:]          (A = K, B = Q^T)
+//   O^T[dim][col]  += V^T[dim][token] . P^T[token][col] (A = V^T, B = P^T)
+// The D-layout result of the first product (lane l: tokens 4*(l/16)..+3 of
+// column l%16) is exactly the B layout the second product needs, so the
+// softmax weights never leave their lanes.  Head dims are permuted freely
+// inside each contraction so that every lane's operands are contiguous in
+// memory: for S^T lane l reads D/4 consecutive dims of token l%16; for O^T the
+// output dim of (tile j, row m) is m * D/16 + j, so lane l reads D/16
+// consecutive dims of each of its 4 tokens.  fp8 K/V are converted to the
+// query type in registers (exact: every e4m3 value is a bf16 and an f16), and
+// the per-(block, head) scales are folded into the score (K) and the weight (V).
+// Only the softmax weights are rounded on the way into the MFMA; they enter as
+// a 16-bit high part plus a 16-bit residual (two PV MFMAs per tile), so the
+// products keep about 16 significant bits instead of 8.
+#include "pkv_launch.h"
+
+namespace pkv {
+
+constexpr int kTileWaves = 4;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int QT>
+__device__ __forceinline__ f32x4 mfma16(uint2 a, uint2 b, f32x4 c) {
+  if constexpr (QT == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+// two fp8 bytes (low or high half of w) -> two 16-bit values of type QT, packed
+template <int QT, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_16(uint32_t w) {
+  if constexpr (QT == kBF16)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HI));
+}
+
+// two floats -> two 16-bit values of type QT (round to nearest even), packed
+template <int QT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)to_out_bits<QT>(a) | ((uint32_t)to_out_bits<QT>(b) << 16);
+}
+
+template <int QT>
+__device__ __forceinline__ float from_bits(uint16_t u) {
+  if constexpr (QT == kBF16) return __uint_as_float((uint32_t)u << 16);
+  else return (float)__builtin_bit_cast(_Float16, u);
+}
+
+// Softmax weights as the MFMA's 16-bit B operand, split hi + lo so that the
+// product keeps ~16 significant bits: hi = round(w), lo = round(w - hi).
+template <int QT>
+__device__ __forceinline__ void split_weights(const float (&w)[4], uint2& hi, uint2& lo) {
+  uint16_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = to_out_bits<QT>(w[i]);
+    l[i] = to_out_bits<QT>(w[i] - from_bits<QT>(h[i]));
+  }
+  hi = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+  lo = make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
+}
+
+// select 16-bit halves: lo(x), lo(y) or hi(x), hi(y)
+template <bool HI>
+__device__ __forceinline__ uint32_t pick16(uint32_t x, uint32_t y) {
+  return HI ? __builtin_amdgcn_perm(y, x, 0x07060302u) : __builtin_amdgcn_perm(y, x, 0x05040100u);
+}
+
+template <int KV, int D>
+struct TileLay {
+  static constexpr int ELT = (KV == kFP8) ? 1 : 2;
+  static constexpr int ROWB = D * ELT;          // bytes of a token row of one head
+  static constexpr int BLKB = 16 * ROWB;        // bytes of one (block, head)
+  static constexpr int KSTEPS = D / 16;         // MFMA steps of the score product
+  static constexpr int KB = D / 4 * ELT;        // K bytes per lane per block (D/4 dims)
+  static constexpr int KLD = (KB + 15) / 16;    // 16-byte loads of K per lane (KB >= 16)
+  static constexpr int VB = D / 16 * ELT;       // V bytes per lane per token (D/16 dims)
+  static constexpr int DT = D / 16;             // output dim tiles
+  static_assert(KB % 16 == 0, "K slice must be whole 16-byte loads");
+};
+
+template <int VB> struct VVec;
+template <> struct VVec<16> { typedef uint4 T; };
+template <> struct VVec<8> { typedef uint2 T; };
+template <> struct VVec<4> { typedef uint32_t T; };
+
+template <int KV, int D>
+struct BlockRegs {
+  using L = TileLay<KV, D>;
+  uint4 k[L::KLD];
+  typename VVec<L::VB>::T v[4];
+  float ksc, vsc;
+  int limit;     // tokens of the block that exist (0: skip the block)
+};
+
+struct TileItem {
+  int seq, kvh, col0, ncols, part, part_tokens, L, Q, row0, max_parts;
+};
+
+// One work item for the whole workgroup (kTileWaves waves share the
+// partition's blocks: wave w takes blocks w, w + kTileWaves, ...).
+template <int KV, int QT, int D>
+__device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& it, int group,
+                                          float* sm_o, float* sm_m, float* sm_l) {
+  using L = TileLay<KV, D>;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 15;          // column of this lane
+  const int gq = lane >> 4;         // lane group: tokens 4*gq..4*gq+3 / dims slice gq
+  const int col = it.col0 + n;
+  const bool col_ok = col < it.ncols;
+  const int rloc = col_ok ? col / group : 0;
+  const int head = it.kvh * group + (col_ok ? col % group : 0);
+  const int row = it.row0 + rloc;
+  const int pos = it.L - it.Q + rloc;                     // last key this column sees
+  const int last_col = min(it.col0 + 15, it.ncols - 1);
+  const int max_pos = it.L - it.Q + last_col / group;
+  const int tok0 = it.part * it.part_tokens;
+  const int tok1 = min(tok0 + it.part_tokens, max_pos + 1);
+  const int blk_begin = tok0 >> 4;
+  const int blk_end = (tok1 + 15) >> 4;
+
+  // Q^T operand: D/4 consecutive dims of this column's query (zero for unused columns)
+  uint2 qb[L::KSTEPS];
+  {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
+                           ((size_t)row * p.num_q_heads + head) * D + gq * (D / 4);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      uint4 r = col_ok ? reinterpret_cast<const uint4*>(qrow)[c] : make_uint4(0, 0, 0, 0);
+      qb[2 * c] = make_uint2(r.x, r.y);
+      qb[2 * c + 1] = make_uint2(r.z, r.w);
+    }
+  }
+
+  const int32_t* trow = p.tables + (size_t)it.seq * p.max_blocks;
+  const int nb = blk_end - blk_begin;
+  const int cnt = nb > wave ? (nb - wave + kTileWaves - 1) / kTileWaves : 0;   // <= 64
+  const int my_tbl = lane < cnt ? trow[blk_begin + wave + kTileWaves * lane] : -1;
+
+  float m = kMaxSeed, lsum = 0.f;
+  f32x4 o[L::DT];
+#pragma unroll
+  for (int j = 0; j < L::DT; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto issue = [&](int i, BlockRegs<KV, D>& r) {
+    const int b = blk_begin + wave + kTileWaves * i;
+    int phys = __builtin_amdgcn_readlane(my_tbl, i);
+    r.limit = min(16, it.L - b * 16);
+    if ((unsigned)phys >= (unsigned)p.num_blocks) { phys = 0; r.limit = 0; }
+    const uint8_t* kb = p.k_pool + ((size_t)phys * p.num_kv_heads + it.kvh) * L::BLKB;
+    const uint8_t* vb = p.v_pool + ((size_t)phys * p.num_kv_heads + it.kvh) * L::BLKB;
+#pragma unroll
+    for (int c = 0; c < L::KLD; ++c)
+      r.k[c] = *reinterpret_cast<const uint4*>(kb + n * L::ROWB + gq * L::KB + c * 16);
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4)
+      r.v[i4] = *reinterpret_cast<const typename VVec<L::VB>::T*>(
+          vb + (gq * 4 + i4) * L::ROWB + n * L::VB);
+    if constexpr (KV == kFP8) {
+      r.ksc = p.k_scale[(size_t)phys * p.num_kv_heads + it.kvh];
+      r.vsc = p.v_scale[(size_t)phys * p.num_kv_heads + it.kvh];
+    } else {
+      r.ksc = 1.f;
+      r.vsc = 1.f;
+    }
+  };
+
+  auto attend = [&](int i, const BlockRegs<KV, D>& r) {
+    const int b = blk_begin + wave + kTileWaves * i;
+    // K operand in the query type: KSTEPS pairs of dwords
+    uint32_t kw[2 * L::KSTEPS];
+    if constexpr (KV == kFP8) {
+#pragma unroll
+      for (int c = 0; c < L::KLD; ++c) {
+        const uint32_t w[4] = {r.k[c].x, r.k[c].y, r.k[c].z, r.k[c].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kw[c * 8 + 2 * e] = fp8x2_to_16<QT, false>(w[e]);
+          kw[c * 8 + 2 * e + 1] = fp8x2_to_16<QT, true>(w[e]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < L::KLD; ++c) {
+        kw[4 * c] = r.k[c].x;
+        kw[4 * c + 1] = r.k[c].y;
+        kw[4 * c + 2] = r.k[c].z;
+        kw[4 * c + 3] = r.k[c].w;
+      }
+    }
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < L::KSTEPS; ++st)
+      s = mfma16<QT>(make_uint2(kw[2 * st], kw[2 * st + 1]), qb[st], s);
+
+    const float mul = p.scale_log2 * r.ksc;
+    float sv[4];
+    bool ok[4];
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int t = b * 16 + gq * 4 + i4;
+      ok[i4] = col_ok && (gq * 4 + i4 < r.limit) && (t <= pos);
+      sv[i4] = s[i4] * mul;
+      mx = fmaxf(mx, ok[i4] ? sv[i4] : -__builtin_inff());
+    }
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    float pw[4];
+    float ps = 0.f;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      pw[i4] = ok[i4] ? __builtin_amdgcn_exp2f(sv[i4] - mn) : 0.f;
+      ps += pw[i4];
+    }
+    lsum = lsum * alpha + ps;
+    m = mn;
+#pragma unroll
+    for (int j = 0; j < L::DT; ++j) o[j] *= alpha;
+    const float wv[4] = {pw[0] * r.vsc, pw[1] * r.vsc, pw[2] * r.vsc, pw[3] * r.vsc};
+    uint2 pb_hi, pb_lo;
+    split_weights<QT>(wv, pb_hi, pb_lo);
+
+    // V^T operand: this lane's D/16 dims of its 4 tokens, in the query type.
+    // Tail slots may hold NaN: their weight is 0, but 0 * NaN is NaN, so the
+    // values of tokens past the block's end are replaced by 0 first.
+    uint32_t vw[4][L::DT / 2];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const bool keep = gq * 4 + i4 < r.limit;
+      if constexpr (KV == kFP8) {
+        uint32_t raw[L::VB / 4];
+        if constexpr (L::VB == 8) { raw[0] = r.v[i4].x; raw[1] = r.v[i4].y; }
+        else { raw[0] = r.v[i4]; }
+#pragma unroll
+        for (int e = 0; e < L::VB / 4; ++e) {
+          vw[i4][2 * e] = keep ? fp8x2_to_16<QT, false>(raw[e]) : 0u;
+          vw[i4][2 * e + 1] = keep ? fp8x2_to_16<QT, true>(raw[e]) : 0u;
+        }
+      } else {
+        if constexpr (L::VB == 16) {
+          vw[i4][0] = keep ? r.v[i4].x : 0u;
+          vw[i4][1] = keep ? r.v[i4].y : 0u;
+          vw[i4][2] = keep ? r.v[i4].z : 0u;
+          vw[i4][3] = keep ? r.v[i4].w : 0u;
+        } else {
+          vw[i4][0] = keep ? r.v[i4].x : 0u;
+          vw[i4][1] = keep ? r.v[i4].y : 0u;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < L::DT; ++j) {
+      uint2 a;
+      if (j & 1) {
+        a.x = pick16<true>(vw[0][j / 2], vw[1][j / 2]);
+        a.y = pick16<true>(vw[2][j / 2], vw[3][j / 2]);
+      } else {
+        a.x = pick16<false>(vw[0][j / 2], vw[1][j / 2]);
+        a.y = pick16<false>(vw[2][j / 2], vw[3][j / 2]);
+      }
+      o[j] = mfma16<QT>(a, pb_hi, o[j]);
+      o[j] = mfma16<QT>(a, pb_lo, o[j]);
+    }
+  };
+
+  BlockRegs<KV, D> bufA, bufB;
+  if (cnt > 0) issue(0, bufA);
+  for (int i = 0; i < cnt; i += 2) {
+    if (i + 1 < cnt) issue(i + 1, bufB);
+    attend(i, bufA);
+    if (i + 1 < cnt) {
+      if (i + 2 < cnt) issue(i + 2, bufA);
+      attend(i + 1, bufB);
+    }
+  }
+
+  // the column's running sum is spread over the 4 lane groups
+  lsum += shfl_xor_f(lsum, 16);
+  lsum += shfl_xor_f(lsum, 32);
+
+  // merge the waves through LDS: sm_o[wave][col][dim], sm_m/sm_l[wave][col]
+#pragma unroll
+  for (int j = 0; j < L::DT; ++j)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4)
+      sm_o[(wave * 16 + n) * D + (gq * 4 + i4) * L::DT + j] = o[j][i4];
+  if (gq == 0) {
+    sm_m[wave * 16 + n] = m;
+    sm_l[wave * 16 + n] = lsum;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < 16 * D; t += kTileWaves * 64) {
+    const int c = t / D;
+    const int d = t - c * D;
+    const int cc = it.col0 + c;
+    if (cc >= it.ncols) continue;
+    const int rl = cc / group;
+    const int cpos = it.L - it.Q + rl;
+    if (cpos < tok0) continue;                     // no key of this partition is visible to it
+    float M = sm_m[c];
+#pragma unroll
+    for (int w = 1; w < kTileWaves; ++w) M = fmaxf(M, sm_m[w * 16 + c]);
+    float ls = 0.f, ov = 0.f;
+#pragma unroll
+    for (int w = 0; w < kTileWaves; ++w) {
+      const float f = __builtin_amdgcn_exp2f(sm_m[w * 16 + c] - M);
+      ls = __builtin_fmaf(sm_l[w * 16 + c], f, ls);
+      ov = __builtin_fmaf(sm_o[(w * 16 + c) * D + d], f, ov);
+    }
+    const size_t rh = (size_t)(it.row0 + rl) * p.num_q_heads + it.kvh * group + cc % group;
+    const int nparts = (cpos + it.part_tokens) / it.part_tokens;   // ceil((cpos + 1) / pt)
+    if (nparts == 1) {
+      reinterpret_cast<uint16_t*>(p.out)[rh * D + d] = to_out_bits<QT>(ov / ls);
+    } else {
+      const size_t idx = rh * it.max_parts + it.part;
+      p.part_o[idx * D + d] = ov;
+      if (d == 0) {
+        p.part_ml[idx * 2] = M;
+        p.part_ml[idx * 2 + 1] = ls;
+      }
+    }
+  }
+}
+
+// Decode rows (query_len 1): grid (kv head x column tiles, sequence, partition).
+template <int KV, int QT, int D>
+__global__ __launch_bounds__(kTileWaves * 64) void decode_mfma_kernel(StepParams p) {
+  __shared__ float sm_o[kTileWaves * 16 * D];
+  __shared__ float sm_m[kTileWaves * 16];
+  __shared__ float sm_l[kTileWaves * 16];
+  const int group = p.num_q_heads / p.num_kv_heads;
+  const int tiles = (group + 15) / 16;
+  TileItem it;
+  it.seq = blockIdx.y;
+  it.kvh = blockIdx.x / tiles;
+  it.col0 = (blockIdx.x % tiles) * 16;
+  it.ncols = group;
+  it.part = blockIdx.z;
+  it.part_tokens = p.part_tokens;
+  it.max_parts = p.max_parts;
+  it.Q = 1;
+  if (p.q_start != nullptr) {
+    if (p.q_lens[it.seq] != 1) return;             // prefill chunks go to the chunk kernel
+    it.row0 = p.q_start[it.seq];
+    if (it.row0 < 0 || it.row0 >= p.total_q) return;
+  } else {
+    it.row0 = it.seq;
+  }
+  it.L = p.ctx_lens[it.seq];
+  if (it.part * it.part_tokens >= it.L || it.L > p.max_blocks * 16 ||
+      it.L > p.max_parts * it.part_tokens)
+    return;
+  tile_item<KV, QT, D>(p, it, group, sm_o, sm_m, sm_l);
+}
+
+// Prefill chunks (query_len > 1): the prologue lists (sequence, column tile)
+// entries; workgroups stride over entries x kv heads x partitions.
+template <int KV, int QT, int D>
+__global__ __launch_bounds__(kTileWaves * 64) void chunk_mfma_kernel(StepParams p) {
+  __shared__ float sm_o[kTileWaves * 16 * D];
+  __shared__ float sm_m[kTileWaves * 16];
+  __shared__ float sm_l[kTileWaves * 16];
+  const int group = p.num_q_heads / p.num_kv_heads;
+  const int n_entries = min(*p.chunk_count, p.chunk_capacity);
+  const int per_entry = p.num_kv_heads * p.chunk_max_parts;
+  const long long items = (long long)n_entries * per_entry;
+  for (long long item = blockIdx.x; item < items; item += gridDim.x) {
+    const int e = (int)(item / per_entry);
+    const int rem = (int)(item - (long long)e * per_entry);
+    TileItem it;
+    it.seq = p.chunk_entries[2 * e];
+    it.col0 = p.chunk_entries[2 * e + 1];
+    it.kvh = rem / p.chunk_max_parts;
+    it.part = rem - it.kvh * p.chunk_max_parts;
+    it.part_tokens = p.chunk_part_tokens;
+    it.max_parts = p.max_parts;
+    if ((unsigned)it.seq >= (unsigned)p.num_seqs) continue;
+    it.Q = p.q_lens[it.seq];
+    it.L = p.ctx_lens[it.seq];
+    it.row0 = p.q_start[it.seq];
+    it.ncols = it.Q * group;
+    if (it.Q < 1 || it.Q > it.L || it.L > p.max_blocks * 16 || it.row0 < 0 ||
+        it.row0 + it.Q > p.total_q || it.col0 >= it.ncols)
+      continue;
+    const int last_col = min(it.col0 + 15, it.ncols - 1);
+    const int max_pos = it.L - it.Q + last_col / group;
+    if (it.part * it.part_tokens > max_pos || max_pos + 1 > p.max_parts * it.part_tokens) continue;
+    __syncthreads();                                // LDS of the previous item is free again
+    tile_item<KV, QT, D>(p, it, group, sm_o, sm_m, sm_l);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <int KV, int QT>
+static hipError_t launch_tile(bool chunk, const StepParams& p, int head_dim, dim3 grid,
+                              hipStream_t stream) {
+  const dim3 block(kTileWaves * 64);
+  (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
+  if (head_dim == 128) {
+    if (chunk) hipLaunchKernelGGL((chunk_mfma_kernel<KV, QT, 128>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<KV, QT, 128>), grid, block, 0, stream, p);
+  } else {
+    if (chunk) hipLaunchKernelGGL((chunk_mfma_kernel<KV, QT, 64>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<KV, QT, 64>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+static hipError_t launch_tile_typed(bool chunk, const StepParams& p, const StepPlan& plan,
+                                    dim3 grid, hipStream_t stream) {
+  if (plan.q_dtype == kBF16) {
+    if (plan.kv_dtype == kBF16) return launch_tile<kBF16, kBF16>(chunk, p, plan.head_dim, grid, stream);
+    if (plan.kv_dtype == kFP8) return launch_tile<kFP8, kBF16>(chunk, p, plan.head_dim, grid, stream);
+  } else if (plan.q_dtype == kF16) {
+    if (plan.kv_dtype == kF16) return launch_tile<kF16, kF16>(chunk, p, plan.head_dim, grid, stream);
+    if (plan.kv_dtype == kFP8) return launch_tile<kFP8, kF16>(chunk, p, plan.head_dim, grid, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_mfma(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
+  const int tiles = (plan.group + 15) / 16;
+  const dim3 grid((uint32_t)(p.num_kv_heads * tiles), (uint32_t)p.num_seqs, (uint32_t)p.max_parts);
+  return launch_tile_typed(false, p, plan, grid, stream);
+}
+
+hipError_t launch_chunk(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
+  const dim3 grid((uint32_t)plan.chunk_grid);
+  return launch_tile_typed(true, p, plan, grid, stream);
+}
+
+}  // namespace pkv

@@ -119,6 +119,24 @@ def test_partition_sizes(part_tokens, monkeypatch):
     _check(wl8, _run(wl8, f"fp8_gqa8 part_tokens={part_tokens}"))
 
 
+@pytest.mark.parametrize("path", ["0", "1"])
+@pytest.mark.parametrize("name", ["mha_bf16_d128_ragged", "gqa4_bf16_d128", "fp8_gqa8_bf16q_d128",
+                                  "mha_f16_d64", "fp8_mha_f16q_d64", "gqa16_bf16_d128"])
+def test_decode_paths_forced(name, path, monkeypatch):
+    # "0": the VALU decode kernel, "1": the MFMA tile kernel, for the same inputs
+    monkeypatch.setenv("PKV_DECODE_MFMA", path)
+    wl = _small(seed=sorted(SMALL).index(name) + 300, **SMALL[name])
+    _check(wl, _run(wl, f"{name} decode_mfma={path}"))
+
+
+@pytest.mark.parametrize("chunk_pt", [64, 256, 1024])
+def test_chunk_partition_sizes(chunk_pt, monkeypatch):
+    monkeypatch.setenv("PKV_CHUNK_PART_TOKENS", str(chunk_pt))
+    for name in ("chunk_bf16_d128", "chunk_gqa4_fp8_d128", "chunk_f16_d64"):
+        wl = _small(seed=sorted(SMALL).index(name) + 400, **SMALL[name])
+        _check(wl, _run(wl, f"{name} chunk_part_tokens={chunk_pt}"))
+
+
 def test_single_token_and_full_table_edges():
     # L = 1 everywhere, and L equal to the whole table (max_blocks * 16)
     wl = _small(Hq=4, Hkv=4, D=128, kv=W.BF16, qd=W.BF16, lens=[1, 1, 1], seed=3)
