@@ -113,8 +113,10 @@ __device__ __forceinline__ void attend_block(const uint4 (&kr)[Lay<KV, D>::NL],
     }
     l[g] = l[g] * alpha + ps;
     m[g] = mn;
+    if (__any(alpha != 1.f)) {       // the running max rarely moves after the first blocks
 #pragma unroll
-    for (int e = 0; e < T::EPL; ++e) acc[g][e] *= alpha;
+      for (int e = 0; e < T::EPL; ++e) acc[g][e] *= alpha;
+    }
   }
 
 #pragma unroll
@@ -167,6 +169,14 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) 
   const int nb = blk_end - blk_begin;
   const int cnt = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;   // <= 64 by construction
   const int my_tbl = lane < cnt ? trow[blk_begin + wave + kWaves * lane] : -1;
+  // fp8 scales of the same blocks, one per lane (read per block with readlane)
+  float my_ks = 1.f, my_vs = 1.f;
+  if constexpr (KV == kFP8) {
+    if ((unsigned)my_tbl < (unsigned)p.num_blocks) {
+      my_ks = p.k_scale[(size_t)my_tbl * p.num_kv_heads + kvh];
+      my_vs = p.v_scale[(size_t)my_tbl * p.num_kv_heads + kvh];
+    }
+  }
 
   // this lane's slice of the GB query vectors: raw 16-bit pairs for the dot2
   // path (the score is scaled afterwards), fp32 pre-scaled into log2 units otherwise
@@ -206,14 +216,19 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) 
 
   const int rg = lane / T::LPR;                  // token row group of this lane
   // Two register buffers: the loads of block i+1 are in flight while block i is
-  // scored.  An out-of-range table entry reads block 0 and counts no tokens.
+  // scored.  Every iteration issues the same loads with no branch around them
+  // (past the wave's last block the index is clamped and the block counts no
+  // tokens), so the compiler can wait for exactly the block it needs instead of
+  // draining every outstanding load at a control-flow join.  An out-of-range
+  // table entry reads block 0 and counts no tokens.
   uint4 kA[T::NL], vA[T::NL], kB[T::NL], vB[T::NL];
   float kscA = 1.f, vscA = 1.f, kscB = 1.f, vscB = 1.f;
   int limA = 0, limB = 0;
   auto issue = [&](int i, uint4 (&kr)[T::NL], uint4 (&vr)[T::NL], float& ks, float& vs, int& lim) {
-    const int b = blk_begin + wave + kWaves * i;
-    int phys = __builtin_amdgcn_readlane(my_tbl, i);
-    lim = min(16, L - b * 16);
+    const int ic = min(i, cnt - 1);
+    const int b = blk_begin + wave + kWaves * ic;
+    int phys = __builtin_amdgcn_readlane(my_tbl, ic);
+    lim = i < cnt ? min(16, L - b * 16) : 0;
     if ((unsigned)phys >= (unsigned)p.num_blocks) { phys = 0; lim = 0; }
     const size_t boff = ((size_t)phys * p.num_kv_heads + kvh) * T::BLKB;
     const uint4* kb = reinterpret_cast<const uint4*>(p.k_pool + boff);
@@ -223,17 +238,17 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) 
 #pragma unroll
     for (int j = 0; j < T::NL; ++j) vr[j] = vb[j * 64 + lane];
     if constexpr (KV == kFP8) {
-      ks = p.k_scale[(size_t)phys * p.num_kv_heads + kvh];
-      vs = p.v_scale[(size_t)phys * p.num_kv_heads + kvh];
+      ks = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_ks), ic));
+      vs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_vs), ic));
     }
   };
 
-  if (cnt > 0) issue(0, kA, vA, kscA, vscA, limA);
-  for (int i = 0; i < cnt; i += 2) {
-    if (i + 1 < cnt) issue(i + 1, kB, vB, kscB, vscB, limB);
-    attend_block<KV, QT, D, GB>(kA, vA, kscA, vscA, limA, rg, qp, qf, p.scale_log2, m, l, acc);
-    if (i + 1 < cnt) {
-      if (i + 2 < cnt) issue(i + 2, kA, vA, kscA, vscA, limA);
+  if (cnt > 0) {
+    issue(0, kA, vA, kscA, vscA, limA);
+    for (int i = 0; i < cnt; i += 2) {
+      issue(i + 1, kB, vB, kscB, vscB, limB);
+      attend_block<KV, QT, D, GB>(kA, vA, kscA, vscA, limA, rg, qp, qf, p.scale_log2, m, l, acc);
+      issue(i + 2, kA, vA, kscA, vscA, limA);
       attend_block<KV, QT, D, GB>(kB, vB, kscB, vscB, limB, rg, qp, qf, p.scale_log2, m, l, acc);
     }
   }
@@ -364,14 +379,16 @@ __device__ __forceinline__ int block_scan_1024(int v, int32_t* wave_tot) {
 // of 16 (row, head) columns of every sequence with more than one query row.
 // One workgroup; only launched when some sequence has more than one row.
 __global__ __launch_bounds__(1024) void step_prologue_kernel(StepParams p) {
+  constexpr int kBig = 256;                 // long sequences filled by the whole workgroup
   __shared__ int32_t wave_tot[16];
-  __shared__ int32_t carry_rows, carry_tiles;
+  __shared__ int32_t carry_rows, carry_tiles, n_big;
+  __shared__ int32_t big_seq[kBig], big_start[kBig], big_q[kBig], big_tstart[kBig], big_tiles[kBig];
   int32_t* q_start = const_cast<int32_t*>(p.q_start);
   int32_t* row_seq = const_cast<int32_t*>(p.row_seq);
   int32_t* entries = const_cast<int32_t*>(p.chunk_entries);
   const int group = p.num_q_heads / p.num_kv_heads;
   const int tid = threadIdx.x;
-  if (tid == 0) { carry_rows = 0; carry_tiles = 0; }
+  if (tid == 0) { carry_rows = 0; carry_tiles = 0; n_big = 0; }
   __syncthreads();
   for (int base = 0; base < p.num_seqs; base += 1024) {
     const int i = base + tid;
@@ -381,17 +398,41 @@ __global__ __launch_bounds__(1024) void step_prologue_kernel(StepParams p) {
     const int t_incl = block_scan_1024(tiles, wave_tot);
     const int start = carry_rows + r_incl - q;
     const int tstart = carry_tiles + t_incl - tiles;
+    bool serial = true;
     if (i < p.num_seqs) {
       q_start[i] = start;
-      const int stop = min(start + q, p.total_q);
-      for (int r = max(start, 0); r < stop; ++r) row_seq[r] = i;
-      for (int t = 0; t < tiles && tstart + t < p.chunk_capacity; ++t) {
-        entries[2 * (tstart + t)] = i;
-        entries[2 * (tstart + t) + 1] = 16 * t;
+      if (q > 32 || tiles > 8) {
+        const int k = atomicAdd(&n_big, 1);
+        if (k < kBig) {
+          big_seq[k] = i; big_start[k] = start; big_q[k] = q;
+          big_tstart[k] = tstart; big_tiles[k] = tiles;
+          serial = false;
+        }
+      }
+      if (serial) {
+        const int stop = min(start + q, p.total_q);
+        for (int r = max(start, 0); r < stop; ++r) row_seq[r] = i;
+        for (int t = 0; t < tiles && tstart + t < p.chunk_capacity; ++t) {
+          entries[2 * (tstart + t)] = i;
+          entries[2 * (tstart + t) + 1] = 16 * t;
+        }
       }
     }
     __syncthreads();
+    const int nb = min(n_big, kBig);
+    for (int k = 0; k < nb; ++k) {
+      const int st = big_start[k];
+      for (int r = tid; r < big_q[k]; r += 1024)
+        if (st + r >= 0 && st + r < p.total_q) row_seq[st + r] = big_seq[k];
+      for (int t = tid; t < big_tiles[k]; t += 1024)
+        if (big_tstart[k] + t < p.chunk_capacity) {
+          entries[2 * (big_tstart[k] + t)] = big_seq[k];
+          entries[2 * (big_tstart[k] + t) + 1] = 16 * t;
+        }
+    }
+    __syncthreads();
     if (tid == 1023) { carry_rows += r_incl; carry_tiles += t_incl; }
+    if (tid == 0) n_big = 0;
     __syncthreads();
   }
   if (tid == 0) {

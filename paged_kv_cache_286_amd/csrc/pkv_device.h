@@ -143,4 +143,24 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// {v[l], v[l ^ 16]} and {v[l], v[l ^ 32]} in lane-independent order (gfx950
+// v_permlane16_swap / v_permlane32_swap: VALU, no LDS round trip), so both
+// lanes of a pair compute the same max or sum.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(p[0]), __int_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(p[0]), __int_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(p[0]) + __int_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(p[0]) + __int_as_float(p[1]);
+}
+
 }  // namespace pkv

@@ -11,40 +11,45 @@
 // Its 16 columns are (query row, query head) pairs that read the same kv head:
 // column c of the sequence is row c / G, head c % G (G = query heads per kv
 // head), so a decode row with G = 8 fills 8 columns and a prefill chunk of an
-// MHA model fills 16 rows.  Every 16-token block of the partition is one
-// 16x16x16 MFMA step in each direction:
-//   S^T[token][col] = K[token][:] . Q[col][:]          (A = K, B = Q^T)
-//   O^T[dim][col]  += V^T[dim][token] . P^T[token][col] (A = V^T, B = P^T)
+// MHA model fills 16 rows.  Blocks are taken two at a time (32 tokens) and
+// each product is a gfx950 16x16x32 MFMA:
+//   S^T[token][col] = K[token][:] . Q[col][:]          (A = K, B = Q^T), per block
+//   O^T[dim][col]  += V^T[dim][token] . P^T[token][col] (A = V^T, B = P^T), per pair
 // The D-layout result of the first product (lane l: tokens 4*(l/16)..+3 of
-// column l%16) is exactly the B layout the second product needs, so the
-// softmax weights never leave their lanes.  Head dims are permuted freely
-// inside each contraction so that every lane's operands are contiguous in
-// memory: for S^T lane l reads D/4 consecutive dims of token l%16; for O^T the
-// output dim of (tile j, row m) is m * D/16 + j, so lane l reads D/16
-// consecutive dims of each of its 4 tokens.  fp8 K/V are converted to the
+// column l%16, for each block of the pair) is, with the pair's contraction
+// index k = 8*(l/16) + i meaning token 4*(l/16) + i%4 of block i/4, exactly the
+// B layout the second product needs, so the softmax weights never leave their
+// lanes.  Head dims are permuted freely inside each contraction so that every
+// lane's operands are contiguous in memory: for S^T lane l reads D/4
+// consecutive dims of token l%16; for O^T the output dim of (tile j, row m) is
+// m * D/16 + j, so lane l reads D/16 consecutive dims of each of its tokens.  fp8 K/V are converted to the
 // query type in registers (exact: every e4m3 value is a bf16 and an f16), and
 // the per-(block, head) scales are folded into the score (K) and the weight (V).
-// Only the softmax weights are rounded on the way into the MFMA; they enter as
-// a 16-bit high part plus a 16-bit residual (two PV MFMAs per tile), so the
-// products keep about 16 significant bits instead of 8.
+// Only the softmax weights are rounded on the way into the MFMA.  With 16-bit
+// KV they enter as a 16-bit high part plus a 16-bit residual (two PV MFMAs per
+// tile), so the products keep about 16 significant bits instead of 8; with fp8
+// KV the values themselves carry 4 significant bits and the high part alone is
+// well inside the error of the data.
 #include "pkv_launch.h"
 
 namespace pkv {
 
 constexpr int kTileWaves = 4;
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// D[16x16] += A[16x32] B[32x16]; lane l holds A[l%16][8*(l/16)..+7],
+// B[8*(l/16)..+7][l%16] and D[4*(l/16)..+3][l%16]
 template <int QT>
-__device__ __forceinline__ f32x4 mfma16(uint2 a, uint2 b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma32(uint4 a, uint4 b, f32x4 c) {
   if constexpr (QT == kBF16)
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
-                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   else
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
-                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
 // two fp8 bytes (low or high half of w) -> two 16-bit values of type QT, packed
@@ -71,15 +76,15 @@ __device__ __forceinline__ float from_bits(uint16_t u) {
 // Softmax weights as the MFMA's 16-bit B operand, split hi + lo so that the
 // product keeps ~16 significant bits: hi = round(w), lo = round(w - hi).
 template <int QT>
-__device__ __forceinline__ void split_weights(const float (&w)[4], uint2& hi, uint2& lo) {
-  uint16_t h[4], l[4];
+__device__ __forceinline__ void split_weights(const float (&w)[8], uint4& hi, uint4& lo) {
+  uint32_t h[8], l[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     h[i] = to_out_bits<QT>(w[i]);
-    l[i] = to_out_bits<QT>(w[i] - from_bits<QT>(h[i]));
+    l[i] = to_out_bits<QT>(w[i] - from_bits<QT>((uint16_t)h[i]));
   }
-  hi = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
-  lo = make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
+  hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+  lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
 }
 
 // select 16-bit halves: lo(x), lo(y) or hi(x), hi(y)
@@ -93,12 +98,16 @@ struct TileLay {
   static constexpr int ELT = (KV == kFP8) ? 1 : 2;
   static constexpr int ROWB = D * ELT;          // bytes of a token row of one head
   static constexpr int BLKB = 16 * ROWB;        // bytes of one (block, head)
-  static constexpr int KSTEPS = D / 16;         // MFMA steps of the score product
+  static constexpr int KSTEPS = D / 32;         // 16x16x32 MFMA steps of the score product
   static constexpr int KB = D / 4 * ELT;        // K bytes per lane per block (D/4 dims)
-  static constexpr int KLD = (KB + 15) / 16;    // 16-byte loads of K per lane (KB >= 16)
+  static constexpr int KLD = KB / 16;           // 16-byte loads of K per lane
   static constexpr int VB = D / 16 * ELT;       // V bytes per lane per token (D/16 dims)
   static constexpr int DT = D / 16;             // output dim tiles
+  // blocks kept in the register ring (pairs of blocks are consumed together):
+  // fp8 blocks are half as big, so one more pair is kept in flight
+  static constexpr int NBUF = (KV == kFP8) ? 4 : 2;
   static_assert(KB % 16 == 0, "K slice must be whole 16-byte loads");
+  static_assert(NBUF % 2 == 0, "blocks are consumed in pairs");
 };
 
 template <int VB> struct VVec;
@@ -112,7 +121,8 @@ struct BlockRegs {
   uint4 k[L::KLD];
   typename VVec<L::VB>::T v[4];
   float ksc, vsc;
-  int limit;     // tokens of the block that exist (0: skip the block)
+  int limit;     // tokens of the block that exist (0: nothing to score)
+  int base;      // absolute position of the block's first token
 };
 
 struct TileItem {
@@ -127,7 +137,7 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   using L = TileLay<KV, D>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int n = lane & 15;          // column of this lane
+  const int n = lane & 15;          // column of this lane (token row of K it loads)
   const int gq = lane >> 4;         // lane group: tokens 4*gq..4*gq+3 / dims slice gq
   const int col = it.col0 + n;
   const bool col_ok = col < it.ncols;
@@ -143,32 +153,46 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   const int blk_end = (tok1 + 15) >> 4;
 
   // Q^T operand: D/4 consecutive dims of this column's query (zero for unused columns)
-  uint2 qb[L::KSTEPS];
+  uint4 qb[L::KSTEPS];
   {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
-                           ((size_t)row * p.num_q_heads + head) * D + gq * (D / 4);
+    const uint4* qrow = reinterpret_cast<const uint4*>(
+        reinterpret_cast<const uint16_t*>(p.q) + ((size_t)row * p.num_q_heads + head) * D + gq * (D / 4));
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      uint4 r = col_ok ? reinterpret_cast<const uint4*>(qrow)[c] : make_uint4(0, 0, 0, 0);
-      qb[2 * c] = make_uint2(r.x, r.y);
-      qb[2 * c + 1] = make_uint2(r.z, r.w);
-    }
+    for (int c = 0; c < L::KSTEPS; ++c) qb[c] = col_ok ? qrow[c] : make_uint4(0, 0, 0, 0);
   }
 
   const int32_t* trow = p.tables + (size_t)it.seq * p.max_blocks;
   const int nb = blk_end - blk_begin;
   const int cnt = nb > wave ? (nb - wave + kTileWaves - 1) / kTileWaves : 0;   // <= 64
   const int my_tbl = lane < cnt ? trow[blk_begin + wave + kTileWaves * lane] : -1;
+  // fp8 scales of the same blocks, one per lane, read per block with readlane: a
+  // scalar load per block would be waited for together with every prefetched
+  // block's scalar load (scalar loads complete out of order)
+  float my_ks = 1.f, my_vs = 1.f;
+  if constexpr (KV == kFP8) {
+    if ((unsigned)my_tbl < (unsigned)p.num_blocks) {
+      my_ks = p.k_scale[(size_t)my_tbl * p.num_kv_heads + it.kvh];
+      my_vs = p.v_scale[(size_t)my_tbl * p.num_kv_heads + it.kvh];
+    }
+  }
 
   float m = kMaxSeed, lsum = 0.f;
   f32x4 o[L::DT];
 #pragma unroll
   for (int j = 0; j < L::DT; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Every call issues the same loads with no branch around them: past the
+  // wave's last block the index is clamped (an L2 re-read) and the block counts
+  // no tokens, so the compiler can wait for exactly the block it consumes
+  // instead of draining all outstanding loads at a control-flow join.
   auto issue = [&](int i, BlockRegs<KV, D>& r) {
-    const int b = blk_begin + wave + kTileWaves * i;
-    int phys = __builtin_amdgcn_readlane(my_tbl, i);
-    r.limit = min(16, it.L - b * 16);
+    const int ic = min(i, cnt - 1);
+    const int b = blk_begin + wave + kTileWaves * ic;
+    r.base = b * 16;
+    r.ksc = 1.f;
+    r.vsc = 1.f;
+    int phys = __builtin_amdgcn_readlane(my_tbl, ic);
+    r.limit = i < cnt ? min(16, it.L - b * 16) : 0;
     if ((unsigned)phys >= (unsigned)p.num_blocks) { phys = 0; r.limit = 0; }
     const uint8_t* kb = p.k_pool + ((size_t)phys * p.num_kv_heads + it.kvh) * L::BLKB;
     const uint8_t* vb = p.v_pool + ((size_t)phys * p.num_kv_heads + it.kvh) * L::BLKB;
@@ -180,76 +204,36 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
       r.v[i4] = *reinterpret_cast<const typename VVec<L::VB>::T*>(
           vb + (gq * 4 + i4) * L::ROWB + n * L::VB);
     if constexpr (KV == kFP8) {
-      r.ksc = p.k_scale[(size_t)phys * p.num_kv_heads + it.kvh];
-      r.vsc = p.v_scale[(size_t)phys * p.num_kv_heads + it.kvh];
-    } else {
-      r.ksc = 1.f;
-      r.vsc = 1.f;
+      r.ksc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_ks), ic));
+      r.vsc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_vs), ic));
     }
   };
 
-  auto attend = [&](int i, const BlockRegs<KV, D>& r) {
-    const int b = blk_begin + wave + kTileWaves * i;
-    // K operand in the query type: KSTEPS pairs of dwords
-    uint32_t kw[2 * L::KSTEPS];
-    if constexpr (KV == kFP8) {
-#pragma unroll
-      for (int c = 0; c < L::KLD; ++c) {
-        const uint32_t w[4] = {r.k[c].x, r.k[c].y, r.k[c].z, r.k[c].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kw[c * 8 + 2 * e] = fp8x2_to_16<QT, false>(w[e]);
-          kw[c * 8 + 2 * e + 1] = fp8x2_to_16<QT, true>(w[e]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < L::KLD; ++c) {
-        kw[4 * c] = r.k[c].x;
-        kw[4 * c + 1] = r.k[c].y;
-        kw[4 * c + 2] = r.k[c].z;
-        kw[4 * c + 3] = r.k[c].w;
-      }
-    }
+  // S^T for one block: 4 scores (tokens 4*gq..+3) of this lane's column
+  auto scores = [&](const BlockRegs<KV, D>& r) -> f32x4 {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int st = 0; st < L::KSTEPS; ++st)
-      s = mfma16<QT>(make_uint2(kw[2 * st], kw[2 * st + 1]), qb[st], s);
-
-    const float mul = p.scale_log2 * r.ksc;
-    float sv[4];
-    bool ok[4];
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int t = b * 16 + gq * 4 + i4;
-      ok[i4] = col_ok && (gq * 4 + i4 < r.limit) && (t <= pos);
-      sv[i4] = s[i4] * mul;
-      mx = fmaxf(mx, ok[i4] ? sv[i4] : -__builtin_inff());
+    for (int st = 0; st < L::KSTEPS; ++st) {
+      uint4 a;
+      if constexpr (KV == kFP8) {
+        // 8 fp8 dims -> 8 16-bit values: half of a 16-byte load
+        const uint4 raw = r.k[st / 2];
+        const uint32_t w0 = (st & 1) ? raw.z : raw.x;
+        const uint32_t w1 = (st & 1) ? raw.w : raw.y;
+        a = make_uint4(fp8x2_to_16<QT, false>(w0), fp8x2_to_16<QT, true>(w0),
+                       fp8x2_to_16<QT, false>(w1), fp8x2_to_16<QT, true>(w1));
+      } else {
+        a = r.k[st];
+      }
+      s = mfma32<QT>(a, qb[st], s);
     }
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    float pw[4];
-    float ps = 0.f;
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      pw[i4] = ok[i4] ? __builtin_amdgcn_exp2f(sv[i4] - mn) : 0.f;
-      ps += pw[i4];
-    }
-    lsum = lsum * alpha + ps;
-    m = mn;
-#pragma unroll
-    for (int j = 0; j < L::DT; ++j) o[j] *= alpha;
-    const float wv[4] = {pw[0] * r.vsc, pw[1] * r.vsc, pw[2] * r.vsc, pw[3] * r.vsc};
-    uint2 pb_hi, pb_lo;
-    split_weights<QT>(wv, pb_hi, pb_lo);
+    return s;
+  };
 
-    // V^T operand: this lane's D/16 dims of its 4 tokens, in the query type.
-    // Tail slots may hold NaN: their weight is 0, but 0 * NaN is NaN, so the
-    // values of tokens past the block's end are replaced by 0 first.
-    uint32_t vw[4][L::DT / 2];
+  // the 16-bit V values of this lane's 4 tokens of a block; slots past the
+  // block's end may hold NaN and their weight 0 cannot cancel NaN, so they
+  // are replaced by 0
+  auto vvals = [&](const BlockRegs<KV, D>& r, uint32_t (&vw)[4][L::DT / 2]) {
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const bool keep = gq * 4 + i4 < r.limit;
@@ -262,47 +246,107 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
           vw[i4][2 * e] = keep ? fp8x2_to_16<QT, false>(raw[e]) : 0u;
           vw[i4][2 * e + 1] = keep ? fp8x2_to_16<QT, true>(raw[e]) : 0u;
         }
+      } else if constexpr (L::VB == 16) {
+        vw[i4][0] = keep ? r.v[i4].x : 0u;
+        vw[i4][1] = keep ? r.v[i4].y : 0u;
+        vw[i4][2] = keep ? r.v[i4].z : 0u;
+        vw[i4][3] = keep ? r.v[i4].w : 0u;
       } else {
-        if constexpr (L::VB == 16) {
-          vw[i4][0] = keep ? r.v[i4].x : 0u;
-          vw[i4][1] = keep ? r.v[i4].y : 0u;
-          vw[i4][2] = keep ? r.v[i4].z : 0u;
-          vw[i4][3] = keep ? r.v[i4].w : 0u;
-        } else {
-          vw[i4][0] = keep ? r.v[i4].x : 0u;
-          vw[i4][1] = keep ? r.v[i4].y : 0u;
-        }
+        vw[i4][0] = keep ? r.v[i4].x : 0u;
+        vw[i4][1] = keep ? r.v[i4].y : 0u;
       }
-    }
-#pragma unroll
-    for (int j = 0; j < L::DT; ++j) {
-      uint2 a;
-      if (j & 1) {
-        a.x = pick16<true>(vw[0][j / 2], vw[1][j / 2]);
-        a.y = pick16<true>(vw[2][j / 2], vw[3][j / 2]);
-      } else {
-        a.x = pick16<false>(vw[0][j / 2], vw[1][j / 2]);
-        a.y = pick16<false>(vw[2][j / 2], vw[3][j / 2]);
-      }
-      o[j] = mfma16<QT>(a, pb_hi, o[j]);
-      o[j] = mfma16<QT>(a, pb_lo, o[j]);
     }
   };
 
-  BlockRegs<KV, D> bufA, bufB;
-  if (cnt > 0) issue(0, bufA);
-  for (int i = 0; i < cnt; i += 2) {
-    if (i + 1 < cnt) issue(i + 1, bufB);
-    attend(i, bufA);
-    if (i + 1 < cnt) {
-      if (i + 2 < cnt) issue(i + 2, bufA);
-      attend(i + 1, bufB);
+  // online softmax and PV over a pair of blocks (32 tokens)
+  auto attend_pair = [&](const BlockRegs<KV, D>& r0, const BlockRegs<KV, D>& r1) {
+    const f32x4 s0 = scores(r0);
+    const f32x4 s1 = scores(r1);
+    float sv[8];
+    bool ok[8];
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int t = gq * 4 + i4;
+      ok[i4] = col_ok && t < r0.limit && r0.base + t <= pos;
+      ok[4 + i4] = col_ok && t < r1.limit && r1.base + t <= pos;
+      sv[i4] = s0[i4] * (p.scale_log2 * r0.ksc);
+      sv[4 + i4] = s1[i4] * (p.scale_log2 * r1.ksc);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, ok[i] ? sv[i] : -__builtin_inff());
+    mx = max_xor32(max_xor16(mx));
+    const float mn = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    float pw[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pw[i] = ok[i] ? __builtin_amdgcn_exp2f(sv[i] - mn) : 0.f;
+      ps += pw[i];
+    }
+    lsum = lsum * alpha + ps;
+    m = mn;
+    if (__any(alpha != 1.f)) {       // the running max rarely moves after the first blocks
+#pragma unroll
+      for (int j = 0; j < L::DT; ++j) o[j] *= alpha;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pw[i] *= r0.vsc;
+      pw[4 + i] *= r1.vsc;
+    }
+    uint4 pb_hi, pb_lo;
+    split_weights<QT>(pw, pb_hi, pb_lo);
+
+    uint32_t v0[4][L::DT / 2], v1[4][L::DT / 2];
+    vvals(r0, v0);
+    vvals(r1, v1);
+#pragma unroll
+    for (int j = 0; j < L::DT; ++j) {
+      uint4 a;
+      if (j & 1) {
+        a.x = pick16<true>(v0[0][j / 2], v0[1][j / 2]);
+        a.y = pick16<true>(v0[2][j / 2], v0[3][j / 2]);
+        a.z = pick16<true>(v1[0][j / 2], v1[1][j / 2]);
+        a.w = pick16<true>(v1[2][j / 2], v1[3][j / 2]);
+      } else {
+        a.x = pick16<false>(v0[0][j / 2], v0[1][j / 2]);
+        a.y = pick16<false>(v0[2][j / 2], v0[3][j / 2]);
+        a.z = pick16<false>(v1[0][j / 2], v1[1][j / 2]);
+        a.w = pick16<false>(v1[2][j / 2], v1[3][j / 2]);
+      }
+      o[j] = mfma32<QT>(a, pb_hi, o[j]);
+      if constexpr (KV != kFP8) o[j] = mfma32<QT>(a, pb_lo, o[j]);
+    }
+  };
+
+  // register ring: NB/2 - 1 pairs are loading while the current pair is scored;
+  // pairs past the end (at most NB/2 - 1 per wave) are scored fully masked
+  constexpr int NB = L::NBUF;
+  constexpr int NP = NB / 2;
+  BlockRegs<KV, D> buf[NB];
+  if (cnt > 0) {
+    const int npairs = (cnt + 1) / 2;
+#pragma unroll
+    for (int k = 0; k < NP - 1; ++k) {
+      issue(2 * k, buf[2 * k]);
+      issue(2 * k + 1, buf[2 * k + 1]);
+    }
+    for (int q2 = 0; q2 < npairs; q2 += NP) {
+#pragma unroll
+      for (int u = 0; u < NP; ++u) {
+        const int nxt = q2 + u + NP - 1;
+        const int slot = (u + NP - 1) % NP;
+        issue(2 * nxt, buf[2 * slot]);
+        issue(2 * nxt + 1, buf[2 * slot + 1]);
+        attend_pair(buf[2 * u], buf[2 * u + 1]);
+      }
     }
   }
 
   // the column's running sum is spread over the 4 lane groups
-  lsum += shfl_xor_f(lsum, 16);
-  lsum += shfl_xor_f(lsum, 32);
+  lsum = sum_xor32(sum_xor16(lsum));
 
   // merge the waves through LDS: sm_o[wave][col][dim], sm_m/sm_l[wave][col]
 #pragma unroll
