@@ -164,10 +164,11 @@ def main():
 
     value = alg["unique"] / (ms_per_step / 1e3) / 1e9
     roofline = None
-    # the kernel that reads the step's KV: the decode kernel that ran, or the chunk
-    # kernel when prefill rows dominate the time
+    # the kernel that reads the step's KV: the decode kernel that ran, or the fused
+    # prefill + decode kernel of a mixed step
     timed = [k for k in (pk.pkv_kernel_name(pk.PKV_KERNEL_DECODE),
-                         pk.pkv_kernel_name(pk.PKV_KERNEL_DECODE_MFMA)) if k in kernels]
+                         pk.pkv_kernel_name(pk.PKV_KERNEL_DECODE_MFMA),
+                         pk.pkv_kernel_name(pk.PKV_KERNEL_STEP_MFMA)) if k in kernels]
     dom = timed[0] if timed else None
     if dom in kernels:
         achieved = alg["unique"] / (kernels[dom]["avg_us"] / 1e6) / 1e9

@@ -163,7 +163,8 @@ typedef enum pkv_kernel_kind {
   PKV_KERNEL_PROLOGUE = 1,     /* step_prologue_kernel: row offsets, prefill tile list */
   PKV_KERNEL_DECODE = 2,       /* decode_valu_kernel: decode rows, 16-bit KV, <= 2 heads per kv head */
   PKV_KERNEL_REDUCE = 3,       /* split_reduce_kernel */
-  PKV_KERNEL_CHUNK = 4,        /* chunk_mfma_kernel: rows of prefill chunks */
+  PKV_KERNEL_STEP_MFMA = 4,    /* step_mfma_kernel: prefill-chunk tiles and decode rows in one launch
+                                  (steps where some query_len > 1) */
   PKV_KERNEL_DECODE_MFMA = 5,  /* decode_mfma_kernel: grouped-query or fp8 decode rows */
   PKV_KERNEL_KINDS = 6
 } pkv_kernel_kind;

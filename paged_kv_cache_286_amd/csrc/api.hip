@@ -89,13 +89,15 @@ int env_int(const char* name, int dflt) {
   return atoi(s);
 }
 
-// Tokens per split-context partition: about 512 KiB of K+V per workgroup,
-// halved while a step of few, long rows would leave the chip under-filled.
+// Tokens per split-context partition: about 512 KiB (fp8: 1 MiB) of K+V per
+// workgroup, halved while a step of few, long rows would leave the chip
+// under-filled.
 int32_t part_tokens_for(const pkv_pool* pool, int32_t rows, int32_t wg_per_row, int32_t max_ctx) {
   const int forced = env_int("PKV_PART_TOKENS", 0);
   if (forced >= 16 && forced <= 4096 && forced % 16 == 0) return forced;
   const int32_t bytes_per_token = 2 * pool->head_dim * elem_bytes(pool->kv_dtype);
-  int32_t pt = 512 * 1024 / bytes_per_token;
+  // fp8 workgroups run the longer MFMA ring; they amortise their start-up over more bytes
+  int32_t pt = (pool->kv_dtype == PKV_FP8_E4M3 ? 1024 : 512) * 1024 / bytes_per_token;
   pt = std::min(4096, std::max(16, pt));
   while (pt > 64) {
     const int64_t wgs = (int64_t)rows * wg_per_row * ((max_ctx + pt - 1) / pt);
@@ -148,7 +150,7 @@ Layout layout_for(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads, i
                   int32_t max_ctx, int32_t max_q) {
   Layout lay;
   const int32_t group = num_q_heads / pool->num_kv_heads;
-  lay.decode_on_mfma = decode_on_mfma_for(pool, group);
+  lay.decode_on_mfma = max_q > 1 || decode_on_mfma_for(pool, group);
   lay.heads_per_wg = heads_per_wg_for(group);
   const int32_t wg_per_row =
       lay.decode_on_mfma ? pool->num_kv_heads * ((group + 15) / 16) : num_q_heads / lay.heads_per_wg;
@@ -223,7 +225,7 @@ const char* pkv_kernel_name(int32_t kind) {
     case PKV_KERNEL_DECODE: return "decode_valu_kernel";
     case PKV_KERNEL_DECODE_MFMA: return "decode_mfma_kernel";
     case PKV_KERNEL_REDUCE: return "split_reduce_kernel";
-    case PKV_KERNEL_CHUNK: return "chunk_mfma_kernel";
+    case PKV_KERNEL_STEP_MFMA: return "step_mfma_kernel";
     default: return "unknown";
   }
 }
@@ -330,16 +332,20 @@ int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_
     plan.chunk_grid = (int32_t)std::min<int64_t>(items, 2048);
   }
 
+  // Steps with prefill chunks run the chunk tiles and the decode rows in one
+  // MFMA launch so the chunks' matrix work overlaps the decodes' HBM traffic;
+  // decode-only steps pick the VALU or MFMA decode kernel.
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
-  if (multi)
+  if (multi) {
     e = timed_launch(PKV_KERNEL_PROLOGUE, s, [&] { return pkv::launch_prologue(p, s); });
-  if (e == hipSuccess)
+    if (e == hipSuccess)
+      e = timed_launch(PKV_KERNEL_STEP_MFMA, s, [&] { return pkv::launch_step_mfma(p, plan, s); });
+  } else {
     e = plan.decode_on_mfma
             ? timed_launch(PKV_KERNEL_DECODE_MFMA, s, [&] { return pkv::launch_decode_mfma(p, plan, s); })
             : timed_launch(PKV_KERNEL_DECODE, s, [&] { return pkv::launch_decode(p, plan, s); });
-  if (e == hipSuccess && multi)
-    e = timed_launch(PKV_KERNEL_CHUNK, s, [&] { return pkv::launch_chunk(p, plan, s); });
+  }
   if (e == hipSuccess && lay.max_parts > 1)
     e = timed_launch(PKV_KERNEL_REDUCE, s, [&] { return pkv::launch_reduce(p, plan, s); });
   return hip_status(e);

@@ -37,7 +37,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_prologue(const StepParams& p, hipStream_t stream);
 hipError_t launch_decode(const StepParams& p, const StepPlan& plan, hipStream_t stream);
 hipError_t launch_decode_mfma(const StepParams& p, const StepPlan& plan, hipStream_t stream);
-hipError_t launch_chunk(const StepParams& p, const StepPlan& plan, hipStream_t stream);
+hipError_t launch_step_mfma(const StepParams& p, const StepPlan& plan, hipStream_t stream);
 hipError_t launch_reduce(const StepParams& p, const StepPlan& plan, hipStream_t stream);
 bool decode_supported(const StepPlan& plan);
 

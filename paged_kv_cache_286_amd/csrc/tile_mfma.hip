@@ -392,25 +392,24 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   }
 }
 
-// Decode rows (query_len 1): grid (kv head x column tiles, sequence, partition).
+// Decode rows (query_len 1): one work item per (kv head x column tile,
+// sequence, partition) coordinate.
 template <int KV, int QT, int D>
-__global__ __launch_bounds__(kTileWaves * 64) void decode_mfma_kernel(StepParams p) {
-  __shared__ float sm_o[kTileWaves * 16 * D];
-  __shared__ float sm_m[kTileWaves * 16];
-  __shared__ float sm_l[kTileWaves * 16];
+__device__ __forceinline__ void decode_wg(const StepParams& p, int x, int seq, int part,
+                                          float* sm_o, float* sm_m, float* sm_l) {
   const int group = p.num_q_heads / p.num_kv_heads;
   const int tiles = (group + 15) / 16;
   TileItem it;
-  it.seq = blockIdx.y;
-  it.kvh = blockIdx.x / tiles;
-  it.col0 = (blockIdx.x % tiles) * 16;
+  it.seq = seq;
+  it.kvh = x / tiles;
+  it.col0 = (x % tiles) * 16;
   it.ncols = group;
-  it.part = blockIdx.z;
+  it.part = part;
   it.part_tokens = p.part_tokens;
   it.max_parts = p.max_parts;
   it.Q = 1;
   if (p.q_start != nullptr) {
-    if (p.q_lens[it.seq] != 1) return;             // prefill chunks go to the chunk kernel
+    if (p.q_lens[it.seq] != 1) return;             // prefill chunks are chunk work items
     it.row0 = p.q_start[it.seq];
     if (it.row0 < 0 || it.row0 >= p.total_q) return;
   } else {
@@ -424,17 +423,16 @@ __global__ __launch_bounds__(kTileWaves * 64) void decode_mfma_kernel(StepParams
 }
 
 // Prefill chunks (query_len > 1): the prologue lists (sequence, column tile)
-// entries; workgroups stride over entries x kv heads x partitions.
+// entries; `nwg` workgroups starting at `wg` stride over entries x kv heads x
+// partitions.
 template <int KV, int QT, int D>
-__global__ __launch_bounds__(kTileWaves * 64) void chunk_mfma_kernel(StepParams p) {
-  __shared__ float sm_o[kTileWaves * 16 * D];
-  __shared__ float sm_m[kTileWaves * 16];
-  __shared__ float sm_l[kTileWaves * 16];
+__device__ __forceinline__ void chunk_wgs(const StepParams& p, int wg, int nwg, float* sm_o,
+                                          float* sm_m, float* sm_l) {
   const int group = p.num_q_heads / p.num_kv_heads;
   const int n_entries = min(*p.chunk_count, p.chunk_capacity);
   const int per_entry = p.num_kv_heads * p.chunk_max_parts;
   const long long items = (long long)n_entries * per_entry;
-  for (long long item = blockIdx.x; item < items; item += gridDim.x) {
+  for (long long item = wg; item < items; item += nwg) {
     const int e = (int)(item / per_entry);
     const int rem = (int)(item - (long long)e * per_entry);
     TileItem it;
@@ -460,32 +458,77 @@ __global__ __launch_bounds__(kTileWaves * 64) void chunk_mfma_kernel(StepParams 
   }
 }
 
+// Decode rows only: grid (kv head x column tiles, sequence, partition).
+template <int KV, int QT, int D>
+__global__ __launch_bounds__(kTileWaves * 64) void decode_mfma_kernel(StepParams p) {
+  __shared__ float sm_o[kTileWaves * 16 * D];
+  __shared__ float sm_m[kTileWaves * 16];
+  __shared__ float sm_l[kTileWaves * 16];
+  decode_wg<KV, QT, D>(p, blockIdx.x, blockIdx.y, blockIdx.z, sm_o, sm_m, sm_l);
+}
+
+// A step with prefill chunks: one launch runs the chunk work items and the
+// decode work items, interleaved in dispatch order (one chunk workgroup every
+// `stride` ids) so that the chunks' MFMA work overlaps the decode rows' HBM
+// traffic across the whole launch.  Decode ids decode as x fastest, then
+// sequence, then partition.
+template <int KV, int QT, int D>
+__global__ __launch_bounds__(kTileWaves * 64) void step_mfma_kernel(StepParams p, int n_chunk_wgs,
+                                                                   int stride, int dec_x, int dec_y) {
+  __shared__ float sm_o[kTileWaves * 16 * D];
+  __shared__ float sm_m[kTileWaves * 16];
+  __shared__ float sm_l[kTileWaves * 16];
+  const int b = blockIdx.x;
+  const int k = b / stride;
+  const int r = b - k * stride;
+  int id;
+  if (k < n_chunk_wgs) {
+    if (r == 0) {
+      chunk_wgs<KV, QT, D>(p, k, n_chunk_wgs, sm_o, sm_m, sm_l);
+      return;
+    }
+    id = k * (stride - 1) + (r - 1);
+  } else {
+    id = n_chunk_wgs * (stride - 1) + (b - n_chunk_wgs * stride);
+  }
+  const int x = id % dec_x;
+  const int y = (id / dec_x) % dec_y;
+  const int z = id / (dec_x * dec_y);
+  decode_wg<KV, QT, D>(p, x, y, z, sm_o, sm_m, sm_l);
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int KV, int QT>
-static hipError_t launch_tile(bool chunk, const StepParams& p, int head_dim, dim3 grid,
-                              hipStream_t stream) {
+template <int KV, int QT, int D>
+static void launch_tile_kernel(bool step, const StepParams& p, dim3 grid, int n_chunk, int dx,
+                               int dy, hipStream_t stream) {
   const dim3 block(kTileWaves * 64);
+  if (step) {
+    const int stride = n_chunk > 0 ? (int)(grid.x / (uint32_t)n_chunk) : 1;
+    hipLaunchKernelGGL((step_mfma_kernel<KV, QT, D>), grid, block, 0, stream, p, n_chunk, stride,
+                       dx, dy);
+  } else
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, QT, D>), grid, block, 0, stream, p);
+}
+
+template <int KV, int QT>
+static hipError_t launch_tile(bool step, const StepParams& p, int head_dim, dim3 grid, int n_chunk,
+                              int dx, int dy, hipStream_t stream) {
   (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
-  if (head_dim == 128) {
-    if (chunk) hipLaunchKernelGGL((chunk_mfma_kernel<KV, QT, 128>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<KV, QT, 128>), grid, block, 0, stream, p);
-  } else {
-    if (chunk) hipLaunchKernelGGL((chunk_mfma_kernel<KV, QT, 64>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<KV, QT, 64>), grid, block, 0, stream, p);
-  }
+  if (head_dim == 128) launch_tile_kernel<KV, QT, 128>(step, p, grid, n_chunk, dx, dy, stream);
+  else launch_tile_kernel<KV, QT, 64>(step, p, grid, n_chunk, dx, dy, stream);
   return hipGetLastError();
 }
 
-static hipError_t launch_tile_typed(bool chunk, const StepParams& p, const StepPlan& plan,
-                                    dim3 grid, hipStream_t stream) {
+static hipError_t launch_tile_typed(bool step, const StepParams& p, const StepPlan& plan, dim3 grid,
+                                    int n_chunk, int dx, int dy, hipStream_t stream) {
   if (plan.q_dtype == kBF16) {
-    if (plan.kv_dtype == kBF16) return launch_tile<kBF16, kBF16>(chunk, p, plan.head_dim, grid, stream);
-    if (plan.kv_dtype == kFP8) return launch_tile<kFP8, kBF16>(chunk, p, plan.head_dim, grid, stream);
+    if (plan.kv_dtype == kBF16) return launch_tile<kBF16, kBF16>(step, p, plan.head_dim, grid, n_chunk, dx, dy, stream);
+    if (plan.kv_dtype == kFP8) return launch_tile<kFP8, kBF16>(step, p, plan.head_dim, grid, n_chunk, dx, dy, stream);
   } else if (plan.q_dtype == kF16) {
-    if (plan.kv_dtype == kF16) return launch_tile<kF16, kF16>(chunk, p, plan.head_dim, grid, stream);
-    if (plan.kv_dtype == kFP8) return launch_tile<kFP8, kF16>(chunk, p, plan.head_dim, grid, stream);
+    if (plan.kv_dtype == kF16) return launch_tile<kF16, kF16>(step, p, plan.head_dim, grid, n_chunk, dx, dy, stream);
+    if (plan.kv_dtype == kFP8) return launch_tile<kFP8, kF16>(step, p, plan.head_dim, grid, n_chunk, dx, dy, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -493,12 +536,17 @@ static hipError_t launch_tile_typed(bool chunk, const StepParams& p, const StepP
 hipError_t launch_decode_mfma(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
   const int tiles = (plan.group + 15) / 16;
   const dim3 grid((uint32_t)(p.num_kv_heads * tiles), (uint32_t)p.num_seqs, (uint32_t)p.max_parts);
-  return launch_tile_typed(false, p, plan, grid, stream);
+  return launch_tile_typed(false, p, plan, grid, 0, 0, 0, stream);
 }
 
-hipError_t launch_chunk(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
-  const dim3 grid((uint32_t)plan.chunk_grid);
-  return launch_tile_typed(true, p, plan, grid, stream);
+hipError_t launch_step_mfma(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
+  const int tiles = (plan.group + 15) / 16;
+  const int dx = p.num_kv_heads * tiles;
+  const int dy = p.num_seqs;
+  const long long dec = (long long)dx * dy * p.max_parts;
+  const long long total = dec + plan.chunk_grid;
+  if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+  return launch_tile_typed(true, p, plan, dim3((uint32_t)total), plan.chunk_grid, dx, dy, stream);
 }
 
 }  // namespace pkv

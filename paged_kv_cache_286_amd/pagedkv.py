@@ -35,7 +35,7 @@ DTYPE_CODES = {"f16": PKV_F16, "bf16": PKV_BF16, "fp8_e4m3": PKV_FP8_E4M3}
 (PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_WORKSPACE,
  PKV_ERR_UNSUPPORTED, PKV_ERR_HIP) = range(7)
 (PKV_KERNEL_APPEND, PKV_KERNEL_PROLOGUE, PKV_KERNEL_DECODE, PKV_KERNEL_REDUCE,
- PKV_KERNEL_CHUNK, PKV_KERNEL_DECODE_MFMA, PKV_KERNEL_KINDS) = range(7)
+ PKV_KERNEL_STEP_MFMA, PKV_KERNEL_DECODE_MFMA, PKV_KERNEL_KINDS) = range(7)
 
 # every symbol include/pagedkv.h declares
 EXPORTS = ("paged_kv_append", "paged_attn_workspace_bytes", "paged_attn_step",
