@@ -134,14 +134,15 @@ bool decode_on_mfma_for(const pkv_pool* pool, int32_t group) {
 int32_t round16(int64_t x) { return (int32_t)((x + 15) / 16 * 16); }
 
 // Tokens per partition of a prefill-chunk row: no split when the chunk's
-// column tiles already give >= 512 work items, otherwise enough partitions to
-// reach ~1024 items.  At most 4096 (64 blocks per wave).
+// 64-column entries already give >= 128 work items (they share the launch
+// with the decode rows), otherwise enough partitions to reach ~256 items.
+// At most 4096 (256 blocks per wave).
 int32_t chunk_part_tokens_for(int32_t group, int32_t num_kv_heads, int32_t max_ctx, int32_t max_q) {
   const int forced = env_int("PKV_CHUNK_PART_TOKENS", 0);
   if (forced >= 16 && forced <= 4096 && forced % 16 == 0) return forced;
-  const int64_t tiles = ((int64_t)max_q * group + 15) / 16;
+  const int64_t tiles = ((int64_t)max_q * group + 63) / 64;
   const int64_t items = tiles * num_kv_heads;
-  int64_t parts = items >= 512 ? 1 : (1024 + items - 1) / items;
+  int64_t parts = items >= 128 ? 1 : (256 + items - 1) / items;
   int32_t pt = round16((max_ctx + parts - 1) / parts);
   return std::min(4096, std::max(64, pt));
 }
@@ -161,8 +162,8 @@ Layout layout_for(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads, i
     lay.chunk_part_tokens = chunk_part_tokens_for(group, pool->num_kv_heads, max_ctx, max_q);
     lay.chunk_max_parts = (max_ctx + lay.chunk_part_tokens - 1) / lay.chunk_part_tokens;
     lay.max_parts = std::max(lay.max_parts, lay.chunk_max_parts);
-    // sum over sequences with q > 1 of ceil(q * group / 16) <= total_q * group / 16 + num_seqs
-    lay.chunk_capacity = (int32_t)(((int64_t)total_q * group + 15) / 16 + num_seqs);
+    // sum over sequences with q > 1 of ceil(q * group / 64) <= total_q * group / 64 + num_seqs
+    lay.chunk_capacity = (int32_t)(((int64_t)total_q * group + 63) / 64 + num_seqs);
     lay.q_start_off = off;
     off = round_up(off + sizeof(int32_t) * ((size_t)num_seqs + 1), 256);
     lay.row_seq_off = off;

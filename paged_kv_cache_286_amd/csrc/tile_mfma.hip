@@ -129,9 +129,14 @@ struct TileItem {
   int seq, kvh, col0, ncols, part, part_tokens, L, Q, row0, max_parts;
 };
 
-// One work item for the whole workgroup (kTileWaves waves share the
-// partition's blocks: wave w takes blocks w, w + kTileWaves, ...).
-template <int KV, int QT, int D>
+// One work item for the whole workgroup.  SPLIT (decode rows): the item is
+// one 16-column tile and the kTileWaves waves share the partition's blocks
+// (wave w takes blocks w, w + kTileWaves, ...), merged through LDS at the end.
+// !SPLIT (prefill chunks): the item is kTileWaves tiles of 16 columns, wave w
+// owns tile w and walks every block up to its own causal limit; the four
+// waves read the same blocks at the same time (one fetch beyond L1 serves
+// them all) and each writes its own columns.
+template <int KV, int QT, int D, bool SPLIT>
 __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& it, int group,
                                           float* sm_o, float* sm_m, float* sm_l) {
   using L = TileLay<KV, D>;
@@ -139,13 +144,15 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   const int wave = threadIdx.x >> 6;
   const int n = lane & 15;          // column of this lane (token row of K it loads)
   const int gq = lane >> 4;         // lane group: tokens 4*gq..4*gq+3 / dims slice gq
-  const int col = it.col0 + n;
+  const int tcol0 = SPLIT ? it.col0 : it.col0 + 16 * wave;   // this wave's column tile
+  if (!SPLIT && tcol0 >= it.ncols) return;                  // no columns for this wave
+  const int col = tcol0 + n;
   const bool col_ok = col < it.ncols;
   const int rloc = col_ok ? col / group : 0;
   const int head = it.kvh * group + (col_ok ? col % group : 0);
   const int row = it.row0 + rloc;
   const int pos = it.L - it.Q + rloc;                     // last key this column sees
-  const int last_col = min(it.col0 + 15, it.ncols - 1);
+  const int last_col = min(tcol0 + 15, it.ncols - 1);
   const int max_pos = it.L - it.Q + last_col / group;
   const int tok0 = it.part * it.part_tokens;
   const int tok1 = min(tok0 + it.part_tokens, max_pos + 1);
@@ -161,20 +168,44 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     for (int c = 0; c < L::KSTEPS; ++c) qb[c] = col_ok ? qrow[c] : make_uint4(0, 0, 0, 0);
   }
 
+  // this wave's blocks: blk_begin + first + stride * i, i < cnt
+  constexpr int stride = SPLIT ? kTileWaves : 1;
+  const int first = SPLIT ? wave : 0;
   const int32_t* trow = p.tables + (size_t)it.seq * p.max_blocks;
   const int nb = blk_end - blk_begin;
-  const int cnt = nb > wave ? (nb - wave + kTileWaves - 1) / kTileWaves : 0;   // <= 64
-  const int my_tbl = lane < cnt ? trow[blk_begin + wave + kTileWaves * lane] : -1;
-  // fp8 scales of the same blocks, one per lane, read per block with readlane: a
-  // scalar load per block would be waited for together with every prefetched
-  // block's scalar load (scalar loads complete out of order)
-  float my_ks = 1.f, my_vs = 1.f;
-  if constexpr (KV == kFP8) {
-    if ((unsigned)my_tbl < (unsigned)p.num_blocks) {
-      my_ks = p.k_scale[(size_t)my_tbl * p.num_kv_heads + it.kvh];
-      my_vs = p.v_scale[(size_t)my_tbl * p.num_kv_heads + it.kvh];
+  const int cnt = nb > first ? (nb - first + stride - 1) / stride : 0;   // <= 256 (partition <= 4096)
+  // Table entries (and fp8 scales) of the wave's blocks, lane l holding blocks
+  // l, l+64, l+128, l+192, read per block with readlane.  Loading them up front
+  // keeps scalar loads out of the block loop: a scalar load per block would be
+  // waited for together with every prefetched block's (they complete out of order).
+  constexpr int TW = SPLIT ? 1 : 4;
+  int my_tbl[TW];
+  float my_ks[TW], my_vs[TW];
+#pragma unroll
+  for (int w = 0; w < TW; ++w) {
+    const int i = lane + 64 * w;
+    my_tbl[w] = i < cnt ? trow[blk_begin + first + stride * i] : -1;
+    my_ks[w] = 1.f;
+    my_vs[w] = 1.f;
+    if constexpr (KV == kFP8) {
+      if ((unsigned)my_tbl[w] < (unsigned)p.num_blocks) {
+        my_ks[w] = p.k_scale[(size_t)my_tbl[w] * p.num_kv_heads + it.kvh];
+        my_vs[w] = p.v_scale[(size_t)my_tbl[w] * p.num_kv_heads + it.kvh];
+      }
     }
   }
+  auto lane_word = [&](const int (&a)[TW], int i) -> int {
+    int v = a[0];
+#pragma unroll
+    for (int w = 1; w < TW; ++w) v = (i >> 6) == w ? a[w] : v;
+    return __builtin_amdgcn_readlane(v, i & 63);
+  };
+  auto lane_float = [&](const float (&a)[TW], int i) -> float {
+    float v = a[0];
+#pragma unroll
+    for (int w = 1; w < TW; ++w) v = (i >> 6) == w ? a[w] : v;
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), i & 63));
+  };
 
   float m = kMaxSeed, lsum = 0.f;
   f32x4 o[L::DT];
@@ -187,11 +218,11 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   // instead of draining all outstanding loads at a control-flow join.
   auto issue = [&](int i, BlockRegs<KV, D>& r) {
     const int ic = min(i, cnt - 1);
-    const int b = blk_begin + wave + kTileWaves * ic;
+    const int b = blk_begin + first + stride * ic;
     r.base = b * 16;
     r.ksc = 1.f;
     r.vsc = 1.f;
-    int phys = __builtin_amdgcn_readlane(my_tbl, ic);
+    int phys = lane_word(my_tbl, ic);
     r.limit = i < cnt ? min(16, it.L - b * 16) : 0;
     if ((unsigned)phys >= (unsigned)p.num_blocks) { phys = 0; r.limit = 0; }
     const uint8_t* kb = p.k_pool + ((size_t)phys * p.num_kv_heads + it.kvh) * L::BLKB;
@@ -204,8 +235,8 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
       r.v[i4] = *reinterpret_cast<const typename VVec<L::VB>::T*>(
           vb + (gq * 4 + i4) * L::ROWB + n * L::VB);
     if constexpr (KV == kFP8) {
-      r.ksc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_ks), ic));
-      r.vsc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_vs), ic));
+      r.ksc = lane_float(my_ks, ic);
+      r.vsc = lane_float(my_vs, ic);
     }
   };
 
@@ -348,6 +379,33 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   // the column's running sum is spread over the 4 lane groups
   lsum = sum_xor32(sum_xor16(lsum));
 
+  if constexpr (!SPLIT) {
+    // this wave alone saw its columns' keys of the partition: write them out
+    if (!col_ok || pos < tok0) return;             // no key of this partition is visible
+    const size_t rh = (size_t)row * p.num_q_heads + head;
+    const int nparts = (pos + it.part_tokens) / it.part_tokens;     // ceil((pos + 1) / pt)
+    if (nparts == 1) {
+      const float inv = 1.f / lsum;
+      uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + rh * D;
+#pragma unroll
+      for (int j = 0; j < L::DT; ++j)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) orow[(gq * 4 + i4) * L::DT + j] = to_out_bits<QT>(o[j][i4] * inv);
+    } else {
+      const size_t idx = rh * it.max_parts + it.part;
+      float* po = p.part_o + idx * D;
+#pragma unroll
+      for (int j = 0; j < L::DT; ++j)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) po[(gq * 4 + i4) * L::DT + j] = o[j][i4];
+      if (gq == 0) {
+        p.part_ml[idx * 2] = m;
+        p.part_ml[idx * 2 + 1] = lsum;
+      }
+    }
+    return;
+  }
+
   // merge the waves through LDS: sm_o[wave][col][dim], sm_m/sm_l[wave][col]
 #pragma unroll
   for (int j = 0; j < L::DT; ++j)
@@ -419,12 +477,12 @@ __device__ __forceinline__ void decode_wg(const StepParams& p, int x, int seq, i
   if (it.part * it.part_tokens >= it.L || it.L > p.max_blocks * 16 ||
       it.L > p.max_parts * it.part_tokens)
     return;
-  tile_item<KV, QT, D>(p, it, group, sm_o, sm_m, sm_l);
+  tile_item<KV, QT, D, true>(p, it, group, sm_o, sm_m, sm_l);
 }
 
-// Prefill chunks (query_len > 1): the prologue lists (sequence, column tile)
-// entries; `nwg` workgroups starting at `wg` stride over entries x kv heads x
-// partitions.
+// Prefill chunks (query_len > 1): the prologue lists (sequence, first column)
+// entries of 64 columns each; `nwg` workgroups starting at `wg` stride over
+// entries x kv heads x partitions.
 template <int KV, int QT, int D>
 __device__ __forceinline__ void chunk_wgs(const StepParams& p, int wg, int nwg, float* sm_o,
                                           float* sm_m, float* sm_l) {
@@ -450,11 +508,10 @@ __device__ __forceinline__ void chunk_wgs(const StepParams& p, int wg, int nwg, 
     if (it.Q < 1 || it.Q > it.L || it.L > p.max_blocks * 16 || it.row0 < 0 ||
         it.row0 + it.Q > p.total_q || it.col0 >= it.ncols)
       continue;
-    const int last_col = min(it.col0 + 15, it.ncols - 1);
+    const int last_col = min(it.col0 + 16 * kTileWaves - 1, it.ncols - 1);
     const int max_pos = it.L - it.Q + last_col / group;
     if (it.part * it.part_tokens > max_pos || max_pos + 1 > p.max_parts * it.part_tokens) continue;
-    __syncthreads();                                // LDS of the previous item is free again
-    tile_item<KV, QT, D>(p, it, group, sm_o, sm_m, sm_l);
+    tile_item<KV, QT, D, false>(p, it, group, sm_o, sm_m, sm_l);
   }
 }
 
