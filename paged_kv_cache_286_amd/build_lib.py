@@ -2,8 +2,9 @@
 
     python -m paged_kv_cache_286_amd.build_lib
 
-Every ``csrc/*.hip`` file is compiled by hipcc into ``_build/`` in parallel
-and the objects are linked into ``libpagedkv.so``.  The build always runs
+Every ``csrc/*.hip`` (device and host) and ``csrc/*.cpp`` (host only) file is
+compiled by hipcc into ``_build/`` in parallel and the objects are linked into
+``libpagedkv.so``.  The build always runs
 (no staleness check), so a changed source is always picked up.
 """
 from __future__ import annotations
@@ -36,7 +37,7 @@ def hipcc() -> str:
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
+    obj = os.path.join(BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(HERE, "..", "include"), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -46,7 +47,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     jobs = max(1, min(8, len(srcs), os.cpu_count() or 1))
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))

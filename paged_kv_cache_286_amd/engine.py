@@ -1,0 +1,289 @@
+"""Continuous batching over the paged KV cache: the host step loop.
+
+Page "Why a Second Kind of Engine", section "Continuous batching" (the
+five-step iteration) and page "Serving LLMs with vLLM: Continuous Batching and
+PagedAttention Explained", sections "Schedule Per Step", "What the Scheduler
+Does", "Chunked Prefill", "Growing During Decode", "Shared Prefixes" and
+"Copy-on-Write".  Every step:
+
+1. arrived requests join the waiting queue;
+2. the batch is formed from the running sequences (one query token each while
+   decoding, the next prompt chunk while prefilling) plus as many waiting
+   requests as the free slots, the token budget and the free KV blocks allow;
+3. if the blocks for the step's tokens are short, the most recently admitted
+   sequence is preempted (its blocks released; it is recomputed later);
+4. the step runs: copy-on-write block copies, the KV append of the step's new
+   rows, then attention for every query row (``paged_kv_copy_blocks``,
+   ``paged_kv_append``, ``paged_attn_step``);
+5. finished sequences leave and release their blocks in the same step.
+
+Only the attention layer is modelled: queries, keys and values of the step's
+tokens are seeded random numbers (there are no model weights), so the loop
+measures the scheduler and the paged-KV kernels, not a language model.
+
+Readings: a slot freed by a sequence that finishes in step s is filled in step
+s+1; a request needs ``prompt`` prefill tokens, then emits its first output
+token at the end of its last prefill chunk and one more per decode step, so it
+runs ``output - 1`` decode steps; a preempted request restarts its prefill.
+"""
+from __future__ import annotations
+
+import dataclasses
+from collections import deque
+from typing import Dict, List, Optional
+
+import numpy as np
+
+from . import pagedkv as pk
+
+
+@dataclasses.dataclass
+class Request:
+    rid: int
+    prompt: int                  # prompt tokens
+    output: int                  # output tokens to generate (>= 1)
+    arrival: int = 0             # step at which it arrives
+    parent: int = -1             # request whose first `shared` tokens it shares (prefix sharing)
+    shared: int = 0
+
+
+@dataclasses.dataclass
+class _Seq:
+    req: Request
+    computed: int = 0            # prompt tokens whose K/V is in the cache
+    generated: int = 0           # output tokens emitted
+    admitted_step: int = -1
+    first_token_step: int = -1
+    token_steps: List[int] = dataclasses.field(default_factory=list)
+
+    @property
+    def prefilling(self) -> bool:
+        return self.computed < self.req.prompt
+
+    @property
+    def kv_len(self) -> int:
+        return self.computed + max(0, self.generated - 1)
+
+
+@dataclasses.dataclass
+class StepBatch:
+    """What one step computes: rows in sequence order, ready for the ABI."""
+    step: int
+    seq_ids: np.ndarray          # int64 [S]
+    query_lens: np.ndarray       # int32 [S]
+    context_lens: np.ndarray     # int32 [S]
+    block_tables: np.ndarray     # int32 [S][max_blocks]
+    slot_mapping: np.ndarray     # int32 [sum(query_lens)]
+    copies: np.ndarray           # int32 [k][2] copy-on-write (source, destination)
+    finished: List[int]
+    preempted: List[int]
+
+
+class ContinuousBatcher:
+    """Per-step batch formation over a pkv_bm block manager (host only)."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16, max_seqs: int = 256,
+                 token_budget: int = 2048, max_blocks_per_seq: int = 2048,
+                 policy: str = "continuous"):
+        if policy not in ("continuous", "static"):
+            raise ValueError(policy)
+        self.bm = pk.BlockManager(num_blocks, block_size)
+        self.block_size = block_size
+        self.max_seqs = max_seqs
+        self.budget = token_budget
+        self.max_blocks = max_blocks_per_seq
+        self.policy = policy
+        self.pending: List[Request] = []
+        self.waiting: deque = deque()
+        self.running: List[_Seq] = []
+        self.done: Dict[int, _Seq] = {}
+        self.step_no = 0
+        self.slot_steps = 0          # sum over steps of batch slots (static batching reckoning)
+        self.useful = 0              # output tokens produced
+        self._release: List[int] = []   # finished in the previous step, blocks not yet returned
+
+    # -- requests ---------------------------------------------------------
+    def submit(self, req: Request) -> None:
+        if req.output < 1 or req.prompt < 1:
+            raise ValueError("a request needs a prompt and at least one output token")
+        self.pending.append(req)
+
+    def idle(self) -> bool:
+        return not (self.pending or self.waiting or self.running)
+
+    def run_to_completion(self, max_steps: int = 1_000_000, on_step=None) -> int:
+        """Plan steps until every request has finished; returns the number of steps."""
+        while not self.idle() and self.step_no < max_steps:
+            batch = self.plan()
+            if on_step is not None:
+                on_step(batch)
+        self.flush()
+        return self.step_no
+
+    def flush(self) -> None:
+        """Return the blocks of sequences that finished in the last planned step."""
+        for rid in self._release:
+            self.bm.release(rid)
+        self._release = []
+
+    # -- one step -----------------------------------------------------------
+    def _tokens_for(self, s: _Seq, budget_left: int) -> int:
+        if s.prefilling:
+            return min(s.req.prompt - s.computed, budget_left)
+        return 1
+
+    def _shared_parent_alive(self, req: Request) -> bool:
+        return req.parent >= 0 and any(r.req.rid == req.parent for r in self.running)
+
+    def plan(self) -> StepBatch:
+        """Form the next step's batch and reserve its KV slots (host only)."""
+        # Sequences that finished in the previous step return their blocks now: the
+        # previous step's kernels are already enqueued, and stream order puts
+        # their reads before this step's writes into reused blocks.
+        self.flush()
+        self.step_no += 1
+        step = self.step_no
+        arrived = [r for r in self.pending if r.arrival <= step]
+        self.pending = [r for r in self.pending if r.arrival > step]
+        self.waiting.extend(sorted(arrived, key=lambda r: (r.arrival, r.rid)))
+
+        preempted: List[int] = []
+        while True:
+            budget = self.budget
+            plan: List[tuple] = []
+            for s in self.running:
+                n = self._tokens_for(s, budget)
+                if n > 0:
+                    plan.append((s, n))
+                    budget -= n
+            seqs = [s.req.rid for s, _ in plan]
+            counts = [n for _, n in plan]
+            need = self.bm.blocks_needed(seqs, counts) if seqs else 0
+            if need <= self.bm.free_blocks:
+                break
+            victim = self.running.pop()                 # most recently admitted
+            self.bm.release(victim.req.rid)
+            preempted.append(victim.req.rid)
+            victim.computed, victim.generated = 0, 0
+            victim.token_steps.clear()
+            self.waiting.appendleft(victim.req)
+
+        may_admit = self.policy == "continuous" or not self.running
+        while may_admit and self.waiting and len(self.running) < self.max_seqs and budget > 0:
+            req = self.waiting[0]
+            parent = req.parent if self._shared_parent_alive(req) else -1
+            shared = req.shared if parent >= 0 else 0
+            if parent >= 0:
+                shared = min(shared, self.bm.length(parent), req.prompt - 1)
+            first = min(req.prompt - shared, budget)
+            self.bm.add(req.rid, parent, shared)
+            if self.bm.blocks_needed(seqs + [req.rid], counts + [first]) > self.bm.free_blocks:
+                self.bm.release(req.rid)
+                break
+            self.waiting.popleft()
+            s = _Seq(req, computed=shared, admitted_step=step)
+            self.running.append(s)
+            plan.append((s, first))
+            seqs.append(req.rid)
+            counts.append(first)
+            budget -= first
+
+        slots, copies = self.bm.append(seqs, counts) if seqs else (np.zeros(0, np.int32),
+                                                                    np.zeros((0, 2), np.int32))
+        tables, lens = self.bm.tables(seqs, self.max_blocks) if seqs else (
+            np.zeros((0, self.max_blocks), np.int32), np.zeros(0, np.int32))
+        self.slot_steps += self.max_seqs if self.policy == "static" else len(plan)
+
+        # advance the host state as the step will leave it
+        finished: List[int] = []
+        for s, n in plan:
+            if s.prefilling:
+                s.computed += n
+                if not s.prefilling:
+                    s.generated = 1
+                    s.first_token_step = step
+                    s.token_steps.append(step)
+            else:
+                s.generated += 1
+                s.token_steps.append(step)
+            if s.generated >= s.req.output:
+                finished.append(s.req.rid)
+        self.useful += sum(1 for s, _ in plan if s.token_steps and s.token_steps[-1] == step)
+        for rid in finished:
+            s = next(x for x in self.running if x.req.rid == rid)
+            self.running.remove(s)
+            self.done[rid] = s
+        self._release = list(finished)
+        return StepBatch(step, np.asarray(seqs, np.int64), np.asarray(counts, np.int32),
+                         lens.astype(np.int32), tables, slots.astype(np.int32), copies,
+                         finished, preempted)
+
+
+class DeviceEngine:
+    """Runs planned steps on the GPU through the C ABI (synthetic q / K / V)."""
+
+    def __init__(self, batcher: ContinuousBatcher, num_q_heads: int, num_kv_heads: int,
+                 head_dim: int, dtype: str = "bf16", seed: int = 0, device: str = "cuda:0",
+                 keep_host_mirror: bool = False):
+        import torch
+        self.torch = torch
+        self.b = batcher
+        self.Hq, self.Hkv, self.D = num_q_heads, num_kv_heads, head_dim
+        self.dtype = dtype
+        self.dev = torch.device(device)
+        nb, bs = batcher.bm.num_blocks, batcher.block_size
+        tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+        self.tdt = tdt
+        self.k_pool = torch.zeros((nb, num_kv_heads, bs, head_dim), dtype=tdt, device=self.dev)
+        self.v_pool = torch.zeros_like(self.k_pool)
+        self.pool = pk.make_pool(nb, bs, num_kv_heads, head_dim, dtype)
+        self.code = pk.DTYPE_CODES[dtype]
+        self.gen = torch.Generator(device=self.dev)
+        self.gen.manual_seed(seed)
+        self.scale = float(np.float32(1.0 / np.sqrt(head_dim)))
+        self.mirror = None
+        if keep_host_mirror:
+            self.mirror = (np.zeros((nb, num_kv_heads, bs, head_dim), np.uint16),
+                           np.zeros((nb, num_kv_heads, bs, head_dim), np.uint16))
+        self.last = None
+
+    def run(self, batch: StepBatch, stream=None):
+        """Enqueue one step; returns (q, out) device tensors of the step's rows."""
+        torch = self.torch
+        stream = stream if stream is not None else torch.cuda.current_stream(self.dev)
+        S = len(batch.seq_ids)
+        if S == 0:
+            return None
+        rows = int(batch.query_lens.sum())
+        q = torch.randn((rows, self.Hq, self.D), generator=self.gen, device=self.dev).to(self.tdt)
+        k_new = torch.randn((rows, self.Hkv, self.D), generator=self.gen, device=self.dev).to(self.tdt)
+        v_new = torch.randn((rows, self.Hkv, self.D), generator=self.gen, device=self.dev).to(self.tdt)
+        out = torch.empty_like(q)
+        if len(batch.copies):
+            pairs = torch.from_numpy(np.ascontiguousarray(batch.copies)).to(self.dev)
+            pk.paged_kv_copy_blocks(self.pool, self.k_pool, self.v_pool, None, None, pairs,
+                                    len(batch.copies), stream)
+        slots = torch.from_numpy(batch.slot_mapping).to(self.dev)
+        pk.paged_kv_append(self.pool, self.k_pool, self.v_pool, k_new, v_new, self.code, slots,
+                           rows, stream)
+        tables = torch.from_numpy(batch.block_tables).to(self.dev)
+        ctx = torch.from_numpy(batch.context_lens).to(self.dev)
+        ql = torch.from_numpy(batch.query_lens).to(self.dev)
+        max_ctx, max_q = int(batch.context_lens.max()), int(batch.query_lens.max())
+        ws_bytes = pk.paged_attn_workspace_bytes(self.pool, S, self.Hq, rows, max_ctx, max_q)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=self.dev)
+        pk.paged_attn_step(self.pool, q, self.code, self.Hq, self.k_pool, self.v_pool, None, None,
+                           tables, self.b.max_blocks, ctx, ql, S, rows, max_ctx, max_q, self.scale,
+                           out, ws, ws_bytes, stream)
+        if self.mirror is not None:
+            kb = k_new.view(torch.int16).cpu().numpy().view(np.uint16)
+            vb = v_new.view(torch.int16).cpu().numpy().view(np.uint16)
+            mk, mv = self.mirror
+            for src, dst in batch.copies:
+                mk[dst], mv[dst] = mk[src], mv[src]
+            bs = self.b.block_size
+            for r, sl in enumerate(batch.slot_mapping):
+                mk[sl // bs, :, sl % bs, :] = kb[r]
+                mv[sl // bs, :, sl % bs, :] = vb[r]
+        self.last = (q, out, ws)
+        return q, out

@@ -37,11 +37,14 @@ DTYPE_CODES = {"f16": PKV_F16, "bf16": PKV_BF16, "fp8_e4m3": PKV_FP8_E4M3}
 (PKV_KERNEL_APPEND, PKV_KERNEL_PROLOGUE, PKV_KERNEL_DECODE, PKV_KERNEL_REDUCE,
  PKV_KERNEL_STEP_MFMA, PKV_KERNEL_DECODE_MFMA, PKV_KERNEL_KINDS) = range(7)
 
-# every symbol include/pagedkv.h declares
+# every symbol include/pagedkv.h and include/pagedkv_blocks.h declare
 EXPORTS = ("paged_kv_append", "paged_attn_workspace_bytes", "paged_attn_step",
            "pkv_status_string", "pkv_timing_enable", "pkv_timing_disable",
            "pkv_timing_collect", "pkv_timing_get", "pkv_kernel_name", "pkv_last_hip_error",
-           "pkv_last_hip_error_string")
+           "pkv_last_hip_error_string",
+           "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_free_blocks", "pkv_bm_refcount", "pkv_bm_add",
+           "pkv_bm_blocks_needed", "pkv_bm_append", "pkv_bm_release", "pkv_bm_length",
+           "pkv_bm_tables", "paged_kv_copy_blocks")
 
 
 class PkvPool(ctypes.Structure):
@@ -78,6 +81,32 @@ _lib.pkv_last_hip_error.argtypes = []
 _lib.pkv_last_hip_error.restype = ctypes.c_int
 _lib.pkv_last_hip_error_string.argtypes = []
 _lib.pkv_last_hip_error_string.restype = ctypes.c_char_p
+_I64 = ctypes.c_int64
+_BM = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_lib.pkv_bm_create.argtypes = [_I, _I]
+_lib.pkv_bm_create.restype = _BM
+_lib.pkv_bm_destroy.argtypes = [_BM]
+_lib.pkv_bm_destroy.restype = None
+_lib.pkv_bm_free_blocks.argtypes = [_BM]
+_lib.pkv_bm_free_blocks.restype = ctypes.c_int32
+_lib.pkv_bm_refcount.argtypes = [_BM, _I]
+_lib.pkv_bm_refcount.restype = ctypes.c_int32
+_lib.pkv_bm_add.argtypes = [_BM, _I64, _I64, _I]
+_lib.pkv_bm_add.restype = ctypes.c_int
+_lib.pkv_bm_blocks_needed.argtypes = [_BM, _I64P, _I32P, _I, _I32P]
+_lib.pkv_bm_blocks_needed.restype = ctypes.c_int
+_lib.pkv_bm_append.argtypes = [_BM, _I64P, _I32P, _I, _I32P, _I32P, _I, _I32P]
+_lib.pkv_bm_append.restype = ctypes.c_int
+_lib.pkv_bm_release.argtypes = [_BM, _I64]
+_lib.pkv_bm_release.restype = ctypes.c_int
+_lib.pkv_bm_length.argtypes = [_BM, _I64, _I32P]
+_lib.pkv_bm_length.restype = ctypes.c_int
+_lib.pkv_bm_tables.argtypes = [_BM, _I64P, _I, _I, _I32P, _I32P]
+_lib.pkv_bm_tables.restype = ctypes.c_int
+_lib.paged_kv_copy_blocks.argtypes = [_POOLP, _P, _P, _P, _P, _P, _I, _P]
+_lib.paged_kv_copy_blocks.restype = ctypes.c_int
 _lib.pkv_timing_enable.argtypes = [_I]
 _lib.pkv_timing_enable.restype = ctypes.c_int
 _lib.pkv_timing_disable.argtypes = []
@@ -180,3 +209,96 @@ def pkv_timing_get(kind: int) -> Tuple[float, int]:
     n = ctypes.c_int64(0)
     _check("pkv_timing_get", _lib.pkv_timing_get(int(kind), ctypes.byref(ms), ctypes.byref(n)))
     return float(ms.value), int(n.value)
+
+
+# ----------------------------------------------------------------------------
+# host block manager (include/pagedkv_blocks.h)
+# ----------------------------------------------------------------------------
+def _i64(a):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+    return a, a.ctypes.data_as(_I64P)
+
+
+def _i32(a):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return a, a.ctypes.data_as(_I32P)
+
+
+class BlockManager:
+    """Free list, per-sequence block tables, reference counts, copy-on-write.
+
+    Thin wrapper over the pkv_bm_* functions of the library; sequences are
+    named by int ids chosen by the caller.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._h = _lib.pkv_bm_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise PagedKVError("pkv_bm_create", PKV_ERR_SHAPE)
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            _lib.pkv_bm_destroy(h)
+            self._h = None
+
+    @property
+    def free_blocks(self) -> int:
+        return int(_lib.pkv_bm_free_blocks(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(_lib.pkv_bm_refcount(self._h, int(block)))
+
+    def add(self, seq: int, parent: int = -1, shared_tokens: int = 0) -> None:
+        _check("pkv_bm_add", _lib.pkv_bm_add(self._h, int(seq), int(parent), int(shared_tokens)))
+
+    def blocks_needed(self, seqs, counts) -> int:
+        s, sp = _i64(seqs)
+        c, cp = _i32(counts)
+        out = ctypes.c_int32(0)
+        _check("pkv_bm_blocks_needed",
+               _lib.pkv_bm_blocks_needed(self._h, sp, cp, len(s), ctypes.byref(out)))
+        return int(out.value)
+
+    def append(self, seqs, counts):
+        """Returns (slots int32[sum(counts)], copies int32[k][2] of (source, destination))."""
+        import numpy as np
+        s, sp = _i64(seqs)
+        c, cp = _i32(counts)
+        slots = np.zeros(max(1, int(c.sum())), dtype=np.int32)
+        copies = np.zeros((max(1, len(s)), 2), dtype=np.int32)
+        nc = ctypes.c_int32(0)
+        _check("pkv_bm_append", _lib.pkv_bm_append(
+            self._h, sp, cp, len(s), slots.ctypes.data_as(_I32P), copies.ctypes.data_as(_I32P),
+            len(copies), ctypes.byref(nc)))
+        return slots[:int(c.sum())], copies[:nc.value]
+
+    def release(self, seq: int) -> None:
+        _check("pkv_bm_release", _lib.pkv_bm_release(self._h, int(seq)))
+
+    def length(self, seq: int) -> int:
+        out = ctypes.c_int32(0)
+        _check("pkv_bm_length", _lib.pkv_bm_length(self._h, int(seq), ctypes.byref(out)))
+        return int(out.value)
+
+    def tables(self, seqs, max_blocks: int):
+        """Returns (tables int32[n][max_blocks] padded with -1, lens int32[n])."""
+        import numpy as np
+        s, sp = _i64(seqs)
+        t = np.zeros((max(1, len(s)), int(max_blocks)), dtype=np.int32)
+        lens = np.zeros(max(1, len(s)), dtype=np.int32)
+        _check("pkv_bm_tables", _lib.pkv_bm_tables(self._h, sp, len(s), int(max_blocks),
+                                                   t.ctypes.data_as(_I32P),
+                                                   lens.ctypes.data_as(_I32P)))
+        return t[:len(s)], lens[:len(s)]
+
+
+def paged_kv_copy_blocks(pool: PkvPool, k_pool, v_pool, k_scale, v_scale, pairs, num_pairs: int,
+                         stream=None) -> None:
+    _check("paged_kv_copy_blocks", _lib.paged_kv_copy_blocks(
+        _poolref(pool), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(pairs),
+        int(num_pairs), _stream(stream)))
