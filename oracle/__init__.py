@@ -11,6 +11,6 @@ is "parity unpinned".
 from .paged_kv import (  # noqa: F401
     F16, BF16, FP8,
     attend, decode_bits, dequant_fp8, gather_scales, gather_sequence, kv_append,
-    kv_bytes_per_token, lse_merge, paged_attention, partition_partials, sequence_kv,
-    tolerance_ok,
+    kv_append_quant, kv_bytes_per_token, lse_merge, paged_attention, partition_partials,
+    quantize_e4m3, sequence_kv, tolerance_ok,
 )

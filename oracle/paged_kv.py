@@ -35,6 +35,10 @@ What it computes, and where each step comes from:
   serving-many-users chapter: an 8-bit KV cache.  Read as OCP FP8 E4M3FN with
   one float32 scale per (block, kv head); a stored value is
   ``float32(e4m3(byte) * scale)``.
+* Same sections, quantising on the way in: a 16-bit row appended to an fp8
+  pool is divided by its block's scale and rounded to the nearest E4M3FN value
+  (ties to even, saturating at +-448); a block whose first slot is written
+  takes the caller's per-head scale.
 * Page "Serving LLMs with vLLM ...", section "The KV Cache Is Big": per-token
   KV bytes = 2 x layers x hidden x bytes-per-value.
 * Splitting a long context into partitions and merging their partial softmax
@@ -206,6 +210,56 @@ def kv_append(pool, new_rows: np.ndarray, slot_mapping: np.ndarray, block_size: 
             continue
         out[int(s // block_size), :, int(s % block_size), :] = new_rows[r]
     return out
+
+
+# ----------------------------------------------------------------------------
+# fp8 quantisation on append
+# ----------------------------------------------------------------------------
+def quantize_e4m3(x) -> np.ndarray:
+    """float32 values -> OCP E4M3FN bytes: nearest representable value, ties to the
+    even code (even mantissa), magnitudes beyond 448 saturate to +-448, NaN -> 0x7F."""
+    x = np.asarray(x, dtype=np.float32)
+    codes = np.arange(0x7F)                                   # finite non-negative codes
+    vals = _FP8_TABLE[codes].astype(np.float64)               # increasing
+    a = np.abs(x.astype(np.float64)).ravel()
+    hi = np.searchsorted(vals, a, side="left")                # first value >= a
+    hi = np.minimum(hi, len(vals) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - vals[lo]
+    d_hi = vals[hi] - a
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(codes[lo] % 2 == 0, lo, hi)))
+    pick = np.where(vals[hi] == a, hi, pick)
+    pick = np.where(a >= 448.0, 0x7E, pick)
+    out = codes[pick].astype(np.uint8)
+    out = np.where(np.signbit(x.ravel()), out | 0x80, out).astype(np.uint8)
+    out = np.where(np.isnan(x.ravel()), np.uint8(0x7F), out)
+    return out.reshape(x.shape)
+
+
+def kv_append_quant(pool, scales, new_rows: np.ndarray, new_dtype: str,
+                    slot_mapping: np.ndarray, block_size: int, new_block_scale=None):
+    """Append 16-bit rows into an fp8 pool (copies of pool and scales are returned).
+
+    First, every block whose slot 0 is written takes ``new_block_scale[h]`` as its
+    scale (if given).  Then each row r with slot s >= 0 is divided, in float32, by
+    the scale of its block and head and quantised with :func:`quantize_e4m3`.
+    """
+    out = pool.copy()
+    sc = np.array(scales, dtype=np.float32, copy=True)
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    if new_block_scale is not None:
+        init = np.asarray(new_block_scale, dtype=np.float32)
+        for s in slots:
+            if s >= 0 and s % block_size == 0:
+                sc[s // block_size, :] = init
+    for r, s in enumerate(slots):
+        if s < 0:
+            continue
+        blk, off = int(s // block_size), int(s % block_size)
+        x = decode_bits(new_rows[r], new_dtype).astype(np.float32)          # [Hkv][D], exact
+        q = (x / sc[blk][:, None]).astype(np.float32)                         # float32 division
+        out[blk, :, off, :] = quantize_e4m3(q)
+    return out, sc
 
 
 # ----------------------------------------------------------------------------

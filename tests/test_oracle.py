@@ -414,3 +414,48 @@ def test_fp8_scales_follow_the_block_holding_each_token():
         g = h // 2
         want = (4 * vs[5, g] + 4 * vs[0, g] + 4 * vs[11, g] + 2 * vs[3, g]) / L
         np.testing.assert_allclose(out[0, h], want, rtol=1e-15, atol=0)
+
+
+# ----------------------------------------------------------------------------
+# fp8 quantisation on append
+# ----------------------------------------------------------------------------
+def test_quantize_e4m3_matches_torch_rounding():
+    rng = np.random.default_rng(13)
+    vals = oracle.decode_bits(np.arange(0x7F, dtype=np.uint8), oracle.FP8)
+    mids = (vals[:-1] + vals[1:]) / 2                         # exact ties
+    x = np.concatenate([
+        rng.standard_normal(20000) * 50, rng.standard_normal(5000) * 1e-2, mids, -mids, vals, -vals,
+        np.nextafter(mids, 0), np.nextafter(mids, 1e9), [0.0, -0.0, 1e-12, 2.0 ** -10, 3 * 2.0 ** -11]])
+    x = x.astype(np.float32)
+    want = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.quantize_e4m3(x)
+    assert np.array_equal(got, want)
+
+
+def test_quantize_e4m3_saturates_and_keeps_nan():
+    x = np.array([448.0, 449.0, 463.9, 464.0, 480.0, 1e30, np.inf, -1e30, -np.inf, np.nan],
+                 dtype=np.float32)
+    got = oracle.quantize_e4m3(x)
+    assert got.tolist() == [0x7E] * 7 + [0xFE, 0xFE, 0x7F]
+
+
+def test_quantize_round_trip_of_representable_values():
+    b = np.arange(256, dtype=np.uint8)
+    b = b[(b & 0x7F) != 0x7F]
+    x = oracle.decode_bits(b, oracle.FP8).astype(np.float32)
+    assert np.array_equal(oracle.quantize_e4m3(x), b)
+
+
+def test_kv_append_quant_hand_worked():
+    # block size 2, one head, D=2; scale 0.5 for new blocks; block 1 keeps scale 4
+    pool = np.zeros((2, 1, 2, 2), dtype=np.uint8)
+    sc = np.array([[1.0], [4.0]], dtype=np.float32)
+    rows = np.array([[[1.0, -3.0]], [[1000.0, 2000.0]], [[0.25, 0.0]]], dtype=np.float32)
+    bits = torch.from_numpy(rows).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    out, sc2 = oracle.kv_append_quant(pool, sc, bits, oracle.BF16, np.array([0, 3, 1]), 2,
+                                      new_block_scale=[0.5])
+    assert sc2.tolist() == [[0.5], [4.0]]                 # slot 0 written: block 0 re-scaled
+    d = lambda v: oracle.decode_bits(np.array(v, dtype=np.uint8), oracle.FP8)
+    assert d(out[0, 0, 0]).tolist() == [2.0, -6.0]         # 1/0.5, -3/0.5
+    assert d(out[0, 0, 1]).tolist() == [0.5, 0.0]          # 0.25/0.5
+    assert d(out[1, 0, 1]).tolist() == [256.0, 448.0]      # 1000/4 = 250 -> 256, 2000/4 saturates
