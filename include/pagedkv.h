@@ -96,6 +96,25 @@ int paged_kv_append(const pkv_pool* pool, void* k_pool, void* v_pool,
                     const void* k_new, const void* v_new, int32_t new_dtype,
                     const int32_t* slot_mapping, int32_t num_tokens, void* stream);
 
+/* paged_kv_append_quant -- append 16-bit rows into an fp8-e4m3 pool, quantising
+ * on the way in (the 8-bit cache of "Why a Second Kind of Engine", section "The
+ * memory that concurrency actually costs", filled the way "Growing During
+ * Decode" fills a block).
+ *   k_scale, v_scale  [num_blocks][num_kv_heads] float32 scales of the pools
+ *                     (read, and written for new blocks).
+ *   k_new, v_new      [num_tokens][num_kv_heads][head_dim], new_dtype PKV_F16 or PKV_BF16.
+ *   new_block_k_scale, new_block_v_scale  [num_kv_heads] float32, or both NULL: every
+ *                     block whose slot 0 (offset 0) is written by this call first takes
+ *                     these per-head scales; other rows use their block's stored scale.
+ *   slot_mapping      as paged_kv_append.
+ * Each value is divided by its block's scale in IEEE float32 and rounded to the
+ * nearest E4M3FN value (ties to even), saturating at +-448 (NaN stays NaN).
+ * pool->kv_dtype must be PKV_FP8_E4M3. */
+int paged_kv_append_quant(const pkv_pool* pool, void* k_pool, void* v_pool, float* k_scale,
+                          float* v_scale, const void* k_new, const void* v_new, int32_t new_dtype,
+                          const float* new_block_k_scale, const float* new_block_v_scale,
+                          const int32_t* slot_mapping, int32_t num_tokens, void* stream);
+
 /* paged_attn_workspace_bytes -- device scratch paged_attn_step needs for these
  * host scalars (split-context partial results and query row offsets).  Returns 0
  * if the arguments are invalid. */

@@ -259,6 +259,40 @@ int paged_kv_append(const pkv_pool* pool, void* k_pool, void* v_pool, const void
   return hip_status(timed_launch(PKV_KERNEL_APPEND, s, [&] { return pkv::launch_append(a, s); }));
 }
 
+int paged_kv_append_quant(const pkv_pool* pool, void* k_pool, void* v_pool, float* k_scale,
+                          float* v_scale, const void* k_new, const void* v_new, int32_t new_dtype,
+                          const float* new_block_k_scale, const float* new_block_v_scale,
+                          const int32_t* slot_mapping, int32_t num_tokens, void* stream) {
+  const int st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (pool->kv_dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+  if (new_dtype != PKV_F16 && new_dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  if (num_tokens < 0) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_scale || !v_scale || !k_new || !v_new || !slot_mapping)
+    return PKV_ERR_NULL;
+  if ((new_block_k_scale == nullptr) != (new_block_v_scale == nullptr)) return PKV_ERR_NULL;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
+    return PKV_ERR_SHAPE;
+  pkv::AppendArgs a;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.elem_bytes = 1;
+  a.block_size = pool->block_size;
+  a.num_blocks = pool->num_blocks;
+  const hipStream_t s = (hipStream_t)stream;
+  return hip_status(timed_launch(PKV_KERNEL_APPEND, s, [&] {
+    return pkv::launch_append_quant(a, new_dtype, k_scale, v_scale, new_block_k_scale,
+                                    new_block_v_scale, s);
+  }));
+}
+
 size_t paged_attn_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t total_q_tokens, int32_t max_context_len,
                                   int32_t max_query_len) {

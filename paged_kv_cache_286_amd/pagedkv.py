@@ -44,7 +44,7 @@ EXPORTS = ("paged_kv_append", "paged_attn_workspace_bytes", "paged_attn_step",
            "pkv_last_hip_error_string",
            "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_free_blocks", "pkv_bm_refcount", "pkv_bm_add",
            "pkv_bm_blocks_needed", "pkv_bm_append", "pkv_bm_release", "pkv_bm_length",
-           "pkv_bm_tables", "paged_kv_copy_blocks")
+           "pkv_bm_tables", "paged_kv_copy_blocks", "paged_kv_append_quant")
 
 
 class PkvPool(ctypes.Structure):
@@ -105,6 +105,8 @@ _lib.pkv_bm_length.argtypes = [_BM, _I64, _I32P]
 _lib.pkv_bm_length.restype = ctypes.c_int
 _lib.pkv_bm_tables.argtypes = [_BM, _I64P, _I, _I, _I32P, _I32P]
 _lib.pkv_bm_tables.restype = ctypes.c_int
+_lib.paged_kv_append_quant.argtypes = [_POOLP, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _P]
+_lib.paged_kv_append_quant.restype = ctypes.c_int
 _lib.paged_kv_copy_blocks.argtypes = [_POOLP, _P, _P, _P, _P, _P, _I, _P]
 _lib.paged_kv_copy_blocks.restype = ctypes.c_int
 _lib.pkv_timing_enable.argtypes = [_I]
@@ -158,6 +160,15 @@ def paged_kv_append(pool: PkvPool, k_pool, v_pool, k_new, v_new, new_dtype: int,
                     slot_mapping, num_tokens: int, stream=None) -> None:
     _check("paged_kv_append", _lib.paged_kv_append(
         _poolref(pool), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), int(new_dtype),
+        _ptr(slot_mapping), int(num_tokens), _stream(stream)))
+
+
+def paged_kv_append_quant(pool: PkvPool, k_pool, v_pool, k_scale, v_scale, k_new, v_new,
+                          new_dtype: int, new_block_k_scale, new_block_v_scale, slot_mapping,
+                          num_tokens: int, stream=None) -> None:
+    _check("paged_kv_append_quant", _lib.paged_kv_append_quant(
+        _poolref(pool), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(k_new),
+        _ptr(v_new), int(new_dtype), _ptr(new_block_k_scale), _ptr(new_block_v_scale),
         _ptr(slot_mapping), int(num_tokens), _stream(stream)))
 
 

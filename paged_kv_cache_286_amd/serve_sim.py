@@ -1,0 +1,117 @@
+"""Serve a synthetic arrival trace with continuous batching on one GPU.
+
+    python -m paged_kv_cache_286_amd.serve_sim [--requests 256] [--rate 4] ...
+
+The exercise on the serving-many-users chapter ("Exercises") asks for a
+simulator of the serving loop; this one drives the real paged-KV kernels: each
+step is formed by :class:`engine.ContinuousBatcher` (running decodes, prompt
+chunks under a token budget, admission by free blocks, preemption) and run by
+:class:`engine.DeviceEngine` (copy-on-write, KV append, attention for every
+query row; one attention layer of the 7B shape, synthetic q/K/V).  Requests
+arrive as a Poisson process (``--rate`` per step); prompt and output lengths
+are geometric with the given means.  ``--shared`` requests reuse the first
+``--system`` tokens of a long-lived system-prompt sequence's blocks.
+
+Prints one JSON line: steps, wall time, batch-steps/s, output tokens/s,
+time-to-first-token and inter-token latency percentiles (in steps and ms),
+and the host planning time per step.  A measurement of the scheduler and the
+attention kernels only: no model weights are read.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+import time
+
+import numpy as np
+
+
+def make_trace(n, rate, prompt_mean, output_mean, seed, max_len):
+    rng = np.random.default_rng(seed)
+    gaps = rng.exponential(1.0 / rate, size=n)
+    arrivals = np.floor(np.cumsum(gaps)).astype(int) + 1
+    prompts = np.minimum(rng.geometric(1.0 / prompt_mean, size=n), max_len // 2)
+    outputs = np.minimum(rng.geometric(1.0 / output_mean, size=n), max_len // 2)
+    return arrivals, prompts, outputs
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--requests", type=int, default=256)
+    ap.add_argument("--rate", type=float, default=4.0, help="mean arrivals per step")
+    ap.add_argument("--prompt-mean", type=float, default=600)
+    ap.add_argument("--output-mean", type=float, default=200)
+    ap.add_argument("--system", type=int, default=1500, help="shared system prompt tokens")
+    ap.add_argument("--shared", type=float, default=0.0, help="fraction of requests sharing it")
+    ap.add_argument("--blocks", type=int, default=32768, help="KV pool blocks (16 tokens each)")
+    ap.add_argument("--budget", type=int, default=2048, help="token budget per step")
+    ap.add_argument("--max-seqs", type=int, default=256)
+    ap.add_argument("--heads", type=int, default=32)
+    ap.add_argument("--kv-heads", type=int, default=32)
+    ap.add_argument("--head-dim", type=int, default=128)
+    ap.add_argument("--policy", default="continuous", choices=["continuous", "static"])
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args(argv)
+
+    import torch
+    from .engine import ContinuousBatcher, DeviceEngine, Request
+
+    max_len = 32768
+    b = ContinuousBatcher(args.blocks, 16, args.max_seqs, args.budget, max_len // 16, args.policy)
+    arrivals, prompts, outputs = make_trace(args.requests, args.rate, args.prompt_mean,
+                                            args.output_mean, args.seed, max_len)
+    parent = -1
+    if args.shared > 0:
+        parent = 10 ** 9          # a long-lived sequence holding the system prompt
+        b.submit(Request(parent, prompt=args.system, output=10 ** 7, arrival=0))
+    rng = np.random.default_rng(args.seed + 1)
+    for i in range(args.requests):
+        share = parent >= 0 and rng.random() < args.shared
+        prompt = int(prompts[i]) + (args.system if share else 0)
+        b.submit(Request(i, prompt=prompt, output=int(outputs[i]), arrival=int(arrivals[i]),
+                         parent=parent if share else -1, shared=args.system if share else 0))
+    eng = DeviceEngine(b, args.heads, args.kv_heads, args.head_dim, "bf16", seed=args.seed)
+    stream = torch.cuda.current_stream()
+    host_s = 0.0
+    steps = 0
+    step_end = {}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while steps < 10 ** 6:
+        if all(r.rid == parent for r in b.running) and not b.waiting and not b.pending:
+            break
+        h0 = time.perf_counter()
+        batch = b.plan()
+        host_s += time.perf_counter() - h0
+        eng.run(batch, stream)
+        ev = torch.cuda.Event(enable_timing=False)
+        ev.record(stream)
+        step_end[batch.step] = ev
+        steps += 1
+        if steps % 200 == 0:
+            print(f"[serve_sim] step {steps}: running {len(b.running)}, waiting {len(b.waiting)}, "
+                  f"done {len(b.done)}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    done = [s for rid, s in b.done.items() if rid != parent]
+    out_tokens = sum(s.req.output for s in done)
+    ttft = np.array([s.first_token_step - s.req.arrival + 1 for s in done])
+    itl = np.concatenate([np.diff(s.token_steps) for s in done if len(s.token_steps) > 1] or [[0]])
+    ms_per_step = 1000 * wall / max(1, steps)
+    line = {
+        "steps": steps, "wall_s": round(wall, 3), "batch_steps_per_s": round(steps / wall, 2),
+        "ms_per_step": round(ms_per_step, 4), "host_plan_ms_per_step": round(1000 * host_s / steps, 4),
+        "requests_done": len(done), "output_tokens": out_tokens,
+        "output_tokens_per_s": round(out_tokens / wall, 1),
+        "ttft_steps_p50": float(np.percentile(ttft, 50)), "ttft_steps_p95": float(np.percentile(ttft, 95)),
+        "ttft_ms_p50": round(float(np.percentile(ttft, 50)) * ms_per_step, 3),
+        "itl_steps_p50": float(np.percentile(itl, 50)), "itl_steps_p95": float(np.percentile(itl, 95)),
+        "config": {k: v for k, v in vars(args).items()},
+    }
+    print(json.dumps(line), flush=True)
+    return line
+
+
+if __name__ == "__main__":
+    main()
