@@ -111,9 +111,19 @@ struct Layout {
   size_t q_start_off = 0, row_seq_off = 0, chunk_count_off = 0, chunk_entries_off = 0;
   size_t ml_off = 0, o_off = 0, total = 0;
   int32_t part_tokens = 0, chunk_part_tokens = 0, max_parts = 0, chunk_max_parts = 0;
-  int32_t chunk_capacity = 0, heads_per_wg = 1;
+  int32_t chunk_capacity = 0, heads_per_wg = 1, small_q = 1;
   bool decode_on_mfma = false;
 };
+
+// Sequences whose query_len * G fits one 16-column tile (a decode, or the few
+// rows a speculative-decoding step verifies) run as decode items, their
+// blocks shared by the workgroup's four waves; longer prefill chunks become
+// 64-column chunk entries.
+int32_t small_q_for(int32_t group) {
+  const int forced = env_int("PKV_SMALL_Q", 0);
+  if (forced >= 1 && forced * group <= 16) return forced;
+  return group <= 16 ? std::max(1, 16 / group) : 1;
+}
 
 int32_t heads_per_wg_for(int32_t group) {
   for (int g : {8, 4, 2, 1})
@@ -155,10 +165,12 @@ Layout layout_for(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads, i
   lay.heads_per_wg = heads_per_wg_for(group);
   const int32_t wg_per_row =
       lay.decode_on_mfma ? pool->num_kv_heads * ((group + 15) / 16) : num_q_heads / lay.heads_per_wg;
+  // (the tiles per kv head of small-query sequences only add columns, not blocks)
   lay.part_tokens = part_tokens_for(pool, num_seqs, wg_per_row, max_ctx);
   lay.max_parts = (max_ctx + lay.part_tokens - 1) / lay.part_tokens;
   size_t off = 0;
   if (max_q > 1) {
+    lay.small_q = small_q_for(group);
     lay.chunk_part_tokens = chunk_part_tokens_for(group, pool->num_kv_heads, max_ctx, max_q);
     lay.chunk_max_parts = (max_ctx + lay.chunk_part_tokens - 1) / lay.chunk_part_tokens;
     lay.max_parts = std::max(lay.max_parts, lay.chunk_max_parts);
@@ -361,6 +373,7 @@ int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_
   p.chunk_part_tokens = multi ? lay.chunk_part_tokens : lay.part_tokens;
   p.chunk_max_parts = lay.chunk_max_parts;
   p.chunk_capacity = lay.chunk_capacity;
+  p.small_q = multi ? lay.small_q : 1;
   p.scale_log2 = scale * pkv::kLog2e;
   if (multi) {
     const int64_t items = (int64_t)lay.chunk_capacity * pool->num_kv_heads * lay.chunk_max_parts;

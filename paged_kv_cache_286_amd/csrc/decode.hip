@@ -328,7 +328,7 @@ __global__ __launch_bounds__(64) void split_reduce_kernel(StepParams p) {
     if ((unsigned)seq >= (unsigned)p.num_seqs) return;
     const int qlen = p.q_lens[seq];
     L = p.ctx_lens[seq] - qlen + (row - p.q_start[seq]) + 1;
-    pt = qlen > 1 ? p.chunk_part_tokens : p.part_tokens;
+    pt = qlen > p.small_q ? p.chunk_part_tokens : p.part_tokens;
   } else {
     L = p.ctx_lens[row];
     pt = p.part_tokens;
@@ -376,8 +376,9 @@ __device__ __forceinline__ int block_scan_1024(int v, int32_t* wave_tot) {
 
 // Row offsets of every sequence (exclusive scan of query_lens), the owning
 // sequence of every query row, and the list of (sequence, first column)
-// entries of 64 (row, head) columns of every sequence with more than one
-// query row.
+// entries of 64 (row, head) columns of every sequence with more than small_q
+// query rows (shorter ones, e.g. speculative-decoding verify rows, run as
+// decode items).
 // One workgroup; only launched when some sequence has more than one row.
 __global__ __launch_bounds__(1024) void step_prologue_kernel(StepParams p) {
   constexpr int kBig = 256;                 // long sequences filled by the whole workgroup
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(1024) void step_prologue_kernel(StepParams p) {
   for (int base = 0; base < p.num_seqs; base += 1024) {
     const int i = base + tid;
     const int q = i < p.num_seqs ? max(p.q_lens[i], 0) : 0;
-    const int tiles = q > 1 ? (q * group + 63) / 64 : 0;   // 64-column chunk entries
+    const int tiles = q > p.small_q ? (q * group + 63) / 64 : 0;   // 64-column chunk entries
     const int r_incl = block_scan_1024(q, wave_tot);
     const int t_incl = block_scan_1024(tiles, wave_tot);
     const int start = carry_rows + r_incl - q;

@@ -50,6 +50,7 @@ struct StepParams {
   int32_t chunk_part_tokens; // tokens per partition of a prefill-chunk row (multiple of 16)
   int32_t chunk_max_parts;   // partitions the chunk kernel walks per entry and kv head
   int32_t chunk_capacity;    // room for chunk entries in the workspace
+  int32_t small_q;           // sequences with query_len <= small_q run as decode items
   float scale_log2;          // softmax scale * log2(e)
 };
 

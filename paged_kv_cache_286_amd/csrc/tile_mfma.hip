@@ -450,31 +450,35 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   }
 }
 
-// Decode rows (query_len 1): one work item per (kv head x column tile,
-// sequence, partition) coordinate.
+// Decode rows (and sequences with at most small_q query rows, e.g. the rows a
+// speculative-decoding step verifies): one work item per (kv head x column
+// tile, sequence, partition) coordinate; the sequence's query_len * G columns
+// fill the tiles and the 4 waves share the partition's blocks.
 template <int KV, int QT, int D>
 __device__ __forceinline__ void decode_wg(const StepParams& p, int x, int seq, int part,
                                           float* sm_o, float* sm_m, float* sm_l) {
   const int group = p.num_q_heads / p.num_kv_heads;
-  const int tiles = (group + 15) / 16;
+  const int tiles = (p.small_q * group + 15) / 16;
   TileItem it;
   it.seq = seq;
   it.kvh = x / tiles;
   it.col0 = (x % tiles) * 16;
-  it.ncols = group;
   it.part = part;
   it.part_tokens = p.part_tokens;
   it.max_parts = p.max_parts;
   it.Q = 1;
   if (p.q_start != nullptr) {
-    if (p.q_lens[it.seq] != 1) return;             // prefill chunks are chunk work items
+    it.Q = p.q_lens[it.seq];
+    if (it.Q < 1 || it.Q > p.small_q) return;      // longer prefill chunks are chunk items
     it.row0 = p.q_start[it.seq];
-    if (it.row0 < 0 || it.row0 >= p.total_q) return;
+    if (it.row0 < 0 || it.row0 + it.Q > p.total_q) return;
   } else {
     it.row0 = it.seq;
   }
+  it.ncols = it.Q * group;
+  if (it.col0 >= it.ncols) return;
   it.L = p.ctx_lens[it.seq];
-  if (it.part * it.part_tokens >= it.L || it.L > p.max_blocks * 16 ||
+  if (it.Q > it.L || it.part * it.part_tokens >= it.L || it.L > p.max_blocks * 16 ||
       it.L > p.max_parts * it.part_tokens)
     return;
   tile_item<KV, QT, D, true>(p, it, group, sm_o, sm_m, sm_l);
@@ -591,13 +595,13 @@ static hipError_t launch_tile_typed(bool step, const StepParams& p, const StepPl
 }
 
 hipError_t launch_decode_mfma(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
-  const int tiles = (plan.group + 15) / 16;
+  const int tiles = (p.small_q * plan.group + 15) / 16;
   const dim3 grid((uint32_t)(p.num_kv_heads * tiles), (uint32_t)p.num_seqs, (uint32_t)p.max_parts);
   return launch_tile_typed(false, p, plan, grid, 0, 0, 0, stream);
 }
 
 hipError_t launch_step_mfma(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
-  const int tiles = (plan.group + 15) / 16;
+  const int tiles = (p.small_q * plan.group + 15) / 16;
   const int dx = p.num_kv_heads * tiles;
   const int dy = p.num_seqs;
   const long long dec = (long long)dx * dy * p.max_parts;

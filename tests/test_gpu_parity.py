@@ -93,6 +93,14 @@ SMALL = {
     "chunk_gqa4_fp8_d128": dict(Hq=8, Hkv=2, D=128, kv=W.FP8, qd=W.BF16, lens=[90, 1000, 20],
                                 qlens=[90, 64, 1]),
     "chunk_f16_d64": dict(Hq=4, Hkv=2, D=64, kv=W.F16, qd=W.F16, lens=[17, 600], qlens=[16, 200]),
+    # several query rows per sequence, as a speculative-decoding step verifies
+    "specdec_mha_bf16_d128": dict(Hq=8, Hkv=8, D=128, kv=W.BF16, qd=W.BF16,
+                                  lens=_rng.integers(50, 3000, 10).tolist(),
+                                  qlens=[1, 2, 3, 4, 5, 6, 2, 3, 8, 1]),
+    "specdec_gqa4_fp8_d128": dict(Hq=8, Hkv=2, D=128, kv=W.FP8, qd=W.BF16,
+                                  lens=[40, 900, 1700, 300, 64], qlens=[4, 3, 2, 9, 1]),
+    "specdec_gqa8_bf16_d64": dict(Hq=16, Hkv=2, D=64, kv=W.BF16, qd=W.BF16,
+                                  lens=[33, 500, 2100], qlens=[2, 3, 1]),
 }
 
 
@@ -127,6 +135,15 @@ def test_decode_paths_forced(name, path, monkeypatch):
     monkeypatch.setenv("PKV_DECODE_MFMA", path)
     wl = _small(seed=sorted(SMALL).index(name) + 300, **SMALL[name])
     _check(wl, _run(wl, f"{name} decode_mfma={path}"))
+
+
+@pytest.mark.parametrize("small_q", ["1", "2"])
+def test_multi_row_routing_forced(small_q, monkeypatch):
+    # sequences with <= small_q rows run as decode items, longer ones as chunk entries
+    monkeypatch.setenv("PKV_SMALL_Q", small_q)
+    for name in ("specdec_mha_bf16_d128", "specdec_gqa4_fp8_d128", "chunk_bf16_d128"):
+        wl = _small(seed=sorted(SMALL).index(name) + 500, **SMALL[name])
+        _check(wl, _run(wl, f"{name} small_q={small_q}"))
 
 
 @pytest.mark.parametrize("chunk_pt", [64, 256, 1024])
@@ -313,9 +330,11 @@ def test_append_quant_bit_exact_whole_pool(new_dtype):
     ks = rng.uniform(0.01, 2.0, size=(NB, H)).astype(np.float32)
     vs = rng.uniform(0.01, 2.0, size=(NB, H)).astype(np.float32)
     T = 150
-    slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int32)
-    slots[:6] = [0, 16, 32, 48, 17, 33]                # new blocks 0..3 and rows after them
+    fixed = np.array([0, 16, 32, 48, 17, 33])          # new blocks 0..3 and rows after them
+    rest = rng.choice(np.setdiff1d(np.arange(NB * bs), fixed), size=T - len(fixed), replace=False)
+    slots = np.concatenate([fixed, rest]).astype(np.int32)   # distinct, as the append requires
     slots[rng.random(T) < 0.05] = -1
+    assert len(np.unique(slots[slots >= 0])) == (slots >= 0).sum()
     mags = np.exp(rng.uniform(-12, 9, size=(T, H, 1)))
     x = (rng.standard_normal((T, H, D)) * mags).astype(np.float32)
     x[0, 0, :4] = [1e6, -1e6, 0.0, -0.0]
