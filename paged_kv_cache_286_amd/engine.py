@@ -100,6 +100,8 @@ class ContinuousBatcher:
         self.step_no = 0
         self.slot_steps = 0          # sum over steps of batch slots (static batching reckoning)
         self.useful = 0              # output tokens produced
+        self.preemptions = 0
+        self.cow_copies = 0
         self._release: List[int] = []   # finished in the previous step, blocks not yet returned
 
     # -- requests ---------------------------------------------------------
@@ -164,18 +166,25 @@ class ContinuousBatcher:
             victim = self.running.pop()                 # most recently admitted
             self.bm.release(victim.req.rid)
             preempted.append(victim.req.rid)
+            self.preemptions += 1
             victim.computed, victim.generated = 0, 0
             victim.token_steps.clear()
             self.waiting.appendleft(victim.req)
 
-        may_admit = self.policy == "continuous" or not self.running
-        while may_admit and self.waiting and len(self.running) < self.max_seqs and budget > 0:
+        # Continuous batching admits while this step's token budget lasts.  A static
+        # batch is formed only when the previous one has drained, and then fills
+        # every slot at once; prompts beyond this step's budget are prefilled in
+        # the following steps.
+        static = self.policy == "static"
+        may_admit = not static or not self.running
+        while (may_admit and self.waiting and len(self.running) < self.max_seqs
+               and (budget > 0 or static)):
             req = self.waiting[0]
             parent = req.parent if self._shared_parent_alive(req) else -1
             shared = req.shared if parent >= 0 else 0
             if parent >= 0:
                 shared = min(shared, self.bm.length(parent), req.prompt - 1)
-            first = min(req.prompt - shared, budget)
+            first = min(req.prompt - shared, max(budget, 0))
             self.bm.add(req.rid, parent, shared)
             if self.bm.blocks_needed(seqs + [req.rid], counts + [first]) > self.bm.free_blocks:
                 self.bm.release(req.rid)
@@ -183,13 +192,15 @@ class ContinuousBatcher:
             self.waiting.popleft()
             s = _Seq(req, computed=shared, admitted_step=step)
             self.running.append(s)
-            plan.append((s, first))
-            seqs.append(req.rid)
-            counts.append(first)
-            budget -= first
+            if first > 0:
+                plan.append((s, first))
+                seqs.append(req.rid)
+                counts.append(first)
+                budget -= first
 
         slots, copies = self.bm.append(seqs, counts) if seqs else (np.zeros(0, np.int32),
                                                                     np.zeros((0, 2), np.int32))
+        self.cow_copies += len(copies)
         tables, lens = self.bm.tables(seqs, self.max_blocks) if seqs else (
             np.zeros((0, self.max_blocks), np.int32), np.zeros(0, np.int32))
         self.slot_steps += self.max_seqs if self.policy == "static" else len(plan)

@@ -15,7 +15,8 @@ are geometric with the given means.  ``--shared`` requests reuse the first
 Prints one JSON line: steps, wall time, batch-steps/s, output tokens/s,
 time-to-first-token and inter-token latency percentiles (in steps and ms),
 and the host planning time per step.  A measurement of the scheduler and the
-attention kernels only: no model weights are read.
+attention kernels only: no model weights are read.  ``--dry-run`` plans the
+same steps on the host without touching a GPU (the schedule, not a timing).
 """
 from __future__ import annotations
 
@@ -52,9 +53,9 @@ def main(argv=None):
     ap.add_argument("--head-dim", type=int, default=128)
     ap.add_argument("--policy", default="continuous", choices=["continuous", "static"])
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--dry-run", action="store_true", help="plan on the host only, no GPU")
     args = ap.parse_args(argv)
 
-    import torch
     from .engine import ContinuousBatcher, DeviceEngine, Request
 
     max_len = 32768
@@ -71,28 +72,29 @@ def main(argv=None):
         prompt = int(prompts[i]) + (args.system if share else 0)
         b.submit(Request(i, prompt=prompt, output=int(outputs[i]), arrival=int(arrivals[i]),
                          parent=parent if share else -1, shared=args.system if share else 0))
-    eng = DeviceEngine(b, args.heads, args.kv_heads, args.head_dim, "bf16", seed=args.seed)
-    stream = torch.cuda.current_stream()
+    eng = stream = torch = None
+    if not args.dry_run:
+        import torch
+        eng = DeviceEngine(b, args.heads, args.kv_heads, args.head_dim, "bf16", seed=args.seed)
+        stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
     host_s = 0.0
     steps = 0
-    step_end = {}
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     while steps < 10 ** 6:
-        if all(r.rid == parent for r in b.running) and not b.waiting and not b.pending:
+        if all(s.req.rid == parent for s in b.running) and not b.waiting and not b.pending:
             break
         h0 = time.perf_counter()
         batch = b.plan()
         host_s += time.perf_counter() - h0
-        eng.run(batch, stream)
-        ev = torch.cuda.Event(enable_timing=False)
-        ev.record(stream)
-        step_end[batch.step] = ev
+        if eng is not None:
+            eng.run(batch, stream)
         steps += 1
         if steps % 200 == 0:
             print(f"[serve_sim] step {steps}: running {len(b.running)}, waiting {len(b.waiting)}, "
                   f"done {len(b.done)}", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
+    if torch is not None:
+        torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     done = [s for rid, s in b.done.items() if rid != parent]
     out_tokens = sum(s.req.output for s in done)
@@ -107,6 +109,7 @@ def main(argv=None):
         "ttft_steps_p50": float(np.percentile(ttft, 50)), "ttft_steps_p95": float(np.percentile(ttft, 95)),
         "ttft_ms_p50": round(float(np.percentile(ttft, 50)) * ms_per_step, 3),
         "itl_steps_p50": float(np.percentile(itl, 50)), "itl_steps_p95": float(np.percentile(itl, 95)),
+        "preemptions": b.preemptions, "cow_copies": b.cow_copies,
         "config": {k: v for k, v in vars(args).items()},
     }
     print(json.dumps(line), flush=True)
