@@ -20,6 +20,13 @@
  *   - "What the Scheduler Does": a sequence is admitted only if enough blocks
  *     are free; a sequence can be preempted by releasing its blocks.
  *
+ * Page "Why a Second Kind of Engine", section "Prefix caching" (and the quiz
+ * question there on a request id placed before a shared tool schema): every
+ * full block is keyed by a hash of its own tokens chained with the key of the
+ * block before it; keys map to cached blocks, which are evicted least recently
+ * used first when space runs out, and a new request whose leading blocks match
+ * cached keys takes those blocks instead of prefilling them.
+ *
  * A sequence is named by a caller-chosen int64 id.  All pointers below are HOST
  * memory unless marked device.  Functions return a pkv_status (pagedkv.h);
  * PKV_ERR_SHAPE also reports an unknown or duplicate sequence id and
@@ -47,9 +54,10 @@ typedef struct pkv_block_manager pkv_block_manager;
 pkv_block_manager* pkv_bm_create(int32_t num_blocks, int32_t block_size);
 void pkv_bm_destroy(pkv_block_manager* bm);
 
-/* free blocks; -1 for a NULL manager */
+/* blocks available to new content: free ones plus cached ones that no sequence
+ * holds (those are evicted on demand); -1 for a NULL manager */
 int32_t pkv_bm_free_blocks(const pkv_block_manager* bm);
-/* reference count of a block (0 = free); -1 if out of range */
+/* reference count of a block (0 = free, or cached with no reader); -1 if out of range */
 int32_t pkv_bm_refcount(const pkv_block_manager* bm, int32_t block);
 
 /* pkv_bm_add -- a new sequence `seq`.  parent < 0: empty.  Otherwise the new
@@ -86,6 +94,49 @@ int pkv_bm_length(const pkv_block_manager* bm, int64_t seq, int32_t* len);
  * PKV_ERR_SHAPE if a sequence holds more than max_blocks blocks. */
 int pkv_bm_tables(const pkv_block_manager* bm, const int64_t* seqs, int32_t n, int32_t max_blocks,
                   int32_t* tables, int32_t* lens);
+
+/* ---- prefix cache ------------------------------------------------------------------
+ *
+ * Key of full block i of a token sequence t (block_size B):
+ *   key_i = FNV1a64( le64(key_{i-1}) || le32(t[iB]) || ... || le32(t[iB+B-1]) ),  key_{-1} = 0,
+ * with 64-bit FNV-1a (offset basis 0xcbf29ce484222325, prime 0x100000001b3) over
+ * bytes.  A key therefore depends on every token up to the block's end.  Only
+ * full blocks whose token ids are known are keyed; a lookup also compares the
+ * stored tokens and parent key, so a hash collision can not return a wrong block.
+ * A cached block keeps its key until it is evicted: when the free list is empty,
+ * the least recently released cached block with no reader is reused.  Blocks of
+ * a released sequence join that list tail first, so a prefix's tail goes before
+ * its head.  The K/V a caller writes must be a function of the token prefix alone
+ * (as a model's is) for a cached block to stand in for a prefill. */
+
+/* pkv_bm_enable_prefix_cache -- turn the cache on (before any sequence is added;
+ * PKV_ERR_SHAPE otherwise or if already on).  Costs 4*block_size + 34 bytes of host
+ * memory per block. */
+int pkv_bm_enable_prefix_cache(pkv_block_manager* bm);
+
+/* pkv_bm_add_prompt -- a new sequence whose first num_tokens token ids are known
+ * (tokens, host int32).  With the cache on, the sequence starts with the longest
+ * run of leading full blocks whose keys are cached, one block fewer if that run
+ * covers all num_tokens (at least one token is always left to compute); their
+ * reference counts rise.  *cached_tokens = tokens already in the cache
+ * (a multiple of B); the sequence's length starts there, and the caller appends
+ * the remaining num_tokens - *cached_tokens.  With the cache off: an empty
+ * sequence whose tokens are recorded, *cached_tokens = 0. */
+int pkv_bm_add_prompt(pkv_block_manager* bm, int64_t seq, const int32_t* tokens, int32_t num_tokens,
+                      int32_t* cached_tokens);
+
+/* pkv_bm_extend_tokens -- record the ids of n further tokens of `seq` (e.g. the
+ * ones it generates), so that the blocks they fill become cacheable.  Blocks
+ * already full when their ids arrive are keyed at once. */
+int pkv_bm_extend_tokens(pkv_block_manager* bm, int64_t seq, const int32_t* tokens, int32_t n);
+
+/* pkv_bm_cache_stats -- stats[5]: keyed blocks, of those the evictable ones (no
+ * reader), full prompt blocks looked up, blocks found, blocks evicted. */
+int pkv_bm_cache_stats(const pkv_block_manager* bm, int64_t* stats);
+
+/* pkv_prefix_keys -- keys of the floor(num_tokens / block_size) full blocks of a
+ * token sequence (host memory), as the manager computes them. */
+int pkv_prefix_keys(const int32_t* tokens, int32_t num_tokens, int32_t block_size, uint64_t* keys);
 
 /* paged_kv_copy_blocks -- device copy for copy-on-write ("Copy-on-Write"): for each
  * pair i, block pairs[2i] of both pools (every kv head, every slot) is copied to

@@ -45,6 +45,7 @@ class Request:
     arrival: int = 0             # step at which it arrives
     parent: int = -1             # request whose first `shared` tokens it shares (prefix sharing)
     shared: int = 0
+    tokens: Optional[np.ndarray] = None   # token ids: the prompt's, optionally followed by the output's
 
 
 @dataclasses.dataclass
@@ -55,6 +56,8 @@ class _Seq:
     admitted_step: int = -1
     first_token_step: int = -1
     token_steps: List[int] = dataclasses.field(default_factory=list)
+    keyed: bool = False          # added with its token ids (the prefix cache can key its blocks)
+    cached: int = 0              # prompt tokens found in the prefix cache at admission
 
     @property
     def prefilling(self) -> bool:
@@ -77,6 +80,8 @@ class StepBatch:
     copies: np.ndarray           # int32 [k][2] copy-on-write (source, destination)
     finished: List[int]
     preempted: List[int]
+    positions: np.ndarray = None  # int32 [rows] position of each new row in its sequence
+    token_ids: np.ndarray = None  # int32 [rows] its token id, -1 where the request gave none
 
 
 class ContinuousBatcher:
@@ -84,10 +89,10 @@ class ContinuousBatcher:
 
     def __init__(self, num_blocks: int, block_size: int = 16, max_seqs: int = 256,
                  token_budget: int = 2048, max_blocks_per_seq: int = 2048,
-                 policy: str = "continuous"):
+                 policy: str = "continuous", prefix_cache: bool = False):
         if policy not in ("continuous", "static"):
             raise ValueError(policy)
-        self.bm = pk.BlockManager(num_blocks, block_size)
+        self.bm = pk.BlockManager(num_blocks, block_size, prefix_cache=prefix_cache)
         self.block_size = block_size
         self.max_seqs = max_seqs
         self.budget = token_budget
@@ -102,12 +107,16 @@ class ContinuousBatcher:
         self.useful = 0              # output tokens produced
         self.preemptions = 0
         self.cow_copies = 0
+        self.prefill_computed = 0    # prompt tokens whose K/V the steps computed
+        self.prefill_cached = 0      # prompt tokens taken from the prefix cache instead
         self._release: List[int] = []   # finished in the previous step, blocks not yet returned
 
     # -- requests ---------------------------------------------------------
     def submit(self, req: Request) -> None:
         if req.output < 1 or req.prompt < 1:
             raise ValueError("a request needs a prompt and at least one output token")
+        if req.tokens is not None and len(req.tokens) < req.prompt:
+            raise ValueError("token ids, when given, cover at least the prompt")
         self.pending.append(req)
 
     def idle(self) -> bool:
@@ -180,17 +189,24 @@ class ContinuousBatcher:
         while (may_admit and self.waiting and len(self.running) < self.max_seqs
                and (budget > 0 or static)):
             req = self.waiting[0]
-            parent = req.parent if self._shared_parent_alive(req) else -1
-            shared = req.shared if parent >= 0 else 0
-            if parent >= 0:
-                shared = min(shared, self.bm.length(parent), req.prompt - 1)
+            keyed = req.tokens is not None
+            if keyed:
+                # the prefix cache (when on) supplies the leading full blocks it holds
+                shared = self.bm.add_prompt(req.rid, req.tokens[:req.prompt])
+            else:
+                parent = req.parent if self._shared_parent_alive(req) else -1
+                shared = req.shared if parent >= 0 else 0
+                if parent >= 0:
+                    shared = min(shared, self.bm.length(parent), req.prompt - 1)
+                self.bm.add(req.rid, parent, shared)
             first = min(req.prompt - shared, max(budget, 0))
-            self.bm.add(req.rid, parent, shared)
             if self.bm.blocks_needed(seqs + [req.rid], counts + [first]) > self.bm.free_blocks:
                 self.bm.release(req.rid)
                 break
             self.waiting.popleft()
-            s = _Seq(req, computed=shared, admitted_step=step)
+            s = _Seq(req, computed=shared, admitted_step=step, keyed=keyed,
+                     cached=shared if keyed else 0)
+            self.prefill_cached += s.cached
             self.running.append(s)
             if first > 0:
                 plan.append((s, first))
@@ -201,6 +217,23 @@ class ContinuousBatcher:
         slots, copies = self.bm.append(seqs, counts) if seqs else (np.zeros(0, np.int32),
                                                                     np.zeros((0, 2), np.int32))
         self.cow_copies += len(copies)
+        positions = np.concatenate([np.arange(s.kv_len, s.kv_len + n, dtype=np.int32)
+                                    for s, n in plan]) if plan else np.zeros(0, np.int32)
+        token_ids = np.full(len(positions), -1, np.int32)
+        r = 0
+        for s, n in plan:
+            t = s.req.tokens
+            if t is not None:
+                lo = s.kv_len
+                hi = min(lo + n, len(t))
+                if hi > lo:
+                    token_ids[r:r + hi - lo] = t[lo:hi]
+                # a decode row's id reaches the prefix cache once its row is written
+                if s.keyed and not s.prefilling and hi > lo:
+                    self.bm.extend_tokens(s.req.rid, t[lo:hi])
+            if s.prefilling:
+                self.prefill_computed += n
+            r += n
         tables, lens = self.bm.tables(seqs, self.max_blocks) if seqs else (
             np.zeros((0, self.max_blocks), np.int32), np.zeros(0, np.int32))
         self.slot_steps += self.max_seqs if self.policy == "static" else len(plan)
@@ -227,15 +260,33 @@ class ContinuousBatcher:
         self._release = list(finished)
         return StepBatch(step, np.asarray(seqs, np.int64), np.asarray(counts, np.int32),
                          lens.astype(np.int32), tables, slots.astype(np.int32), copies,
-                         finished, preempted)
+                         finished, preempted, positions, token_ids)
+
+
+KV_TABLE_ROWS = 4096
+
+
+def kv_row_index(token_ids: np.ndarray, positions: np.ndarray) -> np.ndarray:
+    """Row of the synthetic K/V tables that a token at a position writes: a fixed
+    function of (token id, position), so equal prefixes give equal K/V."""
+    t = np.asarray(token_ids, np.int64)
+    p = np.asarray(positions, np.int64)
+    return (t * 7919 + p * 104729) % KV_TABLE_ROWS
 
 
 class DeviceEngine:
-    """Runs planned steps on the GPU through the C ABI (synthetic q / K / V)."""
+    """Runs planned steps on the GPU through the C ABI (synthetic q / K / V).
+
+    kv_from_tokens=False: each new K/V row is fresh random numbers.  True: every
+    request carries token ids and a row is picked from fixed seeded tables by
+    kv_row_index(token, position), so K/V depend on the token prefix only, as a
+    model's do -- the condition under which a prefix-cache hit can stand in for
+    a prefill.  The tables (bf16 / f16 bits) are kept in ``self.kv_tables``.
+    """
 
     def __init__(self, batcher: ContinuousBatcher, num_q_heads: int, num_kv_heads: int,
                  head_dim: int, dtype: str = "bf16", seed: int = 0, device: str = "cuda:0",
-                 keep_host_mirror: bool = False):
+                 keep_host_mirror: bool = False, kv_from_tokens: bool = False):
         import torch
         self.torch = torch
         self.b = batcher
@@ -252,6 +303,14 @@ class DeviceEngine:
         self.gen = torch.Generator(device=self.dev)
         self.gen.manual_seed(seed)
         self.scale = float(np.float32(1.0 / np.sqrt(head_dim)))
+        self.kv_tables = None
+        if kv_from_tokens:
+            g = torch.Generator().manual_seed(seed + 1)
+            shape = (KV_TABLE_ROWS, num_kv_heads, head_dim)
+            ek, ev = (torch.randn(shape, generator=g).to(tdt) for _ in range(2))
+            self.kv_tables = (ek.view(torch.int16).numpy().view(np.uint16),
+                              ev.view(torch.int16).numpy().view(np.uint16))
+            self._ek, self._ev = ek.to(self.dev), ev.to(self.dev)
         self.mirror = None
         if keep_host_mirror:
             self.mirror = (np.zeros((nb, num_kv_heads, bs, head_dim), np.uint16),
@@ -267,8 +326,17 @@ class DeviceEngine:
             return None
         rows = int(batch.query_lens.sum())
         q = torch.randn((rows, self.Hq, self.D), generator=self.gen, device=self.dev).to(self.tdt)
-        k_new = torch.randn((rows, self.Hkv, self.D), generator=self.gen, device=self.dev).to(self.tdt)
-        v_new = torch.randn((rows, self.Hkv, self.D), generator=self.gen, device=self.dev).to(self.tdt)
+        if self.kv_tables is not None:
+            if (batch.token_ids < 0).any():
+                raise ValueError("kv_from_tokens needs the token id of every row")
+            idx = torch.from_numpy(kv_row_index(batch.token_ids, batch.positions)).to(self.dev)
+            k_new = self._ek.index_select(0, idx)
+            v_new = self._ev.index_select(0, idx)
+        else:
+            k_new = torch.randn((rows, self.Hkv, self.D), generator=self.gen,
+                                device=self.dev).to(self.tdt)
+            v_new = torch.randn((rows, self.Hkv, self.D), generator=self.gen,
+                                device=self.dev).to(self.tdt)
         out = torch.empty_like(q)
         if len(batch.copies):
             pairs = torch.from_numpy(np.ascontiguousarray(batch.copies)).to(self.dev)

@@ -44,7 +44,9 @@ EXPORTS = ("paged_kv_append", "paged_attn_workspace_bytes", "paged_attn_step",
            "pkv_last_hip_error_string",
            "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_free_blocks", "pkv_bm_refcount", "pkv_bm_add",
            "pkv_bm_blocks_needed", "pkv_bm_append", "pkv_bm_release", "pkv_bm_length",
-           "pkv_bm_tables", "paged_kv_copy_blocks", "paged_kv_append_quant")
+           "pkv_bm_tables", "paged_kv_copy_blocks", "paged_kv_append_quant",
+           "pkv_bm_enable_prefix_cache", "pkv_bm_add_prompt", "pkv_bm_extend_tokens",
+           "pkv_bm_cache_stats", "pkv_prefix_keys")
 
 
 class PkvPool(ctypes.Structure):
@@ -105,6 +107,16 @@ _lib.pkv_bm_length.argtypes = [_BM, _I64, _I32P]
 _lib.pkv_bm_length.restype = ctypes.c_int
 _lib.pkv_bm_tables.argtypes = [_BM, _I64P, _I, _I, _I32P, _I32P]
 _lib.pkv_bm_tables.restype = ctypes.c_int
+_lib.pkv_bm_enable_prefix_cache.argtypes = [_BM]
+_lib.pkv_bm_enable_prefix_cache.restype = ctypes.c_int
+_lib.pkv_bm_add_prompt.argtypes = [_BM, _I64, _I32P, _I, _I32P]
+_lib.pkv_bm_add_prompt.restype = ctypes.c_int
+_lib.pkv_bm_extend_tokens.argtypes = [_BM, _I64, _I32P, _I]
+_lib.pkv_bm_extend_tokens.restype = ctypes.c_int
+_lib.pkv_bm_cache_stats.argtypes = [_BM, ctypes.POINTER(ctypes.c_int64)]
+_lib.pkv_bm_cache_stats.restype = ctypes.c_int
+_lib.pkv_prefix_keys.argtypes = [_I32P, _I, _I, ctypes.POINTER(ctypes.c_uint64)]
+_lib.pkv_prefix_keys.restype = ctypes.c_int
 _lib.paged_kv_append_quant.argtypes = [_POOLP, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _P]
 _lib.paged_kv_append_quant.restype = ctypes.c_int
 _lib.paged_kv_copy_blocks.argtypes = [_POOLP, _P, _P, _P, _P, _P, _I, _P]
@@ -244,17 +256,21 @@ class BlockManager:
     named by int ids chosen by the caller.
     """
 
-    def __init__(self, num_blocks: int, block_size: int):
+    def __init__(self, num_blocks: int, block_size: int, prefix_cache: bool = False):
         self._h = _lib.pkv_bm_create(int(num_blocks), int(block_size))
         if not self._h:
             raise PagedKVError("pkv_bm_create", PKV_ERR_SHAPE)
+        self._destroy = _lib.pkv_bm_destroy      # still reachable during interpreter shutdown
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
+        self.prefix_cache = False
+        if prefix_cache:
+            self.enable_prefix_cache()
 
     def __del__(self):
         h = getattr(self, "_h", None)
         if h:
-            _lib.pkv_bm_destroy(h)
+            self._destroy(h)
             self._h = None
 
     @property
@@ -266,6 +282,29 @@ class BlockManager:
 
     def add(self, seq: int, parent: int = -1, shared_tokens: int = 0) -> None:
         _check("pkv_bm_add", _lib.pkv_bm_add(self._h, int(seq), int(parent), int(shared_tokens)))
+
+    def enable_prefix_cache(self) -> None:
+        """Turn the prefix cache on; only before any sequence has been added."""
+        _check("pkv_bm_enable_prefix_cache", _lib.pkv_bm_enable_prefix_cache(self._h))
+        self.prefix_cache = True
+
+    def add_prompt(self, seq: int, tokens) -> int:
+        """New sequence with known prompt token ids; returns the tokens found in
+        the prefix cache (its length starts there)."""
+        t, tp = _i32(tokens)
+        out = ctypes.c_int32(0)
+        _check("pkv_bm_add_prompt",
+               _lib.pkv_bm_add_prompt(self._h, int(seq), tp, len(t), ctypes.byref(out)))
+        return int(out.value)
+
+    def extend_tokens(self, seq: int, tokens) -> None:
+        t, tp = _i32(tokens)
+        _check("pkv_bm_extend_tokens", _lib.pkv_bm_extend_tokens(self._h, int(seq), tp, len(t)))
+
+    def cache_stats(self) -> dict:
+        out = (ctypes.c_int64 * 5)()
+        _check("pkv_bm_cache_stats", _lib.pkv_bm_cache_stats(self._h, out))
+        return dict(zip(("cached", "evictable", "lookups", "hits", "evictions"), map(int, out)))
 
     def blocks_needed(self, seqs, counts) -> int:
         s, sp = _i64(seqs)
@@ -306,6 +345,16 @@ class BlockManager:
                                                    t.ctypes.data_as(_I32P),
                                                    lens.ctypes.data_as(_I32P)))
         return t[:len(s)], lens[:len(s)]
+
+
+def pkv_prefix_keys(tokens, block_size: int):
+    """Chain keys (uint64) of the full blocks of a token sequence."""
+    import numpy as np
+    t, tp = _i32(tokens)
+    keys = np.zeros(max(1, len(t) // int(block_size)), dtype=np.uint64)
+    _check("pkv_prefix_keys", _lib.pkv_prefix_keys(
+        tp, len(t), int(block_size), keys.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))))
+    return keys[:len(t) // int(block_size)]
 
 
 def paged_kv_copy_blocks(pool: PkvPool, k_pool, v_pool, k_scale, v_scale, pairs, num_pairs: int,

@@ -9,8 +9,14 @@ chunks under a token budget, admission by free blocks, preemption) and run by
 :class:`engine.DeviceEngine` (copy-on-write, KV append, attention for every
 query row; one attention layer of the 7B shape, synthetic q/K/V).  Requests
 arrive as a Poisson process (``--rate`` per step); prompt and output lengths
-are geometric with the given means.  ``--shared`` requests reuse the first
-``--system`` tokens of a long-lived system-prompt sequence's blocks.
+are geometric with the given means; the ``--shared`` fraction of requests
+starts with one fixed ``--system``-token prompt.  ``--reuse`` says how they
+reuse it: ``none`` (every request prefills it), ``parent`` (their tables point
+at the blocks of a long-lived sequence holding it, shared with copy-on-write)
+or ``cache`` (every request carries token ids, K/V rows are a function of
+(token, position), and the block manager's prefix cache supplies the blocks of
+any prefix written before: "Prefix caching", and the chapter's exercise on a
+shared 1,500-token system prompt).
 
 Prints one JSON line: steps, wall time, batch-steps/s, output tokens/s,
 time-to-first-token and inter-token latency percentiles (in steps and ms),
@@ -53,29 +59,41 @@ def main(argv=None):
     ap.add_argument("--head-dim", type=int, default=128)
     ap.add_argument("--policy", default="continuous", choices=["continuous", "static"])
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--reuse", default="parent", choices=["none", "parent", "cache"],
+                    help="how shared-prompt requests reuse it")
     ap.add_argument("--dry-run", action="store_true", help="plan on the host only, no GPU")
     args = ap.parse_args(argv)
 
     from .engine import ContinuousBatcher, DeviceEngine, Request
 
     max_len = 32768
-    b = ContinuousBatcher(args.blocks, 16, args.max_seqs, args.budget, max_len // 16, args.policy)
+    b = ContinuousBatcher(args.blocks, 16, args.max_seqs, args.budget, max_len // 16, args.policy,
+                          prefix_cache=args.reuse == "cache")
     arrivals, prompts, outputs = make_trace(args.requests, args.rate, args.prompt_mean,
                                             args.output_mean, args.seed, max_len)
     parent = -1
-    if args.shared > 0:
+    if args.shared > 0 and args.reuse == "parent":
         parent = 10 ** 9          # a long-lived sequence holding the system prompt
         b.submit(Request(parent, prompt=args.system, output=10 ** 7, arrival=0))
     rng = np.random.default_rng(args.seed + 1)
+    system_ids = rng.integers(0, 32000, args.system).astype(np.int32)
     for i in range(args.requests):
-        share = parent >= 0 and rng.random() < args.shared
+        share = rng.random() < args.shared
         prompt = int(prompts[i]) + (args.system if share else 0)
-        b.submit(Request(i, prompt=prompt, output=int(outputs[i]), arrival=int(arrivals[i]),
-                         parent=parent if share else -1, shared=args.system if share else 0))
+        if args.reuse == "cache":
+            own = rng.integers(0, 32000, prompt + int(outputs[i]) - (args.system if share else 0))
+            toks = np.concatenate([system_ids if share else system_ids[:0], own.astype(np.int32)])
+            b.submit(Request(i, prompt=prompt, output=int(outputs[i]), arrival=int(arrivals[i]),
+                             tokens=toks))
+        else:
+            share = share and parent >= 0
+            b.submit(Request(i, prompt=prompt, output=int(outputs[i]), arrival=int(arrivals[i]),
+                             parent=parent if share else -1, shared=args.system if share else 0))
     eng = stream = torch = None
     if not args.dry_run:
         import torch
-        eng = DeviceEngine(b, args.heads, args.kv_heads, args.head_dim, "bf16", seed=args.seed)
+        eng = DeviceEngine(b, args.heads, args.kv_heads, args.head_dim, "bf16", seed=args.seed,
+                           kv_from_tokens=args.reuse == "cache")
         stream = torch.cuda.current_stream()
         torch.cuda.synchronize()
     host_s = 0.0
@@ -110,6 +128,8 @@ def main(argv=None):
         "ttft_ms_p50": round(float(np.percentile(ttft, 50)) * ms_per_step, 3),
         "itl_steps_p50": float(np.percentile(itl, 50)), "itl_steps_p95": float(np.percentile(itl, 95)),
         "preemptions": b.preemptions, "cow_copies": b.cow_copies,
+        "prefill_tokens_computed": b.prefill_computed, "prefill_tokens_cached": b.prefill_cached,
+        "prefix_cache": b.bm.cache_stats() if args.reuse == "cache" else None,
         "config": {k: v for k, v in vars(args).items()},
     }
     print(json.dumps(line), flush=True)

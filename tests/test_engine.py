@@ -96,9 +96,57 @@ def test_serve_sim_dry_run_drains_trace():
     cont = serve_sim.main(common)
     stat = serve_sim.main(common + ["--policy", "static"])
     shared = serve_sim.main(common + ["--shared", "1.0", "--system", "40"])
-    for line in (cont, stat, shared):
+    nocache = serve_sim.main(common + ["--shared", "1.0", "--system", "300", "--reuse", "none"])
+    cache = serve_sim.main(common + ["--shared", "1.0", "--system", "300", "--reuse", "cache"])
+    for line in (cont, stat, shared, nocache, cache):
         assert line["requests_done"] == 40
     assert cont["output_tokens"] == stat["output_tokens"] == shared["output_tokens"]
     # the static batch waits for its slowest member; continuous refills every step
     assert cont["steps"] < stat["steps"] and cont["ttft_steps_p50"] < stat["ttft_steps_p50"]
     assert shared["cow_copies"] > 0         # the 40-token prefix ends inside a block
+    # the cache prefills the shared 300 tokens' 18 full blocks about once
+    assert nocache["prefill_tokens_cached"] == 0
+    assert cache["prefill_tokens_cached"] >= 30 * 288
+    assert (cache["prefill_tokens_computed"] + cache["prefill_tokens_cached"]
+            == nocache["prefill_tokens_computed"])
+
+
+def test_prefix_cache_skips_the_shared_prompt_and_labels_every_row():
+    rng = np.random.default_rng(5)
+    system = rng.integers(0, 30000, 300).astype(np.int32)
+    reqs = []
+    for i in range(12):
+        q = rng.integers(0, 30000, int(rng.integers(1, 60))).astype(np.int32)
+        out = rng.integers(0, 30000, int(rng.integers(1, 30))).astype(np.int32)
+        toks = np.concatenate([system, q, out])
+        # the others arrive after the first has finished its prefill (a block is
+        # keyed once it is full, so a prompt still being prefilled shares only
+        # the blocks written so far)
+        reqs.append(Request(i, prompt=len(system) + len(q), output=len(out),
+                            arrival=0 if i == 0 else 4 + i, tokens=toks))
+    results = {}
+    for cache in (False, True):
+        b = ContinuousBatcher(num_blocks=400, max_seqs=8, token_budget=256, prefix_cache=cache)
+        for r in reqs:
+            b.submit(r)
+        batches = []
+        b.run_to_completion(on_step=lambda bt: batches.append(bt))
+        for bt in batches:
+            start = 0
+            for sid, n in zip(bt.seq_ids.tolist(), bt.query_lens.tolist()):
+                pos = bt.positions[start:start + n]
+                want = reqs[sid].tokens[pos]
+                assert np.array_equal(bt.token_ids[start:start + n], want)
+                assert pos[-1] == bt.context_lens[bt.seq_ids.tolist().index(sid)] - 1
+                start += n
+        assert b.bm.free_blocks == 400 and len(b.done) == 12
+        results[cache] = b
+    plain, cached = results[False], results[True]
+    assert plain.prefill_cached == 0
+    total_prompt = sum(r.prompt for r in reqs)
+    assert plain.prefill_computed == total_prompt
+    # the first request computes the 18 full system blocks; the other eleven reuse them
+    assert cached.prefill_cached == 11 * (300 // 16) * 16
+    assert cached.prefill_computed == total_prompt - cached.prefill_cached
+    ttft = lambda b: np.mean([s.first_token_step - s.req.arrival for s in b.done.values()])
+    assert ttft(cached) < ttft(plain)

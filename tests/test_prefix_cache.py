@@ -1,0 +1,203 @@
+"""Prefix cache of the host block manager (page "Why a Second Kind of Engine",
+section "Prefix caching", its quiz question on a request id placed before a
+tool schema, and the serving chapter's exercise on a shared 1,500-token system
+prompt).  Host only."""
+import numpy as np
+import pytest
+
+pytest.importorskip("paged_kv_cache_286_amd.pagedkv",
+                    reason="libpagedkv.so not built (python -m paged_kv_cache_286_amd.build_lib)")
+from paged_kv_cache_286_amd import pagedkv as pk
+
+BS = 16
+
+
+def fnv1a64(data: bytes) -> int:
+    """64-bit FNV-1a as its authors define it: for each byte, xor then multiply."""
+    h = 0xcbf29ce484222325
+    for byte in data:
+        h ^= byte
+        h = (h * 0x100000001b3) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def test_fnv_helper_matches_published_vectors():
+    # test vectors from the FNV reference test suite
+    assert fnv1a64(b"") == 0xcbf29ce484222325
+    assert fnv1a64(b"a") == 0xaf63dc4c8601ec8c
+    assert fnv1a64(b"foobar") == 0x85944171f73967e8
+
+
+def test_keys_chain_each_block_to_everything_before_it():
+    rng = np.random.default_rng(0)
+    t = rng.integers(0, 50000, 100).astype(np.int32)
+    keys = pk.pkv_prefix_keys(t, BS)
+    assert len(keys) == 100 // BS
+    parent = 0
+    for i, k in enumerate(keys):
+        blob = parent.to_bytes(8, "little") + t[i * BS:(i + 1) * BS].astype("<i4").tobytes()
+        parent = fnv1a64(blob)
+        assert int(k) == parent
+    # a change in block 3 changes keys 3.. and nothing before
+    u = t.copy()
+    u[3 * BS + 5] += 1
+    ku = pk.pkv_prefix_keys(u, BS)
+    assert np.array_equal(ku[:3], keys[:3]) and np.all(ku[3:] != keys[3:])
+
+
+def _schema(rng, n=6000):
+    return rng.integers(100, 50000, n).astype(np.int32)
+
+
+def test_request_id_before_the_schema_defeats_the_cache():
+    # the quiz: a fresh id in front of a 6,000-token tool schema matches nothing;
+    # the same id after the schema lets all 375 schema blocks be reused
+    rng = np.random.default_rng(1)
+    schema = _schema(rng)
+    assert len(schema) // BS == 375
+    for placement, expect in (("front", 0), ("back", 6000)):
+        bm = pk.BlockManager(2048, BS, prefix_cache=True)
+        for step, rid in enumerate((11, 12, 13)):
+            ident = np.array([rid, 7 * rid], dtype=np.int32)
+            prompt = np.concatenate([ident, schema] if placement == "front" else [schema, ident])
+            got = bm.add_prompt(rid, prompt)
+            assert got == (0 if step == 0 else expect), (placement, step)
+            bm.append([rid], [len(prompt) - got])
+            bm.release(rid)
+        st = bm.cache_stats()
+        assert st["hits"] == 2 * expect // BS
+
+
+def test_shared_system_prompt_is_prefilled_once():
+    # the exercise: a shared 1,500-token system prompt costs its prefill once;
+    # later requests compute only the 12 tokens of its partial last block and
+    # their own question
+    rng = np.random.default_rng(2)
+    system = rng.integers(0, 32000, 1500).astype(np.int32)
+    bm = pk.BlockManager(4096, BS, prefix_cache=True)
+    computed = []
+    for rid in range(8):
+        q = rng.integers(0, 32000, int(rng.integers(5, 200))).astype(np.int32)
+        prompt = np.concatenate([system, q])
+        got = bm.add_prompt(rid, prompt)
+        computed.append(len(prompt) - got)
+        bm.append([rid], [len(prompt) - got])
+        if got:
+            assert got == (1500 // BS) * BS == 1488
+    assert computed[0] >= 1500
+    assert all(c < 212 for c in computed[1:])
+    # all eight hold the same 93 physical blocks for the system prompt
+    tables, _ = bm.tables(list(range(8)), 200)
+    assert (tables[:, :93] == tables[0, :93]).all()
+    assert bm.refcount(int(tables[0, 0])) == 8
+
+
+def test_at_least_one_token_is_left_to_compute():
+    bm = pk.BlockManager(64, BS, prefix_cache=True)
+    t = np.arange(48, dtype=np.int32)
+    assert bm.add_prompt(1, t) == 0
+    bm.append([1], [48])
+    assert bm.add_prompt(2, t) == 32            # 48 cached, one block given back
+    assert bm.add_prompt(3, t[:47]) == 32
+    assert bm.add_prompt(4, t[:17]) == 16
+    assert bm.add_prompt(5, t[:16]) == 0
+
+
+def test_generated_tokens_become_cacheable_when_their_ids_arrive():
+    bm = pk.BlockManager(64, BS, prefix_cache=True)
+    prompt = np.arange(10, dtype=np.int32)
+    out = np.arange(100, 130, dtype=np.int32)
+    bm.add_prompt(1, prompt)
+    bm.append([1], [10])
+    for i, tok in enumerate(out):                  # decode: the KV row of each token,
+        bm.append([1], [1])                        # then its id once it is known
+        bm.extend_tokens(1, [tok])
+    st = bm.cache_stats()
+    assert st["cached"] == 40 // BS                # two full blocks of prompt + output
+    assert bm.add_prompt(2, np.concatenate([prompt, out, [7]])) == 32
+
+
+def test_released_blocks_stay_cached_and_are_evicted_least_recently_used():
+    rng = np.random.default_rng(3)
+    nb = 12
+    bm = pk.BlockManager(nb, BS, prefix_cache=True)
+    a = rng.integers(0, 1000, 4 * BS + 1).astype(np.int32)     # 4 full blocks + 1 token
+    b = rng.integers(0, 1000, 4 * BS + 1).astype(np.int32)
+    for rid, t in ((1, a), (2, b)):
+        bm.add_prompt(rid, t)
+        bm.append([rid], [len(t)])
+    bm.release(1)                                 # a's blocks: 4 cached + 1 free
+    bm.release(2)                                 # b's: released later, so more recent
+    assert bm.free_blocks == nb
+    st = bm.cache_stats()
+    assert st["cached"] == 8 and st["evictable"] == 8
+    # a new 7-block prompt: the 4 free blocks (2 never used, 2 partial last blocks),
+    # then 3 evicted, oldest first -- the tail of a's chain goes before its head
+    # (blocks are released in reverse table order)
+    c = rng.integers(2000, 3000, 7 * BS).astype(np.int32)
+    assert bm.add_prompt(3, c) == 0
+    bm.append([3], [len(c)])
+    assert bm.cache_stats()["evictions"] == 3
+    assert bm.add_prompt(4, np.concatenate([a, [1]])) == BS          # only a's first block left
+    assert bm.add_prompt(5, np.concatenate([b, [1]])) == 4 * BS      # b untouched
+    assert bm.cache_stats()["evictable"] == 0
+    assert bm.free_blocks == 0
+
+
+def test_no_cache_when_disabled():
+    bm = pk.BlockManager(64, BS)
+    t = np.arange(40, dtype=np.int32)
+    assert bm.add_prompt(1, t) == 0
+    bm.append([1], [40])
+    assert bm.add_prompt(2, t) == 0
+    assert bm.cache_stats()["cached"] == 0
+    with pytest.raises(pk.PagedKVError):          # only before any sequence exists
+        bm.enable_prefix_cache()
+    fresh = pk.BlockManager(64, BS)
+    fresh.enable_prefix_cache()
+    with pytest.raises(pk.PagedKVError):          # and only once
+        fresh.enable_prefix_cache()
+
+
+def _model_cached(history, prompt):
+    """Longest run of leading full blocks of `prompt` whose whole prefix was
+    appended before (no eviction), capped to leave one token."""
+    full = len(prompt) // BS
+    n = 0
+    while n < full and tuple(prompt[:(n + 1) * BS]) in history:
+        n += 1
+    if n * BS >= len(prompt) and n:
+        n -= 1
+    return n * BS
+
+
+def test_random_traffic_against_a_plain_model():
+    # no eviction (a pool far larger than the traffic): the cache must return
+    # exactly the longest previously written block prefix, and the manager's
+    # accounting must balance at the end
+    rng = np.random.default_rng(4)
+    bm = pk.BlockManager(4096, BS, prefix_cache=True)
+    roots = [rng.integers(0, 50, int(rng.integers(20, 120))).astype(np.int32) for _ in range(4)]
+    history = set()
+    live = {}
+    for rid in range(200):
+        base = roots[int(rng.integers(0, 4))]
+        cut = int(rng.integers(0, len(base) + 1))
+        tail = rng.integers(0, 3, int(rng.integers(1, 40))).astype(np.int32)   # tiny alphabet: repeats
+        prompt = np.concatenate([base[:cut], tail])
+        want = _model_cached(history, prompt)
+        got = bm.add_prompt(rid, prompt)
+        assert got == want, (rid, got, want)
+        bm.append([rid], [len(prompt) - got])
+        for i in range(len(prompt) // BS):
+            history.add(tuple(prompt[:(i + 1) * BS]))
+        live[rid] = prompt
+        if rng.random() < 0.5:
+            victim = list(live)[int(rng.integers(0, len(live)))]
+            bm.release(victim)
+            del live[victim]
+    for rid in live:
+        bm.release(rid)
+    assert bm.free_blocks == 4096
+    st = bm.cache_stats()
+    assert st["evictable"] == st["cached"] and st["evictions"] == 0
