@@ -139,6 +139,13 @@ size_t paged_attn_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_
  *   query_lens      [num_seqs] int32: query rows of sequence i (1 = decode).  Row r sits at
  *                   position context_lens[i] - query_lens[i] + r and attends to keys
  *                   0 .. that position (causal).
+ *   shared_blocks   [num_seqs] int32 or NULL: a cache-policy hint.  The first
+ *                   shared_blocks[i] table entries of sequence i may also be read by
+ *                   other sequences of this step ("Shared Prefixes"; e.g. the leading
+ *                   blocks whose reference count is above one); the decode kernel keeps
+ *                   those in the caches and streams every other block past them
+ *                   (nontemporal loads).  NULL: no block is read twice.  Results do not
+ *                   depend on it; a wrong hint only costs bandwidth.
  *   num_seqs, total_q_tokens, max_context_len, max_query_len  host copies of
  *                   len(context_lens), sum(query_lens), max(context_lens), max(query_lens);
  *                   they size the launch grids and must bound the device values.
@@ -154,6 +161,7 @@ int paged_attn_step(const pkv_pool* pool,
                     const float* k_scale, const float* v_scale,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, const int32_t* query_lens,
+                    const int32_t* shared_blocks,
                     int32_t num_seqs, int32_t total_q_tokens,
                     int32_t max_context_len, int32_t max_query_len,
                     float scale, void* out,

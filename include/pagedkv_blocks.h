@@ -95,6 +95,11 @@ int pkv_bm_length(const pkv_block_manager* bm, int64_t seq, int32_t* len);
 int pkv_bm_tables(const pkv_block_manager* bm, const int64_t* seqs, int32_t n, int32_t max_blocks,
                   int32_t* tables, int32_t* lens);
 
+/* pkv_bm_shared_prefix -- per sequence, the number of leading table entries whose
+ * block is held by more than one sequence: the shared_blocks hint of paged_attn_step. */
+int pkv_bm_shared_prefix(const pkv_block_manager* bm, const int64_t* seqs, int32_t n,
+                         int32_t* shared);
+
 /* ---- prefix cache ------------------------------------------------------------------
  *
  * Key of full block i of a token sequence t (block_size B):

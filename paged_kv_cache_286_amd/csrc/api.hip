@@ -317,7 +317,8 @@ size_t paged_attn_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_
 int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_t num_q_heads,
                     const void* k_pool, const void* v_pool, const float* k_scale,
                     const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                    const int32_t* context_lens, const int32_t* query_lens, int32_t num_seqs,
+                    const int32_t* context_lens, const int32_t* query_lens,
+                    const int32_t* shared_blocks, int32_t num_seqs,
                     int32_t total_q_tokens, int32_t max_context_len, int32_t max_query_len,
                     float scale, void* out, void* workspace, size_t workspace_bytes,
                     void* stream) {
@@ -356,6 +357,7 @@ int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_
   p.tables = block_tables;
   p.ctx_lens = context_lens;
   p.q_lens = query_lens;
+  p.shared_blocks = shared_blocks;
   p.q_start = multi ? reinterpret_cast<const int32_t*>(ws + lay.q_start_off) : nullptr;
   p.row_seq = multi ? reinterpret_cast<const int32_t*>(ws + lay.row_seq_off) : nullptr;
   p.chunk_count = multi ? reinterpret_cast<const int32_t*>(ws + lay.chunk_count_off) : nullptr;

@@ -414,6 +414,21 @@ int pkv_bm_length(const pkv_block_manager* bm, int64_t seq, int32_t* len) {
   return PKV_OK;
 }
 
+int pkv_bm_shared_prefix(const pkv_block_manager* bm, const int64_t* seqs, int32_t n,
+                         int32_t* shared) {
+  if (bm == nullptr || (n > 0 && (seqs == nullptr || shared == nullptr))) return PKV_ERR_NULL;
+  if (n < 0) return PKV_ERR_SHAPE;
+  for (int32_t i = 0; i < n; ++i)
+    if (!bm->seqs.count(seqs[i])) return PKV_ERR_SHAPE;
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq& s = bm->seqs.at(seqs[i]);
+    int32_t k = 0;
+    while (k < (int32_t)s.blocks.size() && bm->ref[s.blocks[k]] > 1) ++k;
+    shared[i] = k;
+  }
+  return PKV_OK;
+}
+
 int pkv_bm_tables(const pkv_block_manager* bm, const int64_t* seqs, int32_t n, int32_t max_blocks,
                   int32_t* tables, int32_t* lens) {
   if (bm == nullptr || (n > 0 && (seqs == nullptr || tables == nullptr || lens == nullptr)))

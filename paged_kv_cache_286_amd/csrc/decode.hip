@@ -27,6 +27,8 @@
 // LDS), are merged once at the end.  A sequence longer than one partition
 // writes (max, sum, unnormalised output) per partition and the reduce kernel
 // merges them with the log-sum-exp rule.
+#include <type_traits>
+
 #include "pkv_launch.h"
 
 namespace pkv {
@@ -217,41 +219,52 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) 
   const int rg = lane / T::LPR;                  // token row group of this lane
   // Two register buffers: the loads of block i+1 are in flight while block i is
   // scored.  Every iteration issues the same loads with no branch around them
-  // (past the wave's last block the index is clamped and the block counts no
+  // (past the phase's last block the index is clamped and the block counts no
   // tokens), so the compiler can wait for exactly the block it needs instead of
   // draining every outstanding load at a control-flow join.  An out-of-range
   // table entry reads block 0 and counts no tokens.
   uint4 kA[T::NL], vA[T::NL], kB[T::NL], vB[T::NL];
   float kscA = 1.f, vscA = 1.f, kscB = 1.f, vscB = 1.f;
   int limA = 0, limB = 0;
-  auto issue = [&](int i, uint4 (&kr)[T::NL], uint4 (&vr)[T::NL], float& ks, float& vs, int& lim) {
-    const int ic = min(i, cnt - 1);
+  auto issue = [&](auto nt, int i, int end, uint4 (&kr)[T::NL], uint4 (&vr)[T::NL], float& ks,
+                   float& vs, int& lim) {
+    constexpr bool NT = decltype(nt)::value;
+    const int ic = min(i, end - 1);
     const int b = blk_begin + wave + kWaves * ic;
     int phys = __builtin_amdgcn_readlane(my_tbl, ic);
-    lim = i < cnt ? min(16, L - b * 16) : 0;
+    lim = i < end ? min(16, L - b * 16) : 0;
     if ((unsigned)phys >= (unsigned)p.num_blocks) { phys = 0; lim = 0; }
     const size_t boff = ((size_t)phys * p.num_kv_heads + kvh) * T::BLKB;
     const uint4* kb = reinterpret_cast<const uint4*>(p.k_pool + boff);
     const uint4* vb = reinterpret_cast<const uint4*>(p.v_pool + boff);
 #pragma unroll
-    for (int j = 0; j < T::NL; ++j) kr[j] = kb[j * 64 + lane];
+    for (int j = 0; j < T::NL; ++j) kr[j] = load_kv16<NT>(kb + j * 64 + lane);
 #pragma unroll
-    for (int j = 0; j < T::NL; ++j) vr[j] = vb[j * 64 + lane];
+    for (int j = 0; j < T::NL; ++j) vr[j] = load_kv16<NT>(vb + j * 64 + lane);
     if constexpr (KV == kFP8) {
       ks = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_ks), ic));
       vs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_vs), ic));
     }
   };
-
-  if (cnt > 0) {
-    issue(0, kA, vA, kscA, vscA, limA);
-    for (int i = 0; i < cnt; i += 2) {
-      issue(i + 1, kB, vB, kscB, vscB, limB);
+  // blocks i0 .. i1-1 of this wave, with one load policy
+  auto walk = [&](auto nt, int i0, int i1) {
+    if (i1 <= i0) return;
+    issue(nt, i0, i1, kA, vA, kscA, vscA, limA);
+    for (int i = i0; i < i1; i += 2) {
+      issue(nt, i + 1, i1, kB, vB, kscB, vscB, limB);
       attend_block<KV, QT, D, GB>(kA, vA, kscA, vscA, limA, rg, qp, qf, p.scale_log2, m, l, acc);
-      issue(i + 2, kA, vA, kscA, vscA, limA);
+      issue(nt, i + 2, i1, kA, vA, kscA, vscA, limA);
       attend_block<KV, QT, D, GB>(kB, vB, kscB, vscB, limB, rg, qp, qf, p.scale_log2, m, l, acc);
     }
-  }
+  };
+  // blocks other sequences also read stay cacheable; the rest stream past the
+  // caches.  The hint is clamped to this partition's blocks first, so no value
+  // of it can overflow the arithmetic below: 0 <= cnt_sh <= cnt.
+  const int hint = p.shared_blocks != nullptr ? p.shared_blocks[seq] : 0;
+  const int nsh = min(max(hint, blk_begin), blk_end);
+  const int cnt_sh = min(cnt, max(0, nsh - blk_begin - wave + kWaves - 1) / kWaves);
+  walk(std::false_type{}, 0, cnt_sh);
+  walk(std::true_type{}, cnt_sh, cnt);
 
   // merge the RPL token-row groups of this wave
 #pragma unroll

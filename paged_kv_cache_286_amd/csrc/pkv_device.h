@@ -33,6 +33,7 @@ struct StepParams {
   const int32_t* tables;     // [S][max_blocks]
   const int32_t* ctx_lens;   // [S]
   const int32_t* q_lens;     // [S]
+  const int32_t* shared_blocks;  // [S] leading blocks other sequences also read (NULL: none)
   const int32_t* q_start;    // [S + 1] row offsets (NULL when every query_len is 1)
   const int32_t* row_seq;    // [Tq] sequence of each row (NULL when every query_len is 1)
   float* part_ml;            // [Tq][Hq][max_parts][2]  (m in log2 units, l)
@@ -73,6 +74,23 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& a, float& b) {
   auto v = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
   a = v[0];
   b = v[1];
+}
+
+// A K/V block that no other reader of the step touches is read exactly once:
+// a nontemporal load (streaming policy) passes it by the caches.  On MI355X a
+// random gather of 4 KiB runs moves ~6.85 TB/s this way against ~6.1 TB/s with
+// ordinary loads -- but lines that other waves read again soon (a shared
+// prefix) then come from HBM again, so those keep ordinary loads.  Used by the
+// VALU decode kernel.
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ uint4 load_kv16(const void* ptr) {
+  if constexpr (NT) {
+    const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(ptr));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *reinterpret_cast<const uint4*>(ptr);
+  }
 }
 
 // unpack a 16-byte load of KV elements into floats (8 for 16-bit types, 16 for fp8)

@@ -135,7 +135,9 @@ struct TileItem {
 // !SPLIT (prefill chunks): the item is kTileWaves tiles of 16 columns, wave w
 // owns tile w and walks every block up to its own causal limit; the four
 // waves read the same blocks at the same time (one fetch beyond L1 serves
-// them all) and each writes its own columns.
+// them all) and each writes its own columns.  K/V use ordinary (cached) loads
+// here: nontemporal loads for the decode items measured no gain with fp8 K/V
+// and cost 25% in steps that mix decodes with prefill chunks.
 template <int KV, int QT, int D, bool SPLIT>
 __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& it, int group,
                                           float* sm_o, float* sm_m, float* sm_l) {

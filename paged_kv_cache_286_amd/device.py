@@ -28,6 +28,23 @@ def _poison_value(bits: int, store):
     return int(bits)
 
 
+def shared_prefix_blocks(tables: np.ndarray, context_lens: np.ndarray) -> np.ndarray:
+    """Per sequence, the leading table entries whose block also appears in another
+    sequence's table (the cache-policy hint of paged_attn_step)."""
+    lens = np.asarray(context_lens, np.int64)
+    nblk = (lens + 15) // 16
+    cols = np.arange(tables.shape[1])[None, :]
+    used = cols < nblk[:, None]
+    ids = tables[used]
+    counts = np.bincount(ids[ids >= 0], minlength=1) if ids.size else np.zeros(1, np.int64)
+    shared = np.zeros(tables.shape, bool)
+    valid = used & (tables >= 0)
+    shared[valid] = counts[tables[valid]] > 1
+    # length of the leading run of shared entries
+    run = np.cumprod(shared, axis=1).sum(axis=1)
+    return run.astype(np.int32)
+
+
 class DeviceStep:
     """Device buffers of one step plus the two ABI calls that run it."""
 
@@ -54,6 +71,8 @@ class DeviceStep:
         self.block_tables = torch.from_numpy(plan.block_tables).to(self.device)
         self.context_lens = torch.from_numpy(plan.context_lens).to(self.device)
         self.query_lens = torch.from_numpy(plan.query_lens).to(self.device)
+        shared = shared_prefix_blocks(plan.block_tables, plan.context_lens)
+        self.shared_blocks = (torch.from_numpy(shared).to(self.device) if shared.any() else None)
         self.q = _bits_tensor(wl.q, self.device)
         self.out = torch.full_like(self.q, _poison_value(0x7FC0 if cfg.q_dtype == "bf16" else 0x7E00,
                                                          torch.int16))
@@ -94,7 +113,8 @@ class DeviceStep:
             self.context_lens, self.query_lens, plan.num_seqs, plan.total_q_tokens,
             plan.max_context_len, plan.max_query_len, float(self.wl.scale), self.out,
             self.workspace, self.ws_bytes,
-            stream if stream is not None else torch.cuda.current_stream(self.device))
+            stream if stream is not None else torch.cuda.current_stream(self.device),
+            shared_blocks=self.shared_blocks)
 
     def step(self, stream=None) -> None:
         self.append(stream)

@@ -80,6 +80,7 @@ class StepBatch:
     copies: np.ndarray           # int32 [k][2] copy-on-write (source, destination)
     finished: List[int]
     preempted: List[int]
+    shared_blocks: np.ndarray = None  # int32 [S] leading blocks held by several sequences
     positions: np.ndarray = None  # int32 [rows] position of each new row in its sequence
     token_ids: np.ndarray = None  # int32 [rows] its token id, -1 where the request gave none
 
@@ -236,6 +237,7 @@ class ContinuousBatcher:
             r += n
         tables, lens = self.bm.tables(seqs, self.max_blocks) if seqs else (
             np.zeros((0, self.max_blocks), np.int32), np.zeros(0, np.int32))
+        shared_blocks = self.bm.shared_prefix(seqs) if seqs else np.zeros(0, np.int32)
         self.slot_steps += self.max_seqs if self.policy == "static" else len(plan)
 
         # advance the host state as the step will leave it
@@ -260,7 +262,7 @@ class ContinuousBatcher:
         self._release = list(finished)
         return StepBatch(step, np.asarray(seqs, np.int64), np.asarray(counts, np.int32),
                          lens.astype(np.int32), tables, slots.astype(np.int32), copies,
-                         finished, preempted, positions, token_ids)
+                         finished, preempted, shared_blocks, positions, token_ids)
 
 
 KV_TABLE_ROWS = 4096
@@ -351,9 +353,12 @@ class DeviceEngine:
         max_ctx, max_q = int(batch.context_lens.max()), int(batch.query_lens.max())
         ws_bytes = pk.paged_attn_workspace_bytes(self.pool, S, self.Hq, rows, max_ctx, max_q)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=self.dev)
+        shared = None
+        if batch.shared_blocks is not None and batch.shared_blocks.any():
+            shared = torch.from_numpy(batch.shared_blocks).to(self.dev)
         pk.paged_attn_step(self.pool, q, self.code, self.Hq, self.k_pool, self.v_pool, None, None,
                            tables, self.b.max_blocks, ctx, ql, S, rows, max_ctx, max_q, self.scale,
-                           out, ws, ws_bytes, stream)
+                           out, ws, ws_bytes, stream, shared_blocks=shared)
         if self.mirror is not None:
             kb = k_new.view(torch.int16).cpu().numpy().view(np.uint16)
             vb = v_new.view(torch.int16).cpu().numpy().view(np.uint16)

@@ -46,7 +46,7 @@ EXPORTS = ("paged_kv_append", "paged_attn_workspace_bytes", "paged_attn_step",
            "pkv_bm_blocks_needed", "pkv_bm_append", "pkv_bm_release", "pkv_bm_length",
            "pkv_bm_tables", "paged_kv_copy_blocks", "paged_kv_append_quant",
            "pkv_bm_enable_prefix_cache", "pkv_bm_add_prompt", "pkv_bm_extend_tokens",
-           "pkv_bm_cache_stats", "pkv_prefix_keys")
+           "pkv_bm_cache_stats", "pkv_prefix_keys", "pkv_bm_shared_prefix")
 
 
 class PkvPool(ctypes.Structure):
@@ -72,8 +72,8 @@ _lib.paged_kv_append.argtypes = [_POOLP, _P, _P, _P, _P, _I, _P, _I, _P]
 _lib.paged_kv_append.restype = ctypes.c_int
 _lib.paged_attn_workspace_bytes.argtypes = [_POOLP, _I, _I, _I, _I, _I]
 _lib.paged_attn_workspace_bytes.restype = ctypes.c_size_t
-_lib.paged_attn_step.argtypes = [_POOLP, _P, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I,
-                                 _I, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+_lib.paged_attn_step.argtypes = [_POOLP, _P, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I,
+                                 _I, _I, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
 _lib.paged_attn_step.restype = ctypes.c_int
 _lib.pkv_status_string.argtypes = [ctypes.c_int]
 _lib.pkv_status_string.restype = ctypes.c_char_p
@@ -107,6 +107,8 @@ _lib.pkv_bm_length.argtypes = [_BM, _I64, _I32P]
 _lib.pkv_bm_length.restype = ctypes.c_int
 _lib.pkv_bm_tables.argtypes = [_BM, _I64P, _I, _I, _I32P, _I32P]
 _lib.pkv_bm_tables.restype = ctypes.c_int
+_lib.pkv_bm_shared_prefix.argtypes = [_BM, _I64P, _I, _I32P]
+_lib.pkv_bm_shared_prefix.restype = ctypes.c_int
 _lib.pkv_bm_enable_prefix_cache.argtypes = [_BM]
 _lib.pkv_bm_enable_prefix_cache.restype = ctypes.c_int
 _lib.pkv_bm_add_prompt.argtypes = [_BM, _I64, _I32P, _I, _I32P]
@@ -196,11 +198,11 @@ def paged_attn_step(pool: PkvPool, q, q_dtype: int, num_q_heads: int, k_pool, v_
                     k_scale, v_scale, block_tables, max_blocks_per_seq: int, context_lens,
                     query_lens, num_seqs: int, total_q_tokens: int, max_context_len: int,
                     max_query_len: int, scale: float, out, workspace, workspace_bytes: int,
-                    stream=None) -> None:
+                    stream=None, shared_blocks=None) -> None:
     _check("paged_attn_step", _lib.paged_attn_step(
         _poolref(pool), _ptr(q), int(q_dtype), int(num_q_heads), _ptr(k_pool), _ptr(v_pool),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), int(max_blocks_per_seq),
-        _ptr(context_lens), _ptr(query_lens), int(num_seqs), int(total_q_tokens),
+        _ptr(context_lens), _ptr(query_lens), _ptr(shared_blocks), int(num_seqs), int(total_q_tokens),
         int(max_context_len), int(max_query_len), float(scale), _ptr(out), _ptr(workspace),
         int(workspace_bytes), _stream(stream)))
 
@@ -334,6 +336,15 @@ class BlockManager:
         out = ctypes.c_int32(0)
         _check("pkv_bm_length", _lib.pkv_bm_length(self._h, int(seq), ctypes.byref(out)))
         return int(out.value)
+
+    def shared_prefix(self, seqs):
+        """Per sequence, leading blocks held by more than one sequence (int32[n])."""
+        import numpy as np
+        s, sp = _i64(seqs)
+        out = np.zeros(max(1, len(s)), dtype=np.int32)
+        _check("pkv_bm_shared_prefix",
+               _lib.pkv_bm_shared_prefix(self._h, sp, len(s), out.ctypes.data_as(_I32P)))
+        return out[:len(s)]
 
     def tables(self, seqs, max_blocks: int):
         """Returns (tables int32[n][max_blocks] padded with -1, lens int32[n])."""

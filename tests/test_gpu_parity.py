@@ -226,6 +226,33 @@ def test_gpu_shared_prefix_equals_copies_bitwise():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("case", ["mha_bf16_valu", "gqa8_fp8_mfma", "mixed_step"])
+def test_gpu_shared_hint_only_changes_the_load_policy(case):
+    # the shared_blocks hint picks cached or streaming loads; whatever it says
+    # (right, absent, negative, past the table) the output bits stay the same
+    Hq, Hkv, kv, qd = {"mha_bf16_valu": (8, 8, W.BF16, W.BF16),
+                       "gqa8_fp8_mfma": (16, 2, W.FP8, W.BF16),
+                       "mixed_step": (8, 8, W.BF16, W.BF16)}[case]
+    lens = [1500, 2600, 700, 40, 2100]
+    qlens = [1, 1, 1, 1, 1] if case != "mixed_step" else [1, 1, 300, 1, 17]
+    cfg = W.Config("hint", "hint", Hq, Hkv, 128, 16, 800, kv, qd, 21)
+    wl = W.generate(W.custom_plan(cfg, lens, qlens, 21, shared_prefix_blocks=40,
+                                  shared_seqs=(0, 1, 4)))
+    ds = _run(wl, f"shared hint {case}")
+    _check(wl, ds)
+    assert ds.shared_blocks is not None
+    assert ds.shared_blocks.cpu().tolist() == [40, 40, 0, 0, 40]
+    want = ds.out_bits()
+    S = len(lens)
+    dev = ds.shared_blocks.device
+    for hint in (None, [0] * S, [-5, 10**6, 3, 2**31 - 1, 17], [200] * S):
+        ds.shared_blocks = None if hint is None else torch.tensor(hint, dtype=torch.int32, device=dev)
+        ds.out.zero_()
+        ds.attend()
+        torch.cuda.synchronize()
+        assert np.array_equal(ds.out_bits(), want), f"hint {hint}"
+
+
 # ----------------------------------------------------------------------------
 # the append, bit for bit over whole pools
 # ----------------------------------------------------------------------------
