@@ -381,8 +381,46 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   // the column's running sum is spread over the 4 lane groups
   lsum = sum_xor32(sum_xor16(lsum));
 
-  if constexpr (!SPLIT) {
-    // this wave alone saw its columns' keys of the partition: write them out
+  if constexpr (SPLIT) {
+    // Merge the four waves' partials of the same 16 columns in two rounds
+    // through 2 x 16 x D floats of LDS (waves 2, 3 -> 0, 1, then 1 -> 0), half
+    // of what one round needs; the LDS then no longer caps the workgroups a
+    // CU holds below what the registers allow.
+    auto put = [&](int slot) {
+#pragma unroll
+      for (int j = 0; j < L::DT; ++j)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) sm_o[(slot * 16 + n) * D + (gq * 4 + i4) * L::DT + j] = o[j][i4];
+      if (gq == 0) {
+        sm_m[slot * 16 + n] = m;
+        sm_l[slot * 16 + n] = lsum;
+      }
+    };
+    auto take = [&](int slot) {
+      const float m2 = sm_m[slot * 16 + n];
+      const float M = fmaxf(m, m2);
+      const float f1 = __builtin_amdgcn_exp2f(m - M);
+      const float f2 = __builtin_amdgcn_exp2f(m2 - M);
+      lsum = lsum * f1 + sm_l[slot * 16 + n] * f2;
+#pragma unroll
+      for (int j = 0; j < L::DT; ++j)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          o[j][i4] = o[j][i4] * f1 + sm_o[(slot * 16 + n) * D + (gq * 4 + i4) * L::DT + j] * f2;
+      m = M;
+    };
+    if (wave >= 2) put(wave - 2);
+    __syncthreads();
+    if (wave < 2) take(wave);
+    __syncthreads();
+    if (wave == 1) put(0);
+    __syncthreads();
+    if (wave != 0) return;
+    take(0);
+  }
+
+  {
+    // this wave holds its columns' result over the partition: write it out
     if (!col_ok || pos < tok0) return;             // no key of this partition is visible
     const size_t rh = (size_t)row * p.num_q_heads + head;
     const int nparts = (pos + it.part_tokens) / it.part_tokens;     // ceil((pos + 1) / pt)
@@ -403,50 +441,6 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
       if (gq == 0) {
         p.part_ml[idx * 2] = m;
         p.part_ml[idx * 2 + 1] = lsum;
-      }
-    }
-    return;
-  }
-
-  // merge the waves through LDS: sm_o[wave][col][dim], sm_m/sm_l[wave][col]
-#pragma unroll
-  for (int j = 0; j < L::DT; ++j)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4)
-      sm_o[(wave * 16 + n) * D + (gq * 4 + i4) * L::DT + j] = o[j][i4];
-  if (gq == 0) {
-    sm_m[wave * 16 + n] = m;
-    sm_l[wave * 16 + n] = lsum;
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < 16 * D; t += kTileWaves * 64) {
-    const int c = t / D;
-    const int d = t - c * D;
-    const int cc = it.col0 + c;
-    if (cc >= it.ncols) continue;
-    const int rl = cc / group;
-    const int cpos = it.L - it.Q + rl;
-    if (cpos < tok0) continue;                     // no key of this partition is visible to it
-    float M = sm_m[c];
-#pragma unroll
-    for (int w = 1; w < kTileWaves; ++w) M = fmaxf(M, sm_m[w * 16 + c]);
-    float ls = 0.f, ov = 0.f;
-#pragma unroll
-    for (int w = 0; w < kTileWaves; ++w) {
-      const float f = __builtin_amdgcn_exp2f(sm_m[w * 16 + c] - M);
-      ls = __builtin_fmaf(sm_l[w * 16 + c], f, ls);
-      ov = __builtin_fmaf(sm_o[(w * 16 + c) * D + d], f, ov);
-    }
-    const size_t rh = (size_t)(it.row0 + rl) * p.num_q_heads + it.kvh * group + cc % group;
-    const int nparts = (cpos + it.part_tokens) / it.part_tokens;   // ceil((cpos + 1) / pt)
-    if (nparts == 1) {
-      reinterpret_cast<uint16_t*>(p.out)[rh * D + d] = to_out_bits<QT>(ov / ls);
-    } else {
-      const size_t idx = rh * it.max_parts + it.part;
-      p.part_o[idx * D + d] = ov;
-      if (d == 0) {
-        p.part_ml[idx * 2] = M;
-        p.part_ml[idx * 2 + 1] = ls;
       }
     }
   }
@@ -524,9 +518,9 @@ __device__ __forceinline__ void chunk_wgs(const StepParams& p, int wg, int nwg, 
 // Decode rows only: grid (kv head x column tiles, sequence, partition).
 template <int KV, int QT, int D>
 __global__ __launch_bounds__(kTileWaves * 64) void decode_mfma_kernel(StepParams p) {
-  __shared__ float sm_o[kTileWaves * 16 * D];
-  __shared__ float sm_m[kTileWaves * 16];
-  __shared__ float sm_l[kTileWaves * 16];
+  __shared__ float sm_o[2 * 16 * D];
+  __shared__ float sm_m[2 * 16];
+  __shared__ float sm_l[2 * 16];
   decode_wg<KV, QT, D>(p, blockIdx.x, blockIdx.y, blockIdx.z, sm_o, sm_m, sm_l);
 }
 
@@ -538,9 +532,9 @@ __global__ __launch_bounds__(kTileWaves * 64) void decode_mfma_kernel(StepParams
 template <int KV, int QT, int D>
 __global__ __launch_bounds__(kTileWaves * 64) void step_mfma_kernel(StepParams p, int n_chunk_wgs,
                                                                    int stride, int dec_x, int dec_y) {
-  __shared__ float sm_o[kTileWaves * 16 * D];
-  __shared__ float sm_m[kTileWaves * 16];
-  __shared__ float sm_l[kTileWaves * 16];
+  __shared__ float sm_o[2 * 16 * D];
+  __shared__ float sm_m[2 * 16];
+  __shared__ float sm_l[2 * 16];
   const int b = blockIdx.x;
   const int k = b / stride;
   const int r = b - k * stride;
