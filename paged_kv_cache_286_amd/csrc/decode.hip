@@ -147,7 +147,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) 
   const int part = blockIdx.z;
   const int seq = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform by construction; readfirstlane lets the compiler keep what derives
+  // from it (block indices, buffer resources) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int group = p.num_q_heads / p.num_kv_heads;
   const int h0 = blockIdx.x * GB;                // first query head of this workgroup
   const int kvh = h0 / group;
@@ -235,12 +237,13 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) 
     lim = i < end ? min(16, L - b * 16) : 0;
     if ((unsigned)phys >= (unsigned)p.num_blocks) { phys = 0; lim = 0; }
     const size_t boff = ((size_t)phys * p.num_kv_heads + kvh) * T::BLKB;
-    const uint4* kb = reinterpret_cast<const uint4*>(p.k_pool + boff);
-    const uint4* vb = reinterpret_cast<const uint4*>(p.v_pool + boff);
+    const int bytes = lim > 0 ? T::BLKB : 0;       // a block with no tokens is not read
+    const __amdgpu_buffer_rsrc_t kres = block_rsrc(p.k_pool + boff, bytes);
+    const __amdgpu_buffer_rsrc_t vres = block_rsrc(p.v_pool + boff, bytes);
 #pragma unroll
-    for (int j = 0; j < T::NL; ++j) kr[j] = load_kv16<NT>(kb + j * 64 + lane);
+    for (int j = 0; j < T::NL; ++j) kr[j] = load_block16<NT>(kres, (j * 64 + lane) * 16);
 #pragma unroll
-    for (int j = 0; j < T::NL; ++j) vr[j] = load_kv16<NT>(vb + j * 64 + lane);
+    for (int j = 0; j < T::NL; ++j) vr[j] = load_block16<NT>(vres, (j * 64 + lane) * 16);
     if constexpr (KV == kFP8) {
       ks = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_ks), ic));
       vs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_vs), ic));
