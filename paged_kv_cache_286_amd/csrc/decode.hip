@@ -237,7 +237,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) 
     lim = i < end ? min(16, L - b * 16) : 0;
     if ((unsigned)phys >= (unsigned)p.num_blocks) { phys = 0; lim = 0; }
     const size_t boff = ((size_t)phys * p.num_kv_heads + kvh) * T::BLKB;
-    const int bytes = lim > 0 ? T::BLKB : 0;       // a block with no tokens is not read
+    // a block with no tokens is not read (the count kept scalar: no waterfall loop)
+    const int bytes = __builtin_amdgcn_readfirstlane(lim > 0 ? T::BLKB : 0);
     const __amdgpu_buffer_rsrc_t kres = block_rsrc(p.k_pool + boff, bytes);
     const __amdgpu_buffer_rsrc_t vres = block_rsrc(p.v_pool + boff, bytes);
 #pragma unroll

@@ -76,6 +76,13 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& a, float& b) {
   b = v[1];
 }
 
+// A value every lane of the wave reads from the same address: readfirstlane
+// tells the compiler it is uniform, so what is computed from it (block
+// indices, buffer resources) stays in scalar registers.
+__device__ __forceinline__ int uniform_load(const int32_t* ptr) {
+  return __builtin_amdgcn_readfirstlane(*ptr);
+}
+
 // Buffer-resource loads of one K or V block.  The resource's record count is
 // the block's byte size, or 0 for a block that counts no tokens (the clamped
 // look-ahead past a wave's last block, an invalid table entry): an

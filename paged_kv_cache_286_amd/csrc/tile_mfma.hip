@@ -110,10 +110,25 @@ struct TileLay {
   static_assert(NBUF % 2 == 0, "blocks are consumed in pairs");
 };
 
+typedef uint32_t u32x2_buf __attribute__((ext_vector_type(2)));
 template <int VB> struct VVec;
-template <> struct VVec<16> { typedef uint4 T; };
-template <> struct VVec<8> { typedef uint2 T; };
-template <> struct VVec<4> { typedef uint32_t T; };
+template <> struct VVec<16> {
+  typedef uint4 T;
+  static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int off) { return load_block16<false>(r, off); }
+};
+template <> struct VVec<8> {
+  typedef uint2 T;
+  static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x2_buf v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(v.x, v.y);
+  }
+};
+template <> struct VVec<4> {
+  typedef uint32_t T;
+  static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+};
 
 template <int KV, int D>
 struct BlockRegs {
@@ -135,15 +150,15 @@ struct TileItem {
 // !SPLIT (prefill chunks): the item is kTileWaves tiles of 16 columns, wave w
 // owns tile w and walks every block up to its own causal limit; the four
 // waves read the same blocks at the same time (one fetch beyond L1 serves
-// them all) and each writes its own columns.  K/V use ordinary (cached) loads
-// here: nontemporal loads for the decode items measured no gain with fp8 K/V
-// and cost 25% in steps that mix decodes with prefill chunks.
+// them all) and each writes its own columns.  K/V use ordinary (cached)
+// loads here: nontemporal loads for the decode items gained at most 1% with
+// fp8 K/V and cost 20% in steps that mix decodes with prefill chunks.
 template <int KV, int QT, int D, bool SPLIT>
 __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& it, int group,
                                           float* sm_o, float* sm_m, float* sm_l) {
   using L = TileLay<KV, D>;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar, provably
   const int n = lane & 15;          // column of this lane (token row of K it loads)
   const int gq = lane >> 4;         // lane group: tokens 4*gq..4*gq+3 / dims slice gq
   const int tcol0 = SPLIT ? it.col0 : it.col0 + 16 * wave;   // this wave's column tile
@@ -227,15 +242,15 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     int phys = lane_word(my_tbl, ic);
     r.limit = i < cnt ? min(16, it.L - b * 16) : 0;
     if ((unsigned)phys >= (unsigned)p.num_blocks) { phys = 0; r.limit = 0; }
-    const uint8_t* kb = p.k_pool + ((size_t)phys * p.num_kv_heads + it.kvh) * L::BLKB;
-    const uint8_t* vb = p.v_pool + ((size_t)phys * p.num_kv_heads + it.kvh) * L::BLKB;
+    const size_t boff = ((size_t)phys * p.num_kv_heads + it.kvh) * L::BLKB;
+    // a block with no tokens is not read (the count kept scalar: no waterfall loop)
+    const int bytes = __builtin_amdgcn_readfirstlane(r.limit > 0 ? L::BLKB : 0);
+    const __amdgpu_buffer_rsrc_t kres = block_rsrc(p.k_pool + boff, bytes);
+    const __amdgpu_buffer_rsrc_t vres = block_rsrc(p.v_pool + boff, bytes);
 #pragma unroll
-    for (int c = 0; c < L::KLD; ++c)
-      r.k[c] = *reinterpret_cast<const uint4*>(kb + n * L::ROWB + gq * L::KB + c * 16);
+    for (int c = 0; c < L::KLD; ++c) r.k[c] = load_block16<false>(kres, n * L::ROWB + gq * L::KB + c * 16);
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4)
-      r.v[i4] = *reinterpret_cast<const typename VVec<L::VB>::T*>(
-          vb + (gq * 4 + i4) * L::ROWB + n * L::VB);
+    for (int i4 = 0; i4 < 4; ++i4) r.v[i4] = VVec<L::VB>::load(vres, (gq * 4 + i4) * L::ROWB + n * L::VB);
     if constexpr (KV == kFP8) {
       r.ksc = lane_float(my_ks, ic);
       r.vsc = lane_float(my_vs, ic);
@@ -464,16 +479,16 @@ __device__ __forceinline__ void decode_wg(const StepParams& p, int x, int seq, i
   it.max_parts = p.max_parts;
   it.Q = 1;
   if (p.q_start != nullptr) {
-    it.Q = p.q_lens[it.seq];
+    it.Q = uniform_load(p.q_lens + it.seq);
     if (it.Q < 1 || it.Q > p.small_q) return;      // longer prefill chunks are chunk items
-    it.row0 = p.q_start[it.seq];
+    it.row0 = uniform_load(p.q_start + it.seq);
     if (it.row0 < 0 || it.row0 + it.Q > p.total_q) return;
   } else {
     it.row0 = it.seq;
   }
   it.ncols = it.Q * group;
   if (it.col0 >= it.ncols) return;
-  it.L = p.ctx_lens[it.seq];
+  it.L = uniform_load(p.ctx_lens + it.seq);
   if (it.Q > it.L || it.part * it.part_tokens >= it.L || it.L > p.max_blocks * 16 ||
       it.L > p.max_parts * it.part_tokens)
     return;
@@ -487,23 +502,23 @@ template <int KV, int QT, int D>
 __device__ __forceinline__ void chunk_wgs(const StepParams& p, int wg, int nwg, float* sm_o,
                                           float* sm_m, float* sm_l) {
   const int group = p.num_q_heads / p.num_kv_heads;
-  const int n_entries = min(*p.chunk_count, p.chunk_capacity);
+  const int n_entries = min(uniform_load(p.chunk_count), p.chunk_capacity);
   const int per_entry = p.num_kv_heads * p.chunk_max_parts;
   const long long items = (long long)n_entries * per_entry;
   for (long long item = wg; item < items; item += nwg) {
     const int e = (int)(item / per_entry);
     const int rem = (int)(item - (long long)e * per_entry);
     TileItem it;
-    it.seq = p.chunk_entries[2 * e];
-    it.col0 = p.chunk_entries[2 * e + 1];
+    it.seq = uniform_load(p.chunk_entries + 2 * e);
+    it.col0 = uniform_load(p.chunk_entries + 2 * e + 1);
     it.kvh = rem / p.chunk_max_parts;
     it.part = rem - it.kvh * p.chunk_max_parts;
     it.part_tokens = p.chunk_part_tokens;
     it.max_parts = p.max_parts;
     if ((unsigned)it.seq >= (unsigned)p.num_seqs) continue;
-    it.Q = p.q_lens[it.seq];
-    it.L = p.ctx_lens[it.seq];
-    it.row0 = p.q_start[it.seq];
+    it.Q = uniform_load(p.q_lens + it.seq);
+    it.L = uniform_load(p.ctx_lens + it.seq);
+    it.row0 = uniform_load(p.q_start + it.seq);
     it.ncols = it.Q * group;
     if (it.Q < 1 || it.Q > it.L || it.L > p.max_blocks * 16 || it.row0 < 0 ||
         it.row0 + it.Q > p.total_q || it.col0 >= it.ncols)
