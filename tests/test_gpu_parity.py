@@ -146,6 +146,17 @@ def test_multi_row_routing_forced(small_q, monkeypatch):
         _check(wl, _run(wl, f"{name} small_q={small_q}"))
 
 
+@pytest.mark.parametrize("kv", [W.BF16, W.FP8])
+def test_mixed_step_decode_verify_and_prefill_rows(kv):
+    # one step with single decode rows, short verify rows, a whole 300-token
+    # prompt and a 129-row chunk, at lengths around block and partition edges
+    lens = [1, 17, 300, 2000, 90, 513, 4000, 64]
+    qlens = [1, 1, 300, 1, 5, 1, 129, 1]
+    cfg = W.Config("mixed", "mixed", 8, 8 if kv == W.BF16 else 2, 128, 16, 900, kv, W.BF16, 31)
+    wl = W.generate(W.custom_plan(cfg, lens, qlens, 31))
+    _check(wl, _run(wl, f"mixed rows kv={kv}"))
+
+
 @pytest.mark.parametrize("chunk_pt", [64, 256, 1024])
 def test_chunk_partition_sizes(chunk_pt, monkeypatch):
     monkeypatch.setenv("PKV_CHUNK_PART_TOKENS", str(chunk_pt))
