@@ -145,12 +145,18 @@ __device__ __forceinline__ float load_q(const void* base, size_t idx) {
   else return (float)__builtin_bit_cast(_Float16, u);
 }
 
-// float -> bfloat16 bits, round to nearest even (NaN stays NaN)
+// float -> bfloat16 bits, round to nearest even (NaN stays NaN): gfx950's
+// v_cvt_pk_bf16_f32.  It agrees bit for bit with the add-0x7fff-plus-lsb
+// rounding of the bit pattern (NaNs quieted, payload kept) on every
+// sign / exponent / top-mantissa pattern with tie and tail variants.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// two floats -> two packed bfloat16 (a in the low half), one instruction
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 template <int T>

@@ -64,7 +64,8 @@ __device__ __forceinline__ uint32_t fp8x2_to_16(uint32_t w) {
 // two floats -> two 16-bit values of type QT (round to nearest even), packed
 template <int QT>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return (uint32_t)to_out_bits<QT>(a) | ((uint32_t)to_out_bits<QT>(b) << 16);
+  if constexpr (QT == kBF16) return f32x2_to_bf16x2(a, b);
+  else return (uint32_t)to_out_bits<QT>(a) | ((uint32_t)to_out_bits<QT>(b) << 16);
 }
 
 template <int QT>
@@ -77,14 +78,16 @@ __device__ __forceinline__ float from_bits(uint16_t u) {
 // product keeps ~16 significant bits: hi = round(w), lo = round(w - hi).
 template <int QT>
 __device__ __forceinline__ void split_weights(const float (&w)[8], uint4& hi, uint4& lo) {
-  uint32_t h[8], l[8];
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    h[i] = to_out_bits<QT>(w[i]);
-    l[i] = to_out_bits<QT>(w[i] - from_bits<QT>((uint16_t)h[i]));
+  for (int i = 0; i < 4; ++i) {
+    h[i] = pack2<QT>(w[2 * i], w[2 * i + 1]);
+    const float h0 = from_bits<QT>((uint16_t)h[i]);
+    const float h1 = from_bits<QT>((uint16_t)(h[i] >> 16));
+    l[i] = pack2<QT>(w[2 * i] - h0, w[2 * i + 1] - h1);
   }
-  hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-  lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
 // select 16-bit halves: lo(x), lo(y) or hi(x), hi(y)
@@ -280,11 +283,13 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
 
   // the 16-bit V values of this lane's 4 tokens of a block; slots past the
   // block's end may hold NaN and their weight 0 cannot cancel NaN, so they
-  // are replaced by 0
+  // are replaced by 0.  Only a partial block has such slots (look-ahead
+  // blocks were read as zeros): full ones skip the selects.
   auto vvals = [&](const BlockRegs<KV, D>& r, uint32_t (&vw)[4][L::DT / 2]) {
+    const bool full = r.limit >= 16;
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const bool keep = gq * 4 + i4 < r.limit;
+      const bool keep = full || gq * 4 + i4 < r.limit;
       if constexpr (KV == kFP8) {
         uint32_t raw[L::VB / 4];
         if constexpr (L::VB == 8) { raw[0] = r.v[i4].x; raw[1] = r.v[i4].y; }
