@@ -19,6 +19,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 // running-max seed: finite, far below any real score, so exp2(seed - seed) = 1 and
 // exp2(seed - real) = 0 without ever forming inf - inf
 constexpr float kMaxSeed = -1.0e30f;
+// An online-softmax reference maximum may lag the true running maximum by up to
+// this much (log2 units): weights are then at most 2^kLazyRescale, numerator and
+// denominator share the reference, and the accumulators are rescaled only when
+// a score passes the reference by more than this.
+constexpr float kLazyRescale = 8.0f;
 
 // ---------------------------------------------------------------------------
 // parameters of one paged_attn_step, as the kernels see them

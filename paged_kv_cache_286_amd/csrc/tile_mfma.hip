@@ -246,8 +246,10 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     r.limit = i < cnt ? min(16, it.L - b * 16) : 0;
     if ((unsigned)phys >= (unsigned)p.num_blocks) { phys = 0; r.limit = 0; }
     const size_t boff = ((size_t)phys * p.num_kv_heads + it.kvh) * L::BLKB;
-    // a block with no tokens is not read (the count kept scalar: no waterfall loop)
-    const int bytes = __builtin_amdgcn_readfirstlane(r.limit > 0 ? L::BLKB : 0);
+    // only the block's existing token rows are in range: the rest (look-ahead
+    // blocks entirely) read as zeros with no memory access, so no V slot past
+    // the end needs a select (the count kept scalar: no waterfall loop)
+    const int bytes = __builtin_amdgcn_readfirstlane(r.limit * L::ROWB);
     const __amdgpu_buffer_rsrc_t kres = block_rsrc(p.k_pool + boff, bytes);
     const __amdgpu_buffer_rsrc_t vres = block_rsrc(p.v_pool + boff, bytes);
 #pragma unroll
@@ -281,32 +283,28 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     return s;
   };
 
-  // the 16-bit V values of this lane's 4 tokens of a block; slots past the
-  // block's end may hold NaN and their weight 0 cannot cancel NaN, so they
-  // are replaced by 0.  Only a partial block has such slots (look-ahead
-  // blocks were read as zeros): full ones skip the selects.
+  // the 16-bit V values of this lane's 4 tokens of a block (slots past the
+  // block's end were read as zeros, so their weight 0 multiplies 0, never NaN)
   auto vvals = [&](const BlockRegs<KV, D>& r, uint32_t (&vw)[4][L::DT / 2]) {
-    const bool full = r.limit >= 16;
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const bool keep = full || gq * 4 + i4 < r.limit;
       if constexpr (KV == kFP8) {
         uint32_t raw[L::VB / 4];
         if constexpr (L::VB == 8) { raw[0] = r.v[i4].x; raw[1] = r.v[i4].y; }
         else { raw[0] = r.v[i4]; }
 #pragma unroll
         for (int e = 0; e < L::VB / 4; ++e) {
-          vw[i4][2 * e] = keep ? fp8x2_to_16<QT, false>(raw[e]) : 0u;
-          vw[i4][2 * e + 1] = keep ? fp8x2_to_16<QT, true>(raw[e]) : 0u;
+          vw[i4][2 * e] = fp8x2_to_16<QT, false>(raw[e]);
+          vw[i4][2 * e + 1] = fp8x2_to_16<QT, true>(raw[e]);
         }
       } else if constexpr (L::VB == 16) {
-        vw[i4][0] = keep ? r.v[i4].x : 0u;
-        vw[i4][1] = keep ? r.v[i4].y : 0u;
-        vw[i4][2] = keep ? r.v[i4].z : 0u;
-        vw[i4][3] = keep ? r.v[i4].w : 0u;
+        vw[i4][0] = r.v[i4].x;
+        vw[i4][1] = r.v[i4].y;
+        vw[i4][2] = r.v[i4].z;
+        vw[i4][3] = r.v[i4].w;
       } else {
-        vw[i4][0] = keep ? r.v[i4].x : 0u;
-        vw[i4][1] = keep ? r.v[i4].y : 0u;
+        vw[i4][0] = r.v[i4].x;
+        vw[i4][1] = r.v[i4].y;
       }
     }
   };
@@ -329,7 +327,7 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
 #pragma unroll
     for (int i = 0; i < 8; ++i) mx = fmaxf(mx, ok[i] ? sv[i] : -__builtin_inff());
     mx = max_xor32(max_xor16(mx));
-    const float mn = fmaxf(m, mx);
+    const float mn = mx > m + kLazyRescale ? mx : m;   // lazy reference maximum
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
     float pw[8];
     float ps = 0.f;
@@ -340,7 +338,7 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     }
     lsum = lsum * alpha + ps;
     m = mn;
-    if (__any(alpha != 1.f)) {       // the running max rarely moves after the first blocks
+    if (__any(alpha != 1.f)) {       // the reference rarely moves after the first blocks
 #pragma unroll
       for (int j = 0; j < L::DT; ++j) o[j] *= alpha;
     }
