@@ -334,11 +334,18 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) 
 
 // Merge the partitions of every (row, query head) whose context was split.
 // A row of a prefill chunk sees keys 0..its position, split by the chunk
-// kernel's partition size; a decode row sees the whole context.
-template <int QT, int D>
-__global__ __launch_bounds__(64) void split_reduce_kernel(StepParams p) {
-  const int h = blockIdx.x;
+// kernel's partition size; a decode row sees the whole context.  A workgroup
+// takes HPW heads of one row, one wave each: in steps with prefill chunks,
+// whose rows mostly have nothing to merge, kMultiReduceHeads per workgroup cut
+// the workgroups that only check and leave; decode steps keep one head per
+// workgroup.
+constexpr int kMultiReduceHeads = 4;
+template <int QT, int D, int HPW>
+__global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
+  const int h = blockIdx.x * HPW + (HPW > 1 ? (int)(threadIdx.x >> 6) : 0);
+  const int lane = threadIdx.x & 63;
   const int row = blockIdx.y;
+  if (h >= p.num_q_heads) return;
   int L, pt;
   if (p.row_seq != nullptr) {
     const int seq = p.row_seq[row];
@@ -367,11 +374,11 @@ __global__ __launch_bounds__(64) void split_reduce_kernel(StepParams p) {
     ls = __builtin_fmaf(ml[2 * q + 1], f, ls);
 #pragma unroll
     for (int c = 0; c < D / 64; ++c)
-      o[c] = __builtin_fmaf(po[(size_t)q * D + c * 64 + threadIdx.x], f, o[c]);
+      o[c] = __builtin_fmaf(po[(size_t)q * D + c * 64 + lane], f, o[c]);
   }
 #pragma unroll
   for (int c = 0; c < D / 64; ++c)
-    reinterpret_cast<uint16_t*>(p.out)[rh * D + c * 64 + threadIdx.x] = to_out_bits<QT>(o[c] / ls);
+    reinterpret_cast<uint16_t*>(p.out)[rh * D + c * 64 + lane] = to_out_bits<QT>(o[c] / ls);
 }
 
 // inclusive scan of v over the 1024 threads of the workgroup
@@ -512,15 +519,26 @@ hipError_t launch_decode(const StepParams& p, const StepPlan& plan, hipStream_t 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_reduce(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
-  const dim3 grid((uint32_t)p.num_q_heads, (uint32_t)p.total_q);
-  (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
+template <int HPW>
+void reduce_typed(const StepParams& p, const StepPlan& plan, dim3 grid, hipStream_t stream) {
+  const dim3 block(64 * HPW);
   if (plan.q_dtype == kBF16) {
-    if (plan.head_dim == 128) hipLaunchKernelGGL((split_reduce_kernel<kBF16, 128>), grid, dim3(64), 0, stream, p);
-    else hipLaunchKernelGGL((split_reduce_kernel<kBF16, 64>), grid, dim3(64), 0, stream, p);
+    if (plan.head_dim == 128) hipLaunchKernelGGL((split_reduce_kernel<kBF16, 128, HPW>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((split_reduce_kernel<kBF16, 64, HPW>), grid, block, 0, stream, p);
   } else {
-    if (plan.head_dim == 128) hipLaunchKernelGGL((split_reduce_kernel<kF16, 128>), grid, dim3(64), 0, stream, p);
-    else hipLaunchKernelGGL((split_reduce_kernel<kF16, 64>), grid, dim3(64), 0, stream, p);
+    if (plan.head_dim == 128) hipLaunchKernelGGL((split_reduce_kernel<kF16, 128, HPW>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((split_reduce_kernel<kF16, 64, HPW>), grid, block, 0, stream, p);
+  }
+}
+
+hipError_t launch_reduce(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
+  (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
+  if (p.row_seq != nullptr) {
+    constexpr int H = kMultiReduceHeads;
+    const dim3 grid((uint32_t)((p.num_q_heads + H - 1) / H), (uint32_t)p.total_q);
+    reduce_typed<H>(p, plan, grid, stream);
+  } else {
+    reduce_typed<1>(p, plan, dim3((uint32_t)p.num_q_heads, (uint32_t)p.total_q), stream);
   }
   return hipGetLastError();
 }
