@@ -25,6 +25,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / f16 matrix rate, vendor figure (no sparsity)
 METRIC = "paged decode attention: KV-read GB/s (% of HBM peak), batch-steps/s"
 
 
@@ -41,16 +42,27 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs, if still current."""
+def measured_counters(workload, kernel):
+    """Counter record of `kernel` from committed rocprofv3 runs (HBM bytes per launch,
+    L2 hit rate, MFMA busy fraction), if the kernel sources have not changed since."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
-        return None
+        return {}
     with open(path) as f:
         t = json.load(f)
     if t.get("source_digest") != source_digest():
-        return None
-    return t.get("hbm_bytes_per_launch")
+        return {}
+    return t
+
+
+def attention_flops(plan):
+    """Multiply-adds x 2 of the step's attention: QK^T and PV over every (row, key)
+    pair the causal mask keeps, for every query head."""
+    D, H = plan.cfg.head_dim, plan.cfg.num_q_heads
+    pairs = 0
+    for L, Q in zip(plan.context_lens.tolist(), plan.query_lens.tolist()):
+        pairs += Q * (L - Q) + Q * (Q + 1) // 2
+    return 4 * D * H * pairs
 
 
 def cpu_baseline(wl, seconds):
@@ -171,11 +183,25 @@ def main():
                          pk.pkv_kernel_name(pk.PKV_KERNEL_STEP_MFMA)) if k in kernels]
     dom = timed[0] if timed else None
     if dom in kernels:
-        achieved = alg["unique"] / (kernels[dom]["avg_us"] / 1e6) / 1e9
-        traffic = measured_traffic(args.workload, dom)
-        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": traffic, "algorithmic_bytes_per_launch": alg["unique"]}
+        meas = measured_counters(args.workload, dom)
+        secs = kernels[dom]["avg_us"] / 1e6
+        if int((p.query_lens == 1).sum()) == 0:
+            # prompt rows only: the tile's matrix work bounds it, not its few KV bytes
+            flops = attention_flops(p)
+            achieved = flops / secs / 1e12
+            roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "traffic": meas.get("hbm_bytes_per_launch"),
+                        "algorithmic_flops_per_launch": flops}
+        else:
+            achieved = alg["unique"] / secs / 1e9
+            roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": meas.get("hbm_bytes_per_launch"),
+                        "algorithmic_bytes_per_launch": alg["unique"]}
+        roofline["l2_hit_rate"] = meas.get("tcc_hit_rate")
+        roofline["mfma_busy"] = meas.get("mfma_busy_frac")
     cpu = None
     if not args.no_cpu_baseline:
         log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
