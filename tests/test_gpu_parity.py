@@ -322,7 +322,7 @@ def _sample_seqs(p, n=6, seed=0):
     pick = {int(np.argmax(lens)), int(np.argmin(lens)), int(np.argmax(p.query_lens))}
     if p.shared_seqs is not None:
         pick.update(int(x) for x in p.shared_seqs[:2])
-    while len(pick) < n + 3:
+    while len(pick) < min(n + 3, p.num_seqs):
         pick.add(int(rng.integers(0, p.num_seqs)))
     return sorted(pick)
 
@@ -342,7 +342,8 @@ def _check_appended(wl, ds, n=64):
         assert np.all(u == wl.k.poison)
 
 
-@pytest.mark.parametrize("name", ["decode_7b", "long_tail", "mixed_prefill", "fp8_gqa_long"])
+@pytest.mark.parametrize("name", ["decode_7b", "long_tail", "mixed_prefill", "fp8_gqa_long",
+                                  "prefill_chunks"])
 def test_full_size_workload_sampled(name):
     _say(f"[gpu] generating {name}")
     wl = W.generate(W.make_plan(name))
@@ -352,6 +353,8 @@ def test_full_size_workload_sampled(name):
     heads = None
     if name == "fp8_gqa_long":
         heads = [0, 1, 7, 8, 31, 40, 63]
+    if name == "prefill_chunks":            # every row of all four prompts, three heads
+        heads = [0, 13, 31]
     _check(wl, ds, seqs=seqs, heads=heads)
     # every output of the step is finite
     out = oracle.decode_bits(ds.out_bits(), wl.cfg.q_dtype)
