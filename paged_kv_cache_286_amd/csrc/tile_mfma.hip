@@ -214,17 +214,26 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
       }
     }
   }
+  // Every word is read with readlane and the choice among them is made on the
+  // scalar results: a select over the lane-held array itself was turned into
+  // an indexed load from scratch memory, which then stalled each block's loads.
   auto lane_word = [&](const int (&a)[TW], int i) -> int {
-    int v = a[0];
+    int v = __builtin_amdgcn_readlane(a[0], i & 63);
 #pragma unroll
-    for (int w = 1; w < TW; ++w) v = (i >> 6) == w ? a[w] : v;
-    return __builtin_amdgcn_readlane(v, i & 63);
+    for (int w = 1; w < TW; ++w) {
+      const int x = __builtin_amdgcn_readlane(a[w], i & 63);
+      v = (i >> 6) == w ? x : v;
+    }
+    return v;
   };
   auto lane_float = [&](const float (&a)[TW], int i) -> float {
-    float v = a[0];
+    int v = __builtin_amdgcn_readlane(__float_as_int(a[0]), i & 63);
 #pragma unroll
-    for (int w = 1; w < TW; ++w) v = (i >> 6) == w ? a[w] : v;
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), i & 63));
+    for (int w = 1; w < TW; ++w) {
+      const int x = __builtin_amdgcn_readlane(__float_as_int(a[w]), i & 63);
+      v = (i >> 6) == w ? x : v;
+    }
+    return __int_as_float(v);
   };
 
   float m = kMaxSeed, lsum = 0.f;
