@@ -111,14 +111,14 @@ struct Layout {
   size_t q_start_off = 0, row_seq_off = 0, chunk_count_off = 0, chunk_entries_off = 0;
   size_t ml_off = 0, o_off = 0, total = 0;
   int32_t part_tokens = 0, chunk_part_tokens = 0, max_parts = 0, chunk_max_parts = 0;
-  int32_t chunk_capacity = 0, heads_per_wg = 1, small_q = 1;
+  int32_t chunk_capacity = 0, chunk_cols = 64, heads_per_wg = 1, small_q = 1;
   bool decode_on_mfma = false;
 };
 
 // Sequences whose query_len * G fits one 16-column tile (a decode, or the few
 // rows a speculative-decoding step verifies) run as decode items, their
 // blocks shared by the workgroup's four waves; longer prefill chunks become
-// 64-column chunk entries.
+// chunk entries of chunk_entry_cols columns.
 int32_t small_q_for(int32_t group) {
   const int forced = env_int("PKV_SMALL_Q", 0);
   if (forced >= 1 && forced * group <= 16) return forced;
@@ -144,13 +144,14 @@ bool decode_on_mfma_for(const pkv_pool* pool, int32_t group) {
 int32_t round16(int64_t x) { return (int32_t)((x + 15) / 16 * 16); }
 
 // Tokens per partition of a prefill-chunk row: no split when the chunk's
-// 64-column entries already give >= 128 work items (they share the launch
-// with the decode rows), otherwise enough partitions to reach ~256 items.
-// At most 4096 (256 blocks per wave).
-int32_t chunk_part_tokens_for(int32_t group, int32_t num_kv_heads, int32_t max_ctx, int32_t max_q) {
+// entries already give >= 128 work items (they share the launch with the
+// decode rows), otherwise enough partitions to reach ~256 items.  At most
+// 4096 (256 blocks per wave).
+int32_t chunk_part_tokens_for(int32_t group, int32_t num_kv_heads, int32_t max_ctx, int32_t max_q,
+                              int32_t cols) {
   const int forced = env_int("PKV_CHUNK_PART_TOKENS", 0);
   if (forced >= 16 && forced <= 4096 && forced % 16 == 0) return forced;
-  const int64_t tiles = ((int64_t)max_q * group + 63) / 64;
+  const int64_t tiles = ((int64_t)max_q * group + cols - 1) / cols;
   const int64_t items = tiles * num_kv_heads;
   int64_t parts = items >= 128 ? 1 : (256 + items - 1) / items;
   int32_t pt = round16((max_ctx + parts - 1) / parts);
@@ -171,11 +172,13 @@ Layout layout_for(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads, i
   size_t off = 0;
   if (max_q > 1) {
     lay.small_q = small_q_for(group);
-    lay.chunk_part_tokens = chunk_part_tokens_for(group, pool->num_kv_heads, max_ctx, max_q);
+    lay.chunk_cols = pkv::chunk_entry_cols(pool->kv_dtype);
+    lay.chunk_part_tokens =
+        chunk_part_tokens_for(group, pool->num_kv_heads, max_ctx, max_q, lay.chunk_cols);
     lay.chunk_max_parts = (max_ctx + lay.chunk_part_tokens - 1) / lay.chunk_part_tokens;
     lay.max_parts = std::max(lay.max_parts, lay.chunk_max_parts);
-    // sum over sequences with q > 1 of ceil(q * group / 64) <= total_q * group / 64 + num_seqs
-    lay.chunk_capacity = (int32_t)(((int64_t)total_q * group + 63) / 64 + num_seqs);
+    // sum over sequences with q > 1 of ceil(q * group / cols) <= total_q * group / cols + num_seqs
+    lay.chunk_capacity = (int32_t)(((int64_t)total_q * group + lay.chunk_cols - 1) / lay.chunk_cols + num_seqs);
     lay.q_start_off = off;
     off = round_up(off + sizeof(int32_t) * ((size_t)num_seqs + 1), 256);
     lay.row_seq_off = off;
@@ -375,6 +378,7 @@ int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_
   p.chunk_part_tokens = multi ? lay.chunk_part_tokens : lay.part_tokens;
   p.chunk_max_parts = lay.chunk_max_parts;
   p.chunk_capacity = lay.chunk_capacity;
+  p.chunk_cols = lay.chunk_cols;
   p.small_q = multi ? lay.small_q : 1;
   p.scale_log2 = scale * pkv::kLog2e;
   if (multi) {

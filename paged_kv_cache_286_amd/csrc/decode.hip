@@ -400,7 +400,7 @@ __device__ __forceinline__ int block_scan_1024(int v, int32_t* wave_tot) {
 
 // Row offsets of every sequence (exclusive scan of query_lens), the owning
 // sequence of every query row, and the list of (sequence, first column)
-// entries of 64 (row, head) columns of every sequence with more than small_q
+// entries of chunk_cols (row, head) columns of every sequence with more than small_q
 // query rows (shorter ones, e.g. speculative-decoding verify rows, run as
 // decode items).
 // One workgroup; only launched when some sequence has more than one row.
@@ -419,7 +419,8 @@ __global__ __launch_bounds__(1024) void step_prologue_kernel(StepParams p) {
   for (int base = 0; base < p.num_seqs; base += 1024) {
     const int i = base + tid;
     const int q = i < p.num_seqs ? max(p.q_lens[i], 0) : 0;
-    const int tiles = q > p.small_q ? (q * group + 63) / 64 : 0;   // 64-column chunk entries
+    const int cc = p.chunk_cols;
+    const int tiles = q > p.small_q ? (q * group + cc - 1) / cc : 0;   // chunk entries
     const int r_incl = block_scan_1024(q, wave_tot);
     const int t_incl = block_scan_1024(tiles, wave_tot);
     const int start = carry_rows + r_incl - q;
@@ -440,7 +441,7 @@ __global__ __launch_bounds__(1024) void step_prologue_kernel(StepParams p) {
         for (int r = max(start, 0); r < stop; ++r) row_seq[r] = i;
         for (int t = 0; t < tiles && tstart + t < p.chunk_capacity; ++t) {
           entries[2 * (tstart + t)] = i;
-          entries[2 * (tstart + t) + 1] = 64 * t;
+          entries[2 * (tstart + t) + 1] = cc * t;
         }
       }
     }
@@ -453,7 +454,7 @@ __global__ __launch_bounds__(1024) void step_prologue_kernel(StepParams p) {
       for (int t = tid; t < big_tiles[k]; t += 1024)
         if (big_tstart[k] + t < p.chunk_capacity) {
           entries[2 * (big_tstart[k] + t)] = big_seq[k];
-          entries[2 * (big_tstart[k] + t) + 1] = 64 * t;
+          entries[2 * (big_tstart[k] + t) + 1] = p.chunk_cols * t;
         }
     }
     __syncthreads();

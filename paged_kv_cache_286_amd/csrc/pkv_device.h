@@ -28,6 +28,14 @@ constexpr float kLazyRescale = 8.0f;
 // ---------------------------------------------------------------------------
 // parameters of one paged_attn_step, as the kernels see them
 // ---------------------------------------------------------------------------
+// The MFMA tile kernel: kTileWaves waves per workgroup; a prefill-chunk work
+// item gives each wave tile_tiles_per_wave 16-column tiles (two for 16-bit K/V,
+// whose registers allow it; one for fp8 and for decode items), so an entry of
+// the prologue's list covers chunk_entry_cols (row, head) columns.
+constexpr int kTileWaves = 4;
+constexpr int tile_tiles_per_wave(int kv_dtype, bool split) { return (!split && kv_dtype != kFP8) ? 2 : 1; }
+constexpr int chunk_entry_cols(int kv_dtype) { return 16 * kTileWaves * tile_tiles_per_wave(kv_dtype, false); }
+
 struct StepParams {
   const void* q;             // [Tq][Hq][D]
   void* out;                 // [Tq][Hq][D]
@@ -56,6 +64,7 @@ struct StepParams {
   int32_t chunk_part_tokens; // tokens per partition of a prefill-chunk row (multiple of 16)
   int32_t chunk_max_parts;   // partitions the chunk kernel walks per entry and kv head
   int32_t chunk_capacity;    // room for chunk entries in the workspace
+  int32_t chunk_cols;        // (row, head) columns per chunk entry (chunk_entry_cols)
   int32_t small_q;           // sequences with query_len <= small_q run as decode items
   float scale_log2;          // softmax scale * log2(e)
 };

@@ -34,7 +34,6 @@
 
 namespace pkv {
 
-constexpr int kTileWaves = 4;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -150,10 +149,12 @@ struct TileItem {
 // One work item for the whole workgroup.  SPLIT (decode rows): the item is
 // one 16-column tile and the kTileWaves waves share the partition's blocks
 // (wave w takes blocks w, w + kTileWaves, ...), merged through LDS at the end.
-// !SPLIT (prefill chunks): the item is kTileWaves tiles of 16 columns, wave w
-// owns tile w and walks every block up to its own causal limit; the four
-// waves read the same blocks at the same time (one fetch beyond L1 serves
-// them all) and each writes its own columns.  K/V use ordinary (cached)
+// !SPLIT (prefill chunks): the item is kTileWaves x TPW tiles of 16 columns,
+// wave w owns tiles w*TPW .. w*TPW+TPW-1 and walks every block up to its last
+// column's causal limit; the four waves read the same blocks at the same time
+// (one fetch beyond L1 serves them all) and each writes its own columns.  With
+// two tiles per wave (16-bit K/V) a block's loads and the permutes that bring V
+// into the MFMA operand layout serve twice the matrix work.  K/V use ordinary (cached)
 // loads here: nontemporal loads for the decode items gained at most 1% with
 // fp8 K/V and cost 20% in steps that mix decodes with prefill chunks.
 template <int KV, int QT, int D, bool SPLIT>
@@ -164,15 +165,21 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar, provably
   const int n = lane & 15;          // column of this lane (token row of K it loads)
   const int gq = lane >> 4;         // lane group: tokens 4*gq..4*gq+3 / dims slice gq
-  const int tcol0 = SPLIT ? it.col0 : it.col0 + 16 * wave;   // this wave's column tile
-  if (!SPLIT && tcol0 >= it.ncols) return;                  // no columns for this wave
-  const int col = tcol0 + n;
-  const bool col_ok = col < it.ncols;
-  const int rloc = col_ok ? col / group : 0;
-  const int head = it.kvh * group + (col_ok ? col % group : 0);
-  const int row = it.row0 + rloc;
-  const int pos = it.L - it.Q + rloc;                     // last key this column sees
-  const int last_col = min(tcol0 + 15, it.ncols - 1);
+  constexpr int TPW = tile_tiles_per_wave(KV, SPLIT);
+  const int wcol0 = SPLIT ? it.col0 : it.col0 + 16 * TPW * wave;   // this wave's first column
+  if (!SPLIT && wcol0 >= it.ncols) return;                        // no columns for this wave
+  int row[TPW], head[TPW], pos[TPW];
+  bool col_ok[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int col = wcol0 + 16 * t + n;
+    col_ok[t] = col < it.ncols;
+    const int rloc = col_ok[t] ? col / group : 0;
+    head[t] = it.kvh * group + (col_ok[t] ? col % group : 0);
+    row[t] = it.row0 + rloc;
+    pos[t] = it.L - it.Q + rloc;                          // last key this column sees
+  }
+  const int last_col = min(wcol0 + 16 * TPW - 1, it.ncols - 1);
   const int max_pos = it.L - it.Q + last_col / group;
   const int tok0 = it.part * it.part_tokens;
   const int tok1 = min(tok0 + it.part_tokens, max_pos + 1);
@@ -180,12 +187,14 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   const int blk_end = (tok1 + 15) >> 4;
 
   // Q^T operand: D/4 consecutive dims of this column's query (zero for unused columns)
-  uint4 qb[L::KSTEPS];
-  {
-    const uint4* qrow = reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(p.q) + ((size_t)row * p.num_q_heads + head) * D + gq * (D / 4));
+  uint4 qb[TPW][L::KSTEPS];
 #pragma unroll
-    for (int c = 0; c < L::KSTEPS; ++c) qb[c] = col_ok ? qrow[c] : make_uint4(0, 0, 0, 0);
+  for (int t = 0; t < TPW; ++t) {
+    const uint4* qrow = reinterpret_cast<const uint4*>(
+        reinterpret_cast<const uint16_t*>(p.q) + ((size_t)row[t] * p.num_q_heads + head[t]) * D +
+        gq * (D / 4));
+#pragma unroll
+    for (int c = 0; c < L::KSTEPS; ++c) qb[t][c] = col_ok[t] ? qrow[c] : make_uint4(0, 0, 0, 0);
   }
 
   // this wave's blocks: blk_begin + first + stride * i, i < cnt
@@ -236,10 +245,15 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     return __int_as_float(v);
   };
 
-  float m = kMaxSeed, lsum = 0.f;
-  f32x4 o[L::DT];
+  float m[TPW], lsum[TPW];
+  f32x4 o[TPW][L::DT];
 #pragma unroll
-  for (int j = 0; j < L::DT; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TPW; ++t) {
+    m[t] = kMaxSeed;
+    lsum[t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < L::DT; ++j) o[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // Every call issues the same loads with no branch around them: past the
   // wave's last block the index is clamped (an L2 re-read) and the block counts
@@ -271,9 +285,11 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     }
   };
 
-  // S^T for one block: 4 scores (tokens 4*gq..+3) of this lane's column
-  auto scores = [&](const BlockRegs<KV, D>& r) -> f32x4 {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  // S^T for one block: 4 scores (tokens 4*gq..+3) of this lane's column in
+  // every tile of the wave, each K operand built once
+  auto scores = [&](const BlockRegs<KV, D>& r, f32x4 (&s)[TPW]) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < L::KSTEPS; ++st) {
       uint4 a;
@@ -287,9 +303,9 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
       } else {
         a = r.k[st];
       }
-      s = mfma32<QT>(a, qb[st], s);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) s[t] = mfma32<QT>(a, qb[t][st], s[t]);
     }
-    return s;
   };
 
   // the 16-bit V values of this lane's 4 tokens of a block (slots past the
@@ -320,44 +336,48 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
 
   // online softmax and PV over a pair of blocks (32 tokens)
   auto attend_pair = [&](const BlockRegs<KV, D>& r0, const BlockRegs<KV, D>& r1) {
-    const f32x4 s0 = scores(r0);
-    const f32x4 s1 = scores(r1);
-    float sv[8];
-    bool ok[8];
-    float mx = -__builtin_inff();
+    f32x4 s0[TPW], s1[TPW];
+    scores(r0, s0);
+    scores(r1, s1);
+    uint4 pb_hi[TPW], pb_lo[TPW];
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int t = gq * 4 + i4;
-      ok[i4] = col_ok && t < r0.limit && r0.base + t <= pos;
-      ok[4 + i4] = col_ok && t < r1.limit && r1.base + t <= pos;
-      sv[i4] = s0[i4] * (p.scale_log2 * r0.ksc);
-      sv[4 + i4] = s1[i4] * (p.scale_log2 * r1.ksc);
+    for (int t = 0; t < TPW; ++t) {
+      float sv[8];
+      bool ok[8];
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int tk = gq * 4 + i4;
+        ok[i4] = col_ok[t] && tk < r0.limit && r0.base + tk <= pos[t];
+        ok[4 + i4] = col_ok[t] && tk < r1.limit && r1.base + tk <= pos[t];
+        sv[i4] = s0[t][i4] * (p.scale_log2 * r0.ksc);
+        sv[4 + i4] = s1[t][i4] * (p.scale_log2 * r1.ksc);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, ok[i] ? sv[i] : -__builtin_inff());
+      mx = max_xor32(max_xor16(mx));
+      const float mn = mx > m[t] + kLazyRescale ? mx : m[t];   // lazy reference maximum
+      const float alpha = __builtin_amdgcn_exp2f(m[t] - mn);
+      float pw[8];
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pw[i] = ok[i] ? __builtin_amdgcn_exp2f(sv[i] - mn) : 0.f;
+        ps += pw[i];
+      }
+      lsum[t] = lsum[t] * alpha + ps;
+      m[t] = mn;
+      if (__any(alpha != 1.f)) {     // the reference rarely moves after the first blocks
+#pragma unroll
+        for (int j = 0; j < L::DT; ++j) o[t][j] *= alpha;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pw[i] *= r0.vsc;
+        pw[4 + i] *= r1.vsc;
+      }
+      split_weights<QT>(pw, pb_hi[t], pb_lo[t]);
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, ok[i] ? sv[i] : -__builtin_inff());
-    mx = max_xor32(max_xor16(mx));
-    const float mn = mx > m + kLazyRescale ? mx : m;   // lazy reference maximum
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    float pw[8];
-    float ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pw[i] = ok[i] ? __builtin_amdgcn_exp2f(sv[i] - mn) : 0.f;
-      ps += pw[i];
-    }
-    lsum = lsum * alpha + ps;
-    m = mn;
-    if (__any(alpha != 1.f)) {       // the reference rarely moves after the first blocks
-#pragma unroll
-      for (int j = 0; j < L::DT; ++j) o[j] *= alpha;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pw[i] *= r0.vsc;
-      pw[4 + i] *= r1.vsc;
-    }
-    uint4 pb_hi, pb_lo;
-    split_weights<QT>(pw, pb_hi, pb_lo);
 
     uint32_t v0[4][L::DT / 2], v1[4][L::DT / 2];
     vvals(r0, v0);
@@ -376,8 +396,11 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
         a.z = pick16<false>(v1[0][j / 2], v1[1][j / 2]);
         a.w = pick16<false>(v1[2][j / 2], v1[3][j / 2]);
       }
-      o[j] = mfma32<QT>(a, pb_hi, o[j]);
-      if constexpr (KV != kFP8) o[j] = mfma32<QT>(a, pb_lo, o[j]);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        o[t][j] = mfma32<QT>(a, pb_hi[t], o[t][j]);
+        if constexpr (KV != kFP8) o[t][j] = mfma32<QT>(a, pb_lo[t], o[t][j]);
+      }
     }
   };
 
@@ -406,7 +429,8 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   }
 
   // the column's running sum is spread over the 4 lane groups
-  lsum = sum_xor32(sum_xor16(lsum));
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) lsum[t] = sum_xor32(sum_xor16(lsum[t]));
 
   if constexpr (SPLIT) {
     // Merge the four waves' partials of the same 16 columns in two rounds
@@ -417,24 +441,24 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
 #pragma unroll
       for (int j = 0; j < L::DT; ++j)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) sm_o[(slot * 16 + n) * D + (gq * 4 + i4) * L::DT + j] = o[j][i4];
+        for (int i4 = 0; i4 < 4; ++i4) sm_o[(slot * 16 + n) * D + (gq * 4 + i4) * L::DT + j] = o[0][j][i4];
       if (gq == 0) {
-        sm_m[slot * 16 + n] = m;
-        sm_l[slot * 16 + n] = lsum;
+        sm_m[slot * 16 + n] = m[0];
+        sm_l[slot * 16 + n] = lsum[0];
       }
     };
     auto take = [&](int slot) {
       const float m2 = sm_m[slot * 16 + n];
-      const float M = fmaxf(m, m2);
-      const float f1 = __builtin_amdgcn_exp2f(m - M);
+      const float M = fmaxf(m[0], m2);
+      const float f1 = __builtin_amdgcn_exp2f(m[0] - M);
       const float f2 = __builtin_amdgcn_exp2f(m2 - M);
-      lsum = lsum * f1 + sm_l[slot * 16 + n] * f2;
+      lsum[0] = lsum[0] * f1 + sm_l[slot * 16 + n] * f2;
 #pragma unroll
       for (int j = 0; j < L::DT; ++j)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4)
-          o[j][i4] = o[j][i4] * f1 + sm_o[(slot * 16 + n) * D + (gq * 4 + i4) * L::DT + j] * f2;
-      m = M;
+          o[0][j][i4] = o[0][j][i4] * f1 + sm_o[(slot * 16 + n) * D + (gq * 4 + i4) * L::DT + j] * f2;
+      m[0] = M;
     };
     if (wave >= 2) put(wave - 2);
     __syncthreads();
@@ -446,28 +470,29 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     take(0);
   }
 
-  {
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
     // this wave holds its columns' result over the partition: write it out
-    if (!col_ok || pos < tok0) return;             // no key of this partition is visible
-    const size_t rh = (size_t)row * p.num_q_heads + head;
-    const int nparts = (pos + it.part_tokens) / it.part_tokens;     // ceil((pos + 1) / pt)
+    if (!col_ok[t] || pos[t] < tok0) continue;     // no key of this partition is visible
+    const size_t rh = (size_t)row[t] * p.num_q_heads + head[t];
+    const int nparts = (pos[t] + it.part_tokens) / it.part_tokens;   // ceil((pos + 1) / pt)
     if (nparts == 1) {
-      const float inv = 1.f / lsum;
+      const float inv = 1.f / lsum[t];
       uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + rh * D;
 #pragma unroll
       for (int j = 0; j < L::DT; ++j)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) orow[(gq * 4 + i4) * L::DT + j] = to_out_bits<QT>(o[j][i4] * inv);
+        for (int i4 = 0; i4 < 4; ++i4) orow[(gq * 4 + i4) * L::DT + j] = to_out_bits<QT>(o[t][j][i4] * inv);
     } else {
       const size_t idx = rh * it.max_parts + it.part;
       float* po = p.part_o + idx * D;
 #pragma unroll
       for (int j = 0; j < L::DT; ++j)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) po[(gq * 4 + i4) * L::DT + j] = o[j][i4];
+        for (int i4 = 0; i4 < 4; ++i4) po[(gq * 4 + i4) * L::DT + j] = o[t][j][i4];
       if (gq == 0) {
-        p.part_ml[idx * 2] = m;
-        p.part_ml[idx * 2 + 1] = lsum;
+        p.part_ml[idx * 2] = m[t];
+        p.part_ml[idx * 2 + 1] = lsum[t];
       }
     }
   }
@@ -535,7 +560,7 @@ __device__ __forceinline__ void chunk_wgs(const StepParams& p, int wg, int nwg, 
     if (it.Q < 1 || it.Q > it.L || it.L > p.max_blocks * 16 || it.row0 < 0 ||
         it.row0 + it.Q > p.total_q || it.col0 >= it.ncols)
       continue;
-    const int last_col = min(it.col0 + 16 * kTileWaves - 1, it.ncols - 1);
+    const int last_col = min(it.col0 + p.chunk_cols - 1, it.ncols - 1);
     const int max_pos = it.L - it.Q + last_col / group;
     if (it.part * it.part_tokens > max_pos || max_pos + 1 > p.max_parts * it.part_tokens) continue;
     tile_item<KV, QT, D, false>(p, it, group, sm_o, sm_m, sm_l);
@@ -557,7 +582,7 @@ __global__ __launch_bounds__(kTileWaves * 64) void decode_mfma_kernel(StepParams
 // traffic across the whole launch.  Decode ids decode as x fastest, then
 // sequence, then partition.
 template <int KV, int QT, int D>
-__global__ __launch_bounds__(kTileWaves * 64) void step_mfma_kernel(StepParams p, int n_chunk_wgs,
+__global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void step_mfma_kernel(StepParams p, int n_chunk_wgs,
                                                                    int stride, int dec_x, int dec_y) {
   __shared__ float sm_o[2 * 16 * D];
   __shared__ float sm_m[2 * 16];
