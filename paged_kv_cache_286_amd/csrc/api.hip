@@ -143,17 +143,22 @@ bool decode_on_mfma_for(const pkv_pool* pool, int32_t group) {
 
 int32_t round16(int64_t x) { return (int32_t)((x + 15) / 16 * 16); }
 
-// Tokens per partition of a prefill-chunk row: no split when the chunk's
-// entries already give >= 128 work items (they share the launch with the
-// decode rows), otherwise enough partitions to reach ~256 items.  At most
-// 4096 (256 blocks per wave).
+// Tokens per partition of a prefill-chunk row.  In a step with many
+// sequences the decode items fill the launch: no split when the chunk's
+// entries already give >= 128 work items, otherwise enough partitions to reach
+// ~256.  A step of at most kFewSeqs sequences has too few decode rows to fill
+// 256 CUs, so its chunks are split to ~512 items (a lone 512-row chunk over
+// 2,560 keys at the 7B shape: 179 us unsplit, 95 us in four partitions).
+// At most 4096 (256 blocks per wave).
+constexpr int32_t kFewSeqs = 8;
 int32_t chunk_part_tokens_for(int32_t group, int32_t num_kv_heads, int32_t max_ctx, int32_t max_q,
-                              int32_t cols) {
+                              int32_t cols, int32_t num_seqs) {
   const int forced = env_int("PKV_CHUNK_PART_TOKENS", 0);
   if (forced >= 16 && forced <= 4096 && forced % 16 == 0) return forced;
   const int64_t tiles = ((int64_t)max_q * group + cols - 1) / cols;
   const int64_t items = tiles * num_kv_heads;
-  int64_t parts = items >= 128 ? 1 : (256 + items - 1) / items;
+  const int64_t want = num_seqs <= kFewSeqs ? 512 : 256;
+  int64_t parts = (num_seqs > kFewSeqs && items >= 128) ? 1 : (want + items - 1) / items;
   int32_t pt = round16((max_ctx + parts - 1) / parts);
   return std::min(4096, std::max(64, pt));
 }
@@ -174,7 +179,7 @@ Layout layout_for(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads, i
     lay.small_q = small_q_for(group);
     lay.chunk_cols = pkv::chunk_entry_cols(pool->kv_dtype);
     lay.chunk_part_tokens =
-        chunk_part_tokens_for(group, pool->num_kv_heads, max_ctx, max_q, lay.chunk_cols);
+        chunk_part_tokens_for(group, pool->num_kv_heads, max_ctx, max_q, lay.chunk_cols, num_seqs);
     lay.chunk_max_parts = (max_ctx + lay.chunk_part_tokens - 1) / lay.chunk_part_tokens;
     lay.max_parts = std::max(lay.max_parts, lay.chunk_max_parts);
     // sum over sequences with q > 1 of ceil(q * group / cols) <= total_q * group / cols + num_seqs
