@@ -405,7 +405,14 @@ int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_
             ? timed_launch(PKV_KERNEL_DECODE_MFMA, s, [&] { return pkv::launch_decode_mfma(p, plan, s); })
             : timed_launch(PKV_KERNEL_DECODE, s, [&] { return pkv::launch_decode(p, plan, s); });
   }
-  if (e == hipSuccess && lay.max_parts > 1)
+  // When every sequence has max_query_len rows (total_q == num_seqs * max_q) and
+  // that exceeds small_q, every row is a prompt row; if their partition covers
+  // the whole context no row has partitions to merge and the merge launch (one
+  // workgroup per row and four heads) is skipped.
+  const bool all_prompt_rows = multi && (int64_t)num_seqs * max_query_len == total_q_tokens &&
+                               max_query_len > lay.small_q;
+  const bool merge = lay.max_parts > 1 && !(all_prompt_rows && lay.chunk_max_parts == 1);
+  if (e == hipSuccess && merge)
     e = timed_launch(PKV_KERNEL_REDUCE, s, [&] { return pkv::launch_reduce(p, plan, s); });
   return hip_status(e);
 }

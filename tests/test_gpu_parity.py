@@ -157,6 +157,18 @@ def test_mixed_step_decode_verify_and_prefill_rows(kv):
     _check(wl, _run(wl, f"mixed rows kv={kv}"))
 
 
+@pytest.mark.parametrize("chunk_pt", ["0", "64"])
+def test_uniform_prompt_steps(chunk_pt, monkeypatch):
+    # every sequence a whole prompt (or one chunk) of the same length: the merge
+    # launch is skipped only when no chunk row is split ("0": the library's own
+    # partition; "64": forced splits, so partitions must be merged)
+    monkeypatch.setenv("PKV_CHUNK_PART_TOKENS", chunk_pt)
+    for lens, qlens in (([700, 700], [700, 700]), ([2560], [512]), ([300, 300, 300], [300, 300, 300])):
+        cfg = W.Config("uni", "uni", 8, 8, 128, 16, 400, W.BF16, W.BF16, 17)
+        wl = W.generate(W.custom_plan(cfg, lens, qlens, 17))
+        _check(wl, _run(wl, f"uniform prompts {lens}/{qlens} chunk_pt={chunk_pt}"))
+
+
 @pytest.mark.parametrize("chunk_pt", [64, 256, 1024])
 def test_chunk_partition_sizes(chunk_pt, monkeypatch):
     monkeypatch.setenv("PKV_CHUNK_PART_TOKENS", str(chunk_pt))
