@@ -97,39 +97,29 @@ __device__ __forceinline__ int uniform_load(const int32_t* ptr) {
   return __builtin_amdgcn_readfirstlane(*ptr);
 }
 
-// Buffer-resource loads of one K or V block.  The resource's record count is
-// the block's byte size, or 0 for a block that counts no tokens (the clamped
-// look-ahead past a wave's last block, an invalid table entry): an
-// out-of-range buffer load returns zeros without touching memory, so those
-// issue the same instructions with no branch and move no bytes.  Word 3 is the
-// gfx9-family untyped-buffer descriptor (32-bit data format).
+// Buffer-resource loads of one K or V block.  The resource's record count
+// covers the block's existing token rows only (0 for a block that counts no
+// tokens: the clamped look-ahead past a wave's last block, an invalid table
+// entry): an out-of-range buffer load returns zeros without touching memory,
+// so those issue the same instructions with no branch and move no bytes.
+// Word 3 is the gfx9-family untyped-buffer descriptor (32-bit data format).
 constexpr int kBufferRsrcWord3 = 0x00020000;
 typedef uint32_t u32x4_buf __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, kBufferRsrcWord3);
 }
-// aux bit 1 (value 2) is the nontemporal hint of the load
+
+// NT sets the load's nontemporal hint (aux bit 1, value 2).  A K/V block that
+// no other reader of the step touches is read exactly once: a nontemporal load
+// (streaming policy) passes it by the caches.  On MI355X a random gather of
+// 4 KiB runs moves ~6.85 TB/s this way against ~6.1 TB/s with ordinary loads
+// -- but lines that other waves read again soon (a shared prefix, the four
+// waves of a prefill tile) then come from HBM again, so those keep ordinary
+// loads.
 template <bool NT>
 __device__ __forceinline__ uint4 load_block16(__amdgpu_buffer_rsrc_t r, int byte_off) {
   const u32x4_buf v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, NT ? 2 : 0);
   return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// A K/V block that no other reader of the step touches is read exactly once:
-// a nontemporal load (streaming policy) passes it by the caches.  On MI355X a
-// random gather of 4 KiB runs moves ~6.85 TB/s this way against ~6.1 TB/s with
-// ordinary loads -- but lines that other waves read again soon (a shared
-// prefix) then come from HBM again, so those keep ordinary loads.  Used by the
-// VALU decode kernel.
-typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
-template <bool NT>
-__device__ __forceinline__ uint4 load_kv16(const void* ptr) {
-  if constexpr (NT) {
-    const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(ptr));
-    return make_uint4(v.x, v.y, v.z, v.w);
-  } else {
-    return *reinterpret_cast<const uint4*>(ptr);
-  }
 }
 
 // unpack a 16-byte load of KV elements into floats (8 for 16-bit types, 16 for fp8)

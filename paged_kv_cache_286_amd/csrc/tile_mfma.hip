@@ -256,9 +256,9 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   }
 
   // Every call issues the same loads with no branch around them: past the
-  // wave's last block the index is clamped (an L2 re-read) and the block counts
-  // no tokens, so the compiler can wait for exactly the block it consumes
-  // instead of draining all outstanding loads at a control-flow join.
+  // wave's last block the index is clamped and the block counts no tokens (its
+  // loads move no bytes), so the compiler can wait for exactly the block it
+  // consumes instead of draining all outstanding loads at a control-flow join.
   auto issue = [&](int i, BlockRegs<KV, D>& r) {
     const int ic = min(i, cnt - 1);
     const int b = blk_begin + first + stride * ic;
