@@ -533,7 +533,7 @@ __device__ __forceinline__ void decode_wg(const StepParams& p, int x, int seq, i
 }
 
 // Prefill chunks (query_len > 1): the prologue lists (sequence, first column)
-// entries of 64 columns each; `nwg` workgroups starting at `wg` stride over
+// entries of chunk_cols columns each; `nwg` workgroups starting at `wg` stride over
 // entries x kv heads x partitions.
 template <int KV, int QT, int D>
 __device__ __forceinline__ void chunk_wgs(const StepParams& p, int wg, int nwg, float* sm_o,
