@@ -113,6 +113,13 @@ struct TileLay {
 };
 
 typedef uint32_t u32x2_buf __attribute__((ext_vector_type(2)));
+// 32-bit word w of a token's V slice as loaded (VB bytes per lane)
+template <int VB, typename T>
+__device__ __forceinline__ uint32_t vword(const T& v, int w) {
+  if constexpr (VB == 16) return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+  else if constexpr (VB == 8) return w == 0 ? v.x : v.y;
+  else return v;
+}
 template <int VB> struct VVec;
 template <> struct VVec<16> {
   typedef uint4 T;
@@ -379,27 +386,55 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
       split_weights<QT>(pw, pb_hi[t], pb_lo[t]);
     }
 
-    uint32_t v0[4][L::DT / 2], v1[4][L::DT / 2];
-    vvals(r0, v0);
-    vvals(r1, v1);
+    // V^T operand of each 16-dim slice j: the 16-bit pairs (token t, token t+1)
+    // of dim j for tokens 0..3 of r0 and of r1
+    uint4 va[L::DT];
+    if constexpr (KV == kFP8) {
+      // one byte permute gathers tokens t, t+1 at dims j, j+1; its two
+      // conversions are then the operand words of slices j and j+1
+#pragma unroll
+      for (int j = 0; j < L::DT; j += 2) {
+        const uint32_t b = j % 4;
+        const uint32_t sel = b | ((4 + b) << 8) | ((b + 1) << 16) | ((5 + b) << 24);
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const BlockRegs<KV, D>& r = q < 2 ? r0 : r1;
+          const int tk = (q & 1) * 2;
+          const uint32_t x = vword<L::VB>(r.v[tk], j / 4);
+          const uint32_t y = vword<L::VB>(r.v[tk + 1], j / 4);
+          const uint32_t w = __builtin_amdgcn_perm(y, x, sel);
+          lo[q] = fp8x2_to_16<QT, false>(w);
+          hi[q] = fp8x2_to_16<QT, true>(w);
+        }
+        va[j] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        va[j + 1] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      }
+    } else {
+      uint32_t v0[4][L::DT / 2], v1[4][L::DT / 2];
+      vvals(r0, v0);
+      vvals(r1, v1);
+#pragma unroll
+      for (int j = 0; j < L::DT; ++j) {
+        if (j & 1) {
+          va[j].x = pick16<true>(v0[0][j / 2], v0[1][j / 2]);
+          va[j].y = pick16<true>(v0[2][j / 2], v0[3][j / 2]);
+          va[j].z = pick16<true>(v1[0][j / 2], v1[1][j / 2]);
+          va[j].w = pick16<true>(v1[2][j / 2], v1[3][j / 2]);
+        } else {
+          va[j].x = pick16<false>(v0[0][j / 2], v0[1][j / 2]);
+          va[j].y = pick16<false>(v0[2][j / 2], v0[3][j / 2]);
+          va[j].z = pick16<false>(v1[0][j / 2], v1[1][j / 2]);
+          va[j].w = pick16<false>(v1[2][j / 2], v1[3][j / 2]);
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < L::DT; ++j) {
-      uint4 a;
-      if (j & 1) {
-        a.x = pick16<true>(v0[0][j / 2], v0[1][j / 2]);
-        a.y = pick16<true>(v0[2][j / 2], v0[3][j / 2]);
-        a.z = pick16<true>(v1[0][j / 2], v1[1][j / 2]);
-        a.w = pick16<true>(v1[2][j / 2], v1[3][j / 2]);
-      } else {
-        a.x = pick16<false>(v0[0][j / 2], v0[1][j / 2]);
-        a.y = pick16<false>(v0[2][j / 2], v0[3][j / 2]);
-        a.z = pick16<false>(v1[0][j / 2], v1[1][j / 2]);
-        a.w = pick16<false>(v1[2][j / 2], v1[3][j / 2]);
-      }
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        o[t][j] = mfma32<QT>(a, pb_hi[t], o[t][j]);
-        if constexpr (KV != kFP8) o[t][j] = mfma32<QT>(a, pb_lo[t], o[t][j]);
+        o[t][j] = mfma32<QT>(va[j], pb_hi[t], o[t][j]);
+        if constexpr (KV != kFP8) o[t][j] = mfma32<QT>(va[j], pb_lo[t], o[t][j]);
       }
     }
   };
