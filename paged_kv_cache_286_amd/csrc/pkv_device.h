@@ -29,11 +29,11 @@ constexpr float kLazyRescale = 8.0f;
 // parameters of one paged_attn_step, as the kernels see them
 // ---------------------------------------------------------------------------
 // The MFMA tile kernel: kTileWaves waves per workgroup; a prefill-chunk work
-// item gives each wave tile_tiles_per_wave 16-column tiles (two for 16-bit K/V,
-// whose registers allow it; one for fp8 and for decode items), so an entry of
-// the prologue's list covers chunk_entry_cols (row, head) columns.
+// item gives each wave tile_tiles_per_wave 16-column tiles (two; one for the
+// decode items, which split their blocks over the waves instead), so an entry
+// of the prologue's list covers chunk_entry_cols (row, head) columns.
 constexpr int kTileWaves = 4;
-constexpr int tile_tiles_per_wave(int kv_dtype, bool split) { return (!split && kv_dtype != kFP8) ? 2 : 1; }
+constexpr int tile_tiles_per_wave(int, bool split) { return split ? 1 : 2; }
 constexpr int chunk_entry_cols(int kv_dtype) { return 16 * kTileWaves * tile_tiles_per_wave(kv_dtype, false); }
 
 struct StepParams {

@@ -160,8 +160,8 @@ struct TileItem {
 // wave w owns tiles w*TPW .. w*TPW+TPW-1 and walks every block up to its last
 // column's causal limit; the four waves read the same blocks at the same time
 // (one fetch beyond L1 serves them all) and each writes its own columns.  With
-// two tiles per wave (16-bit K/V) a block's loads and the permutes that bring V
-// into the MFMA operand layout serve twice the matrix work.  K/V use ordinary (cached)
+// two tiles per wave a block's loads, fp8 conversions and the permutes that
+// bring V into the MFMA operand layout serve twice the matrix work.  K/V use ordinary (cached)
 // loads here: nontemporal loads for the decode items gained at most 1% with
 // fp8 K/V and cost 20% in steps that mix decodes with prefill chunks.
 template <int KV, int QT, int D, bool SPLIT>
