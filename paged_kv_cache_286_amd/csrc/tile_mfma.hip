@@ -186,6 +186,7 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     row[t] = it.row0 + rloc;
     pos[t] = it.L - it.Q + rloc;                          // last key this column sees
   }
+  const int min_pos = it.L - it.Q + wcol0 / group;        // positions rise with the column
   const int last_col = min(wcol0 + 16 * TPW - 1, it.ncols - 1);
   const int max_pos = it.L - it.Q + last_col / group;
   const int tok0 = it.part * it.part_tokens;
@@ -341,37 +342,58 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     }
   };
 
-  // online softmax and PV over a pair of blocks (32 tokens)
-  auto attend_pair = [&](const BlockRegs<KV, D>& r0, const BlockRegs<KV, D>& r1) {
+  // online softmax and PV over a pair of blocks (32 tokens).  DENSE: both
+  // blocks are whole and every column of the wave sees all 32 tokens, so no
+  // score is masked and the scale folds into the exponent's argument (for a
+  // positive factor the maximum of the products is the product of the maximum).
+  auto attend_pair = [&](auto dense_tag, const BlockRegs<KV, D>& r0, const BlockRegs<KV, D>& r1) {
+    constexpr bool DENSE = decltype(dense_tag)::value;
     f32x4 s0[TPW], s1[TPW];
     scores(r0, s0);
     scores(r1, s1);
     uint4 pb_hi[TPW], pb_lo[TPW];
+    const float c0 = p.scale_log2 * r0.ksc, c1 = p.scale_log2 * r1.ksc;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      float sv[8];
-      bool ok[8];
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int tk = gq * 4 + i4;
-        ok[i4] = col_ok[t] && tk < r0.limit && r0.base + tk <= pos[t];
-        ok[4 + i4] = col_ok[t] && tk < r1.limit && r1.base + tk <= pos[t];
-        sv[i4] = s0[t][i4] * (p.scale_log2 * r0.ksc);
-        sv[4 + i4] = s1[t][i4] * (p.scale_log2 * r1.ksc);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, ok[i] ? sv[i] : -__builtin_inff());
-      mx = max_xor32(max_xor16(mx));
-      const float mn = mx > m[t] + kLazyRescale ? mx : m[t];   // lazy reference maximum
-      const float alpha = __builtin_amdgcn_exp2f(m[t] - mn);
       float pw[8];
       float ps = 0.f;
+      float mx, mn;
+      if constexpr (DENSE) {
+        float mx0 = s0[t][0], mx1 = s1[t][0];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pw[i] = ok[i] ? __builtin_amdgcn_exp2f(sv[i] - mn) : 0.f;
-        ps += pw[i];
+        for (int i = 1; i < 4; ++i) {
+          mx0 = fmaxf(mx0, s0[t][i]);
+          mx1 = fmaxf(mx1, s1[t][i]);
+        }
+        mx = max_xor32(max_xor16(fmaxf(mx0 * c0, mx1 * c1)));
+        mn = mx > m[t] + kLazyRescale ? mx : m[t];   // lazy reference maximum
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pw[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[t][i], c0, -mn));
+          pw[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[t][i], c1, -mn));
+        }
+      } else {
+        float sv[8];
+        bool ok[8];
+        mx = -__builtin_inff();
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int tk = gq * 4 + i4;
+          ok[i4] = col_ok[t] && tk < r0.limit && r0.base + tk <= pos[t];
+          ok[4 + i4] = col_ok[t] && tk < r1.limit && r1.base + tk <= pos[t];
+          sv[i4] = s0[t][i4] * c0;
+          sv[4 + i4] = s1[t][i4] * c1;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, ok[i] ? sv[i] : -__builtin_inff());
+        mx = max_xor32(max_xor16(mx));
+        mn = mx > m[t] + kLazyRescale ? mx : m[t];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pw[i] = ok[i] ? __builtin_amdgcn_exp2f(sv[i] - mn) : 0.f;
       }
+      const float alpha = __builtin_amdgcn_exp2f(m[t] - mn);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ps += pw[i];
       lsum[t] = lsum[t] * alpha + ps;
       m[t] = mn;
       if (__any(alpha != 1.f)) {     // the reference rarely moves after the first blocks
@@ -440,27 +462,37 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   };
 
   // register ring: NB/2 - 1 pairs are loading while the current pair is scored;
-  // pairs past the end (at most NB/2 - 1 per wave) are scored fully masked
+  // pairs past the end (at most NB/2 - 1 per wave) are scored fully masked.
+  // The wave's blocks rise in position, so the dense pairs (both blocks wholly
+  // at or before min_pos) form a prefix; it runs in a loop of its own, cut to a
+  // multiple of the ring's pairs so both loops use the same register slots.
   constexpr int NB = L::NBUF;
   constexpr int NP = NB / 2;
   BlockRegs<KV, D> buf[NB];
   if (cnt > 0) {
     const int npairs = (cnt + 1) / 2;
+    const int vis_blocks = (min_pos + 1) >> 4;   // blocks 0 .. vis_blocks-1 end at or before min_pos
+    const int dense_blocks = min(cnt, max(0, vis_blocks - blk_begin - first + stride - 1) / stride);
+    const int dense_pairs = dense_blocks / 2 / NP * NP;
 #pragma unroll
     for (int k = 0; k < NP - 1; ++k) {
       issue(2 * k, buf[2 * k]);
       issue(2 * k + 1, buf[2 * k + 1]);
     }
-    for (int q2 = 0; q2 < npairs; q2 += NP) {
+    auto run = [&](auto dense_tag, int q_begin, int q_end) {
+      for (int q2 = q_begin; q2 < q_end; q2 += NP) {
 #pragma unroll
-      for (int u = 0; u < NP; ++u) {
-        const int nxt = q2 + u + NP - 1;
-        const int slot = (u + NP - 1) % NP;
-        issue(2 * nxt, buf[2 * slot]);
-        issue(2 * nxt + 1, buf[2 * slot + 1]);
-        attend_pair(buf[2 * u], buf[2 * u + 1]);
+        for (int u = 0; u < NP; ++u) {
+          const int nxt = q2 + u + NP - 1;
+          const int slot = (u + NP - 1) % NP;
+          issue(2 * nxt, buf[2 * slot]);
+          issue(2 * nxt + 1, buf[2 * slot + 1]);
+          attend_pair(dense_tag, buf[2 * u], buf[2 * u + 1]);
+        }
       }
-    }
+    };
+    run(std::true_type{}, 0, dense_pairs);
+    run(std::false_type{}, dense_pairs, npairs);
   }
 
   // the column's running sum is spread over the 4 lane groups
