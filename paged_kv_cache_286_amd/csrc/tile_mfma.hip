@@ -124,6 +124,7 @@ template <int VB> struct VVec;
 template <> struct VVec<16> {
   typedef uint4 T;
   static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int off) { return load_block16<false>(r, off); }
+  static __device__ __forceinline__ T lds(const uint4* base, int off) { return base[off / 16]; }
 };
 template <> struct VVec<8> {
   typedef uint2 T;
@@ -131,13 +132,50 @@ template <> struct VVec<8> {
     const u32x2_buf v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
     return make_uint2(v.x, v.y);
   }
+  static __device__ __forceinline__ T lds(const uint4* base, int off) {
+    return reinterpret_cast<const uint2*>(base)[off / 8];
+  }
 };
 template <> struct VVec<4> {
   typedef uint32_t T;
   static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   }
+  static __device__ __forceinline__ T lds(const uint4* base, int off) {
+    return reinterpret_cast<const uint32_t*>(base)[off / 4];
+  }
 };
+
+// Stages of the LDS pipeline of prefill items.
+constexpr int kStages = 4;
+
+// LDS staging of prefill items: a stage is one pair of blocks, laid out as
+// K0, K1, V0, V1 (each the block's (block, head) slice, BLKB bytes); two
+// stages alternate.  K rows are stored with their 16-byte chunks permuted
+// (chunk c of row r at c ^ key(r)) so that the 16 lanes reading one chunk
+// index of 16 different rows hit 16 different bank groups; V is read along
+// rows and kept as is.
+template <int KV, int D>
+struct StageLay {
+  using L = TileLay<KV, D>;
+  static constexpr int CHB = L::BLKB / 16;            // 16-byte chunks per block
+  static constexpr int CHUNKS = 4 * CHB;              // per stage
+  static constexpr int LOADS = CHUNKS / (kTileWaves * 64);   // 16-byte loads per thread
+  static constexpr int CPR = L::ROWB / 16;            // chunks per token row
+  static_assert(CHB % 64 == 0, "each wave's chunks of a stage lie in one block");
+  static_assert(LOADS >= 1 && CHUNKS % (kTileWaves * 64) == 0, "whole loads per thread");
+  static __device__ __forceinline__ int k_chunk(int row, int c) {
+    return row * CPR + (c ^ ((row * CPR / 16) & (CPR - 1)));
+  }
+  // s_waitcnt immediate: at most n vector memory operations outstanding, no
+  // LDS/scalar operation outstanding (gfx9 fields: vmcnt [3:0] and [15:14],
+  // expcnt [6:4] left at its maximum, lgkmcnt [11:8] = 0)
+  static constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+  static_assert((kStages - 2) * LOADS < 64, "outstanding copies fit the counter");
+  // LDS of one stage; stage 0 also holds the decode items' merge buffer
+  static constexpr int STAGE0 = CHUNKS > 2 * 16 * D / 4 ? CHUNKS : 2 * 16 * D / 4;
+};
+constexpr int kWaitAll = 0x0070;   // vmcnt 0, lgkmcnt 0
 
 template <int KV, int D>
 struct BlockRegs {
@@ -166,7 +204,9 @@ struct TileItem {
 // fp8 K/V and cost 20% in steps that mix decodes with prefill chunks.
 template <int KV, int QT, int D, bool SPLIT>
 __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& it, int group,
-                                          float* sm_o, float* sm_m, float* sm_l) {
+                                          float* sm_o, float* sm_m, float* sm_l, uint4* st0 = nullptr,
+                                          uint4* st1 = nullptr, uint4* st2 = nullptr,
+                                          uint4* st3 = nullptr) {
   using L = TileLay<KV, D>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar, provably
@@ -174,7 +214,7 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   const int gq = lane >> 4;         // lane group: tokens 4*gq..4*gq+3 / dims slice gq
   constexpr int TPW = tile_tiles_per_wave(KV, SPLIT);
   const int wcol0 = SPLIT ? it.col0 : it.col0 + 16 * TPW * wave;   // this wave's first column
-  if (!SPLIT && wcol0 >= it.ncols) return;                        // no columns for this wave
+  // (a wave of a prefill item with no columns still helps stage the blocks)
   int row[TPW], head[TPW], pos[TPW];
   bool col_ok[TPW];
 #pragma unroll
@@ -211,25 +251,35 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   const int32_t* trow = p.tables + (size_t)it.seq * p.max_blocks;
   const int nb = blk_end - blk_begin;
   const int cnt = nb > first ? (nb - first + stride - 1) / stride : 0;   // <= 256 (partition <= 4096)
-  // Table entries (and fp8 scales) of the wave's blocks, lane l holding blocks
-  // l, l+64, l+128, l+192, read per block with readlane.  Loading them up front
-  // keeps scalar loads out of the block loop: a scalar load per block would be
-  // waited for together with every prefetched block's (they complete out of order).
+  // prefill items: the blocks the workgroup stages, up to its last column's limit
+  const int item_max_pos = it.L - it.Q + (it.ncols - 1) / group;
+  const int cnt_item = max(0, ((min(tok0 + it.part_tokens, item_max_pos + 1) + 15) >> 4) - blk_begin);
+  const int tbl_cnt = SPLIT ? cnt : cnt_item;
+  // Table entries (and fp8 scales) of the wave's blocks, read per block with
+  // readlane.  Loading them up front keeps scalar loads out of the block loop:
+  // a scalar load per block would be waited for together with every
+  // prefetched block's (they complete out of order).  Decode items: lane l
+  // holds block l.  Prefill items: lane l holds blocks 4l .. 4l+3, one per
+  // word, so that the pairs of an unrolled round of the stage loop find their
+  // entries in words known at compile time, and an entry is already the
+  // (block, head) slice index, or -1 for an invalid block.
   constexpr int TW = SPLIT ? 1 : 4;
   int my_tbl[TW];
   float my_ks[TW], my_vs[TW];
 #pragma unroll
   for (int w = 0; w < TW; ++w) {
-    const int i = lane + 64 * w;
-    my_tbl[w] = i < cnt ? trow[blk_begin + first + stride * i] : -1;
+    const int i = SPLIT ? lane + 64 * w : 4 * lane + w;
+    my_tbl[w] = i < tbl_cnt ? trow[blk_begin + first + stride * i] : -1;
     my_ks[w] = 1.f;
     my_vs[w] = 1.f;
+    const bool valid = (unsigned)my_tbl[w] < (unsigned)p.num_blocks;
     if constexpr (KV == kFP8) {
-      if ((unsigned)my_tbl[w] < (unsigned)p.num_blocks) {
+      if (valid) {
         my_ks[w] = p.k_scale[(size_t)my_tbl[w] * p.num_kv_heads + it.kvh];
         my_vs[w] = p.v_scale[(size_t)my_tbl[w] * p.num_kv_heads + it.kvh];
       }
     }
+    if constexpr (!SPLIT) my_tbl[w] = valid ? my_tbl[w] * p.num_kv_heads + it.kvh : -1;
   }
   // Every word is read with readlane and the choice among them is made on the
   // scalar results: a select over the lane-held array itself was turned into
@@ -466,13 +516,14 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   // The wave's blocks rise in position, so the dense pairs (both blocks wholly
   // at or before min_pos) form a prefix; it runs in a loop of its own, cut to a
   // multiple of the ring's pairs so both loops use the same register slots.
+  const int vis_blocks = (min_pos + 1) >> 4;   // blocks 0 .. vis_blocks-1 end at or before min_pos
+  const int dense_blocks = min(cnt, max(0, vis_blocks - blk_begin - first + stride - 1) / stride);
   constexpr int NB = L::NBUF;
   constexpr int NP = NB / 2;
+  if constexpr (SPLIT) {
   BlockRegs<KV, D> buf[NB];
   if (cnt > 0) {
     const int npairs = (cnt + 1) / 2;
-    const int vis_blocks = (min_pos + 1) >> 4;   // blocks 0 .. vis_blocks-1 end at or before min_pos
-    const int dense_blocks = min(cnt, max(0, vis_blocks - blk_begin - first + stride - 1) / stride);
     const int dense_pairs = dense_blocks / 2 / NP * NP;
 #pragma unroll
     for (int k = 0; k < NP - 1; ++k) {
@@ -493,6 +544,114 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     };
     run(std::true_type{}, 0, dense_pairs);
     run(std::false_type{}, dense_pairs, npairs);
+  }
+  } else {
+    // Prefill item: the four waves read the same blocks, so the workgroup
+    // stages each pair once in LDS and every wave builds its operands from
+    // there.  Blocks go straight from memory into LDS (buffer loads with the
+    // LDS destination: no registers held while they travel), kStages stages
+    // deep: pair q+kStages-1 is requested while pair q is attended.  Each
+    // stage is an LDS array of its own and the loop is unrolled over them, so
+    // the compiler can tell which outstanding copies a read depends on.  One
+    // barrier per pair: a wave first waits for its own copies of pair q (and
+    // for its reads of the previous pair), so after the barrier the whole
+    // pair is in place and the stage read before it is free for reuse.  All
+    // waves step through the item's pairs (a wave stops attending past its
+    // own last column).
+    using SL = StageLay<KV, D>;
+    constexpr int S = kStages;
+    const int np_item = (cnt_item + 1) / 2;
+    const bool has_cols = wcol0 < it.ncols;
+    const int np_w = has_cols ? (cnt + 1) / 2 : 0;
+    const int dense_pairs = has_cols ? dense_blocks / 2 : 0;
+    // tokens held by block i of the item
+    auto tokens = [&](int i) { return i < cnt_item ? min(16, it.L - (blk_begin + i) * 16) : 0; };
+    // block 2q+j: lane q/2 holds it in word 2(q%2)+j, and q%2 = u%2 for the
+    // step u of a round (rounds start at multiples of S)
+    auto entry = [&](const auto& a, int q, int j, int u) -> int {
+      return __builtin_amdgcn_readlane(__builtin_bit_cast(int, a[2 * (u & 1) + j]), (q >> 1) & 63);
+    };
+    // Copy pair q into a stage.  Wave w moves chunk groups g = k*4 + w (64
+    // chunks each, all within block g*64/CHB of the stage); lane l fills LDS
+    // chunk g*64 + l, fetching the K chunk the row permutation puts there.
+    // Rows past the block's tokens (all rows of a block past the item's end
+    // or with an invalid table entry) are out of the buffer's range.
+    auto copy_pair = [&](int q, int u, uint4* stage) {
+      int ent[2], bytes[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        ent[j] = entry(my_tbl, q, j, u);
+        bytes[j] = __builtin_amdgcn_readfirstlane(ent[j] >= 0 ? tokens(2 * q + j) * L::ROWB : 0);
+      }
+#pragma unroll
+      for (int k = 0; k < SL::LOADS; ++k) {
+        const int g = k * kTileWaves + wave;
+        const int bi = g * 64 / SL::CHB;
+        const int d = (g * 64) % SL::CHB + lane;
+        const int row = d / SL::CPR, c = d % SL::CPR;
+        const int goff = (bi < 2 ? SL::k_chunk(row, c) : d) * 16;
+        const int e = (bi & 1) ? ent[1] : ent[0];
+        const size_t boff = (size_t)(uint32_t)max(e, 0) * L::BLKB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            block_rsrc((bi < 2 ? p.k_pool : p.v_pool) + boff, (bi & 1) ? bytes[1] : bytes[0]),
+            (__attribute__((address_space(3))) void*)(stage + g * 64), 16, goff, 0, 0, 0);
+      }
+    };
+    // block j of pair q from a stage, in the register layout the ring uses
+    // (an invalid table entry is not masked here: a caller error gives wrong
+    // numbers, never an access outside the pools)
+    auto from_stage = [&](const uint4* stage, int q, int j, int u, BlockRegs<KV, D>& r) {
+      const uint4* kb = stage + j * SL::CHB;
+      const uint4* vb = stage + (2 + j) * SL::CHB;
+#pragma unroll
+      for (int c = 0; c < L::KLD; ++c) r.k[c] = kb[SL::k_chunk(n, gq * L::KLD + c)];
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) r.v[i4] = VVec<L::VB>::lds(vb, (gq * 4 + i4) * L::ROWB + n * L::VB);
+      r.base = (blk_begin + 2 * q + j) * 16;
+      r.limit = tokens(2 * q + j);
+      r.ksc = 1.f;
+      r.vsc = 1.f;
+      if constexpr (KV == kFP8) {
+        r.ksc = __int_as_float(entry(my_ks, q, j, u));
+        r.vsc = __int_as_float(entry(my_vs, q, j, u));
+      }
+    };
+    uint4* const stage[4] = {st0, st1, st2, st3};
+    if (cnt_item > 0) {
+      // the previous item's reads of the stages and its copies are done
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+      __builtin_amdgcn_s_barrier();
+      // Copies are issued without conditions (a pair past the item's end
+      // moves no bytes and is never read), so every step leaves exactly S-1
+      // pairs in flight and the compiler's count of them stays exact.
+#pragma unroll
+      for (int k = 0; k < S - 1; ++k) copy_pair(k, k, stage[k]);
+      // pairs [0, dense_end): whole blocks every column sees (cut to whole
+      // rounds of the stages); then the rest, masked, in whole rounds
+      auto run = [&](auto dense_tag, int q_begin, int q_end) {
+        for (int q0 = q_begin; q0 < q_end; q0 += S) {
+#pragma unroll
+          for (int u = 0; u < S; ++u) {
+            const int q = q0 + u;
+            // own copies of pair q landed (later pairs may still travel),
+            // own reads of pair q-1 done; then the workgroup's barrier
+            __builtin_amdgcn_s_waitcnt(SL::wait_vm((S - 2) * SL::LOADS));
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+            copy_pair(q + S - 1, u + S - 1, stage[(u + S - 1) % S]);
+            if (q < np_w) {
+              BlockRegs<KV, D> r0, r1;
+              from_stage(stage[u], q, 0, u, r0);
+              from_stage(stage[u], q, 1, u, r1);
+              attend_pair(dense_tag, r0, r1);
+            }
+          }
+        }
+      };
+      const int dense_end = dense_pairs / S * S;
+      run(std::true_type{}, 0, dense_end);
+      run(std::false_type{}, dense_end, np_item);
+    }
   }
 
   // the column's running sum is spread over the 4 lane groups
@@ -604,7 +763,8 @@ __device__ __forceinline__ void decode_wg(const StepParams& p, int x, int seq, i
 // entries x kv heads x partitions.
 template <int KV, int QT, int D>
 __device__ __forceinline__ void chunk_wgs(const StepParams& p, int wg, int nwg, float* sm_o,
-                                          float* sm_m, float* sm_l) {
+                                          float* sm_m, float* sm_l, uint4* st0, uint4* st1,
+                                          uint4* st2, uint4* st3) {
   const int group = p.num_q_heads / p.num_kv_heads;
   const int n_entries = min(uniform_load(p.chunk_count), p.chunk_capacity);
   const int per_entry = p.num_kv_heads * p.chunk_max_parts;
@@ -630,7 +790,7 @@ __device__ __forceinline__ void chunk_wgs(const StepParams& p, int wg, int nwg, 
     const int last_col = min(it.col0 + p.chunk_cols - 1, it.ncols - 1);
     const int max_pos = it.L - it.Q + last_col / group;
     if (it.part * it.part_tokens > max_pos || max_pos + 1 > p.max_parts * it.part_tokens) continue;
-    tile_item<KV, QT, D, false>(p, it, group, sm_o, sm_m, sm_l);
+    tile_item<KV, QT, D, false>(p, it, group, sm_o, sm_m, sm_l, st0, st1, st2, st3);
   }
 }
 
@@ -651,16 +811,21 @@ __global__ __launch_bounds__(kTileWaves * 64) void decode_mfma_kernel(StepParams
 template <int KV, int QT, int D>
 __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void step_mfma_kernel(StepParams p, int n_chunk_wgs,
                                                                    int stride, int dec_x, int dec_y) {
-  __shared__ float sm_o[2 * 16 * D];
+  // four stage arrays (a decode item's merge buffer lives in the first)
+  __shared__ uint4 st0[StageLay<KV, D>::STAGE0];
+  __shared__ uint4 st1[StageLay<KV, D>::CHUNKS];
+  __shared__ uint4 st2[StageLay<KV, D>::CHUNKS];
+  __shared__ uint4 st3[StageLay<KV, D>::CHUNKS];
   __shared__ float sm_m[2 * 16];
   __shared__ float sm_l[2 * 16];
+  float* sm_o = reinterpret_cast<float*>(st0);
   const int b = blockIdx.x;
   const int k = b / stride;
   const int r = b - k * stride;
   int id;
   if (k < n_chunk_wgs) {
     if (r == 0) {
-      chunk_wgs<KV, QT, D>(p, k, n_chunk_wgs, sm_o, sm_m, sm_l);
+      chunk_wgs<KV, QT, D>(p, k, n_chunk_wgs, sm_o, sm_m, sm_l, st0, st1, st2, st3);
       return;
     }
     id = k * (stride - 1) + (r - 1);
