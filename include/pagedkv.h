@@ -71,7 +71,9 @@ typedef enum pkv_status {
  * Layout of each pool: [num_blocks][num_kv_heads][block_size][head_dim], elements of
  * kv_dtype, row-major, so one (block, kv head) is one contiguous run of
  * block_size * head_dim elements.
- * Supported: block_size == 16, head_dim in {64, 128}, num_kv_heads >= 1. */
+ * Supported: block_size == 16, head_dim in {64, 128}, num_kv_heads >= 1;
+ * num_blocks * block_size and num_blocks * num_kv_heads must each fit an int32
+ * (PKV_ERR_SHAPE otherwise). */
 typedef struct pkv_pool {
   int32_t num_blocks;
   int32_t block_size;

@@ -37,6 +37,7 @@ int check_pool(const pkv_pool* pool) {
   if (pool->num_blocks < 1 || pool->num_kv_heads < 1 || pool->block_size < 1 || pool->head_dim < 1)
     return PKV_ERR_SHAPE;
   if ((int64_t)pool->num_blocks * pool->block_size > INT32_MAX) return PKV_ERR_SHAPE;
+  if ((int64_t)pool->num_blocks * pool->num_kv_heads > INT32_MAX) return PKV_ERR_SHAPE;
   if (pool->block_size != 16) return PKV_ERR_UNSUPPORTED;
   if (pool->head_dim != 64 && pool->head_dim != 128) return PKV_ERR_UNSUPPORTED;
   return PKV_OK;

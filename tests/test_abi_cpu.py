@@ -76,6 +76,8 @@ def test_step_validation():
     assert _step(p, max_query_len=3, total_q_tokens=5) == pk.PKV_ERR_SHAPE
     assert _step(p, q=FAKE + 2) == pk.PKV_ERR_SHAPE                   # misaligned
     assert _step(_pool(block_size=8)) == pk.PKV_ERR_UNSUPPORTED
+    # (block, kv head) slice indices must fit an int32
+    assert _step(_pool(num_blocks=2**26, num_kv_heads=64), num_q_heads=64) == pk.PKV_ERR_SHAPE
     assert _step(_pool(head_dim=96)) == pk.PKV_ERR_UNSUPPORTED
     assert _step(_pool(kv_dtype=7)) == pk.PKV_ERR_DTYPE
     assert _step(_pool(kv_dtype="fp8_e4m3")) == pk.PKV_ERR_NULL       # scales missing
