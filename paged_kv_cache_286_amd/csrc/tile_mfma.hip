@@ -796,7 +796,7 @@ __device__ __forceinline__ void chunk_wgs(const StepParams& p, int wg, int nwg, 
 
 // Decode rows only: grid (kv head x column tiles, sequence, partition).
 template <int KV, int QT, int D>
-__global__ __launch_bounds__(kTileWaves * 64) void decode_mfma_kernel(StepParams p) {
+__global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(StepParams p) {
   __shared__ float sm_o[2 * 16 * D];
   __shared__ float sm_m[2 * 16];
   __shared__ float sm_l[2 * 16];
