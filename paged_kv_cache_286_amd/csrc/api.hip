@@ -168,8 +168,12 @@ Layout layout_for(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads, i
                   int32_t max_ctx, int32_t max_q) {
   Layout lay;
   const int32_t group = num_q_heads / pool->num_kv_heads;
-  lay.decode_on_mfma = max_q > 1 || decode_on_mfma_for(pool, group);
+  // Steps with prefill chunks run every row in the step kernel; there too the
+  // single-row sequences of VALU-decode shapes run as VALU decode workgroups,
+  // and every sequence with more rows becomes chunk entries (small_q = 1).
   lay.heads_per_wg = heads_per_wg_for(group);
+  lay.decode_on_mfma = decode_on_mfma_for(pool, group) ||
+                       (max_q > 1 && (pool->kv_dtype == PKV_FP8_E4M3 || lay.heads_per_wg > 2));
   const int32_t wg_per_row =
       lay.decode_on_mfma ? pool->num_kv_heads * ((group + 15) / 16) : num_q_heads / lay.heads_per_wg;
   // (the tiles per kv head of small-query sequences only add columns, not blocks)
@@ -177,7 +181,7 @@ Layout layout_for(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads, i
   lay.max_parts = (max_ctx + lay.part_tokens - 1) / lay.part_tokens;
   size_t off = 0;
   if (max_q > 1) {
-    lay.small_q = small_q_for(group);
+    lay.small_q = lay.decode_on_mfma ? small_q_for(group) : 1;
     lay.chunk_cols = pkv::chunk_entry_cols(pool->kv_dtype);
     lay.chunk_part_tokens =
         chunk_part_tokens_for(group, pool->num_kv_heads, max_ctx, max_q, lay.chunk_cols, num_seqs);

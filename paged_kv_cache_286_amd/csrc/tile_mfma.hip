@@ -30,6 +30,7 @@
 // tile), so the products keep about 16 significant bits instead of 8; with fp8
 // KV the values themselves carry 4 significant bits and the high part alone is
 // well inside the error of the data.
+#include "decode_valu.h"
 #include "pkv_launch.h"
 
 namespace pkv {
@@ -103,6 +104,14 @@ struct TileLay {
   static constexpr int KSTEPS = D / 32;         // 16x16x32 MFMA steps of the score product
   static constexpr int KB = D / 4 * ELT;        // K bytes per lane per block (D/4 dims)
   static constexpr int KLD = KB / 16;           // 16-byte loads of K per lane
+  // K load c of lane group gq covers bytes c*64 + gq*16 of its token row, so
+  // one load instruction reads 64 contiguous bytes of each of the 16 rows (a
+  // whole 64-byte segment, not four 16-byte pieces of four); score step st
+  // contracts over the 8 dims starting at k_dim(st, gq), which the query
+  // operand of that step holds too
+  static __host__ __device__ constexpr int k_dim(int st, int gq) {
+    return ELT == 2 ? st * 32 + gq * 8 : (st / 2) * 64 + gq * 16 + (st % 2) * 8;
+  }
   static constexpr int VB = D / 16 * ELT;       // V bytes per lane per token (D/16 dims)
   static constexpr int DT = D / 16;             // output dim tiles
   // blocks kept in the register ring (pairs of blocks are consumed together):
@@ -234,15 +243,16 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   const int blk_begin = tok0 >> 4;
   const int blk_end = (tok1 + 15) >> 4;
 
-  // Q^T operand: D/4 consecutive dims of this column's query (zero for unused columns)
+  // Q^T operand of score step st: the 8 dims of this column's query that the
+  // K operand of the same step holds (zero for unused columns)
   uint4 qb[TPW][L::KSTEPS];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    const uint4* qrow = reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(p.q) + ((size_t)row[t] * p.num_q_heads + head[t]) * D +
-        gq * (D / 4));
+    const uint16_t* qrow =
+        reinterpret_cast<const uint16_t*>(p.q) + ((size_t)row[t] * p.num_q_heads + head[t]) * D;
 #pragma unroll
-    for (int c = 0; c < L::KSTEPS; ++c) qb[t][c] = col_ok[t] ? qrow[c] : make_uint4(0, 0, 0, 0);
+    for (int st = 0; st < L::KSTEPS; ++st)
+      qb[t][st] = col_ok[t] ? *reinterpret_cast<const uint4*>(qrow + L::k_dim(st, gq)) : make_uint4(0, 0, 0, 0);
   }
 
   // this wave's blocks: blk_begin + first + stride * i, i < cnt
@@ -334,7 +344,7 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     const __amdgpu_buffer_rsrc_t kres = block_rsrc(p.k_pool + boff, bytes);
     const __amdgpu_buffer_rsrc_t vres = block_rsrc(p.v_pool + boff, bytes);
 #pragma unroll
-    for (int c = 0; c < L::KLD; ++c) r.k[c] = load_block16<false>(kres, n * L::ROWB + gq * L::KB + c * 16);
+    for (int c = 0; c < L::KLD; ++c) r.k[c] = load_block16<false>(kres, n * L::ROWB + c * 64 + gq * 16);
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) r.v[i4] = VVec<L::VB>::load(vres, (gq * 4 + i4) * L::ROWB + n * L::VB);
     if constexpr (KV == kFP8) {
@@ -604,7 +614,7 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
       const uint4* kb = stage + j * SL::CHB;
       const uint4* vb = stage + (2 + j) * SL::CHB;
 #pragma unroll
-      for (int c = 0; c < L::KLD; ++c) r.k[c] = kb[SL::k_chunk(n, gq * L::KLD + c)];
+      for (int c = 0; c < L::KLD; ++c) r.k[c] = kb[SL::k_chunk(n, c * 4 + gq)];
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) r.v[i4] = VVec<L::VB>::lds(vb, (gq * 4 + i4) * L::ROWB + n * L::VB);
       r.base = (blk_begin + 2 * q + j) * 16;
@@ -807,8 +817,11 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
 // decode work items, interleaved in dispatch order (one chunk workgroup every
 // `stride` ids) so that the chunks' MFMA work overlaps the decode rows' HBM
 // traffic across the whole launch.  Decode ids decode as x fastest, then
-// sequence, then partition.
-template <int KV, int QT, int D>
+// sequence, then partition.  VGB = 0: decode items are MFMA tiles (x = kv
+// head x column tile); VGB = 1 or 2: single-row sequences run as the VALU
+// decode kernel's workgroups of VGB query heads (x = head group), which hold
+// their HBM rate at this kernel's two waves per SIMD.
+template <int KV, int QT, int D, int VGB>
 __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void step_mfma_kernel(StepParams p, int n_chunk_wgs,
                                                                    int stride, int dec_x, int dec_y) {
   // four stage arrays (a decode item's merge buffer lives in the first)
@@ -835,41 +848,55 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int x = id % dec_x;
   const int y = (id / dec_x) % dec_y;
   const int z = id / (dec_x * dec_y);
-  decode_wg<KV, QT, D>(p, x, y, z, sm_o, sm_m, sm_l);
+  if constexpr (VGB > 0) decode_valu_wg<KV, QT, D, VGB>(p, x, y, z);
+  else decode_wg<KV, QT, D>(p, x, y, z, sm_o, sm_m, sm_l);
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// vgb: 0, or the VALU decode workgroup's query heads (16-bit KV only)
 template <int KV, int QT, int D>
-static void launch_tile_kernel(bool step, const StepParams& p, dim3 grid, int n_chunk, int dx,
-                               int dy, hipStream_t stream) {
+static void launch_tile_kernel(bool step, int vgb, const StepParams& p, dim3 grid, int n_chunk,
+                               int dx, int dy, hipStream_t stream) {
   const dim3 block(kTileWaves * 64);
   if (step) {
     const int stride = n_chunk > 0 ? (int)(grid.x / (uint32_t)n_chunk) : 1;
-    hipLaunchKernelGGL((step_mfma_kernel<KV, QT, D>), grid, block, 0, stream, p, n_chunk, stride,
+    if constexpr (KV != kFP8) {
+      if (vgb == 1) {
+        hipLaunchKernelGGL((step_mfma_kernel<KV, QT, D, 1>), grid, block, 0, stream, p, n_chunk,
+                           stride, dx, dy);
+        return;
+      }
+      if (vgb == 2) {
+        hipLaunchKernelGGL((step_mfma_kernel<KV, QT, D, 2>), grid, block, 0, stream, p, n_chunk,
+                           stride, dx, dy);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((step_mfma_kernel<KV, QT, D, 0>), grid, block, 0, stream, p, n_chunk, stride,
                        dx, dy);
   } else
     hipLaunchKernelGGL((decode_mfma_kernel<KV, QT, D>), grid, block, 0, stream, p);
 }
 
 template <int KV, int QT>
-static hipError_t launch_tile(bool step, const StepParams& p, int head_dim, dim3 grid, int n_chunk,
-                              int dx, int dy, hipStream_t stream) {
+static hipError_t launch_tile(bool step, int vgb, const StepParams& p, int head_dim, dim3 grid,
+                              int n_chunk, int dx, int dy, hipStream_t stream) {
   (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
-  if (head_dim == 128) launch_tile_kernel<KV, QT, 128>(step, p, grid, n_chunk, dx, dy, stream);
-  else launch_tile_kernel<KV, QT, 64>(step, p, grid, n_chunk, dx, dy, stream);
+  if (head_dim == 128) launch_tile_kernel<KV, QT, 128>(step, vgb, p, grid, n_chunk, dx, dy, stream);
+  else launch_tile_kernel<KV, QT, 64>(step, vgb, p, grid, n_chunk, dx, dy, stream);
   return hipGetLastError();
 }
 
-static hipError_t launch_tile_typed(bool step, const StepParams& p, const StepPlan& plan, dim3 grid,
-                                    int n_chunk, int dx, int dy, hipStream_t stream) {
+static hipError_t launch_tile_typed(bool step, int vgb, const StepParams& p, const StepPlan& plan,
+                                    dim3 grid, int n_chunk, int dx, int dy, hipStream_t stream) {
   if (plan.q_dtype == kBF16) {
-    if (plan.kv_dtype == kBF16) return launch_tile<kBF16, kBF16>(step, p, plan.head_dim, grid, n_chunk, dx, dy, stream);
-    if (plan.kv_dtype == kFP8) return launch_tile<kFP8, kBF16>(step, p, plan.head_dim, grid, n_chunk, dx, dy, stream);
+    if (plan.kv_dtype == kBF16) return launch_tile<kBF16, kBF16>(step, vgb, p, plan.head_dim, grid, n_chunk, dx, dy, stream);
+    if (plan.kv_dtype == kFP8) return launch_tile<kFP8, kBF16>(step, vgb, p, plan.head_dim, grid, n_chunk, dx, dy, stream);
   } else if (plan.q_dtype == kF16) {
-    if (plan.kv_dtype == kF16) return launch_tile<kF16, kF16>(step, p, plan.head_dim, grid, n_chunk, dx, dy, stream);
-    if (plan.kv_dtype == kFP8) return launch_tile<kFP8, kF16>(step, p, plan.head_dim, grid, n_chunk, dx, dy, stream);
+    if (plan.kv_dtype == kF16) return launch_tile<kF16, kF16>(step, vgb, p, plan.head_dim, grid, n_chunk, dx, dy, stream);
+    if (plan.kv_dtype == kFP8) return launch_tile<kFP8, kF16>(step, vgb, p, plan.head_dim, grid, n_chunk, dx, dy, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -877,17 +904,21 @@ static hipError_t launch_tile_typed(bool step, const StepParams& p, const StepPl
 hipError_t launch_decode_mfma(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
   const int tiles = (p.small_q * plan.group + 15) / 16;
   const dim3 grid((uint32_t)(p.num_kv_heads * tiles), (uint32_t)p.num_seqs, (uint32_t)p.max_parts);
-  return launch_tile_typed(false, p, plan, grid, 0, 0, 0, stream);
+  return launch_tile_typed(false, 0, p, plan, grid, 0, 0, 0, stream);
 }
 
 hipError_t launch_step_mfma(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
+  // decode rows as VALU decode workgroups (plan.decode_on_mfma false: 16-bit KV,
+  // at most two query heads per kv head) or as MFMA tiles
+  const int vgb = plan.decode_on_mfma ? 0 : plan.heads_per_wg;
+  if (vgb != 0 && (plan.kv_dtype == kFP8 || vgb > 2)) return hipErrorInvalidValue;
   const int tiles = (p.small_q * plan.group + 15) / 16;
-  const int dx = p.num_kv_heads * tiles;
+  const int dx = vgb ? p.num_q_heads / vgb : p.num_kv_heads * tiles;
   const int dy = p.num_seqs;
   const long long dec = (long long)dx * dy * p.max_parts;
   const long long total = dec + plan.chunk_grid;
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-  return launch_tile_typed(true, p, plan, dim3((uint32_t)total), plan.chunk_grid, dx, dy, stream);
+  return launch_tile_typed(true, vgb, p, plan, dim3((uint32_t)total), plan.chunk_grid, dx, dy, stream);
 }
 
 }  // namespace pkv
