@@ -132,13 +132,15 @@ __device__ __forceinline__ uint32_t vword(const T& v, int w) {
 template <int VB> struct VVec;
 template <> struct VVec<16> {
   typedef uint4 T;
-  static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int off) { return load_block16<false>(r, off); }
+  template <bool NT = false>
+  static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int off) { return load_block16<NT>(r, off); }
   static __device__ __forceinline__ T lds(const uint4* base, int off) { return base[off / 16]; }
 };
 template <> struct VVec<8> {
   typedef uint2 T;
+  template <bool NT = false>
   static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int off) {
-    const u32x2_buf v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const u32x2_buf v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, NT ? 2 : 0);
     return make_uint2(v.x, v.y);
   }
   static __device__ __forceinline__ T lds(const uint4* base, int off) {
@@ -147,8 +149,9 @@ template <> struct VVec<8> {
 };
 template <> struct VVec<4> {
   typedef uint32_t T;
+  template <bool NT = false>
   static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, NT ? 2 : 0);
   }
   static __device__ __forceinline__ T lds(const uint4* base, int off) {
     return reinterpret_cast<const uint32_t*>(base)[off / 4];
@@ -327,7 +330,9 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   // wave's last block the index is clamped and the block counts no tokens (its
   // loads move no bytes), so the compiler can wait for exactly the block it
   // consumes instead of draining all outstanding loads at a control-flow join.
-  auto issue = [&](int i, BlockRegs<KV, D>& r) {
+  // NT: nontemporal loads (blocks no other sequence of the step reads)
+  auto issue = [&](auto nt_tag, int i, BlockRegs<KV, D>& r) {
+    constexpr bool NT = decltype(nt_tag)::value;
     const int ic = min(i, cnt - 1);
     const int b = blk_begin + first + stride * ic;
     r.base = b * 16;
@@ -344,9 +349,9 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     const __amdgpu_buffer_rsrc_t kres = block_rsrc(p.k_pool + boff, bytes);
     const __amdgpu_buffer_rsrc_t vres = block_rsrc(p.v_pool + boff, bytes);
 #pragma unroll
-    for (int c = 0; c < L::KLD; ++c) r.k[c] = load_block16<false>(kres, n * L::ROWB + c * 64 + gq * 16);
+    for (int c = 0; c < L::KLD; ++c) r.k[c] = load_block16<NT>(kres, n * L::ROWB + c * 64 + gq * 16);
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) r.v[i4] = VVec<L::VB>::load(vres, (gq * 4 + i4) * L::ROWB + n * L::VB);
+    for (int i4 = 0; i4 < 4; ++i4) r.v[i4] = VVec<L::VB>::template load<NT>(vres, (gq * 4 + i4) * L::ROWB + n * L::VB);
     if constexpr (KV == kFP8) {
       r.ksc = lane_float(my_ks, ic);
       r.vsc = lane_float(my_vs, ic);
@@ -531,29 +536,44 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   constexpr int NB = L::NBUF;
   constexpr int NP = NB / 2;
   if constexpr (SPLIT) {
+  // Each block of a decode item is read by one wave only, so the blocks are
+  // streamed past the caches (nontemporal loads), except the leading blocks
+  // the caller marks as shared with other sequences of the step (a prefix
+  // that other waves read too stays cached).  Pairs [0, shared_pairs) load
+  // cached, the rest nontemporal (both ends cut to whole rounds of the ring).
   BlockRegs<KV, D> buf[NB];
   if (cnt > 0) {
     const int npairs = (cnt + 1) / 2;
     const int dense_pairs = dense_blocks / 2 / NP * NP;
+    const int hint = p.shared_blocks != nullptr ? uniform_load(p.shared_blocks + it.seq) : 0;
+    const int nsh = min(max(hint, blk_begin), blk_end);      // clamped before any arithmetic
+    const int cnt_sh = min(cnt, max(0, nsh - blk_begin - first + stride - 1) / stride);
+    const int shared_pairs = min((cnt_sh + 1) / 2 + NP - 1, dense_pairs) / NP * NP;
 #pragma unroll
     for (int k = 0; k < NP - 1; ++k) {
-      issue(2 * k, buf[2 * k]);
-      issue(2 * k + 1, buf[2 * k + 1]);
+      if (shared_pairs > 0) {
+        issue(std::false_type{}, 2 * k, buf[2 * k]);
+        issue(std::false_type{}, 2 * k + 1, buf[2 * k + 1]);
+      } else {
+        issue(std::true_type{}, 2 * k, buf[2 * k]);
+        issue(std::true_type{}, 2 * k + 1, buf[2 * k + 1]);
+      }
     }
-    auto run = [&](auto dense_tag, int q_begin, int q_end) {
+    auto run = [&](auto dense_tag, auto nt_tag, int q_begin, int q_end) {
       for (int q2 = q_begin; q2 < q_end; q2 += NP) {
 #pragma unroll
         for (int u = 0; u < NP; ++u) {
           const int nxt = q2 + u + NP - 1;
           const int slot = (u + NP - 1) % NP;
-          issue(2 * nxt, buf[2 * slot]);
-          issue(2 * nxt + 1, buf[2 * slot + 1]);
+          issue(nt_tag, 2 * nxt, buf[2 * slot]);
+          issue(nt_tag, 2 * nxt + 1, buf[2 * slot + 1]);
           attend_pair(dense_tag, buf[2 * u], buf[2 * u + 1]);
         }
       }
     };
-    run(std::true_type{}, 0, dense_pairs);
-    run(std::false_type{}, dense_pairs, npairs);
+    run(std::true_type{}, std::false_type{}, 0, shared_pairs);
+    run(std::true_type{}, std::true_type{}, shared_pairs, dense_pairs);
+    run(std::false_type{}, std::true_type{}, dense_pairs, npairs);
   }
   } else {
     // Prefill item: the four waves read the same blocks, so the workgroup
