@@ -93,6 +93,13 @@ SMALL = {
     "chunk_gqa4_fp8_d128": dict(Hq=8, Hkv=2, D=128, kv=W.FP8, qd=W.BF16, lens=[90, 1000, 20],
                                 qlens=[90, 64, 1]),
     "chunk_f16_d64": dict(Hq=4, Hkv=2, D=64, kv=W.F16, qd=W.F16, lens=[17, 600], qlens=[16, 200]),
+    # single-row sequences beside chunks: decode rows as two-head VALU workgroups in the step kernel
+    "chunk_gqa2_bf16_d128_decodes": dict(Hq=8, Hkv=4, D=128, kv=W.BF16, qd=W.BF16,
+                                         lens=[50, 700, 1300, 90, 2500, 16],
+                                         qlens=[1, 1, 300, 1, 1, 16]),
+    # fp8 prefill items at head_dim 64 (one 16-byte copy per thread and stage)
+    "chunk_fp8_mha_f16q_d64": dict(Hq=4, Hkv=4, D=64, kv=W.FP8, qd=W.F16, lens=[200, 900, 35, 64],
+                                   qlens=[200, 1, 35, 3]),
     # several query rows per sequence, as a speculative-decoding step verifies
     "specdec_mha_bf16_d128": dict(Hq=8, Hkv=8, D=128, kv=W.BF16, qd=W.BF16,
                                   lens=_rng.integers(50, 3000, 10).tolist(),
