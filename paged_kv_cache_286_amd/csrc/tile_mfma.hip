@@ -179,6 +179,12 @@ struct StageLay {
   static __device__ __forceinline__ int k_chunk(int row, int c) {
     return row * CPR + (c ^ ((row * CPR / 16) & (CPR - 1)));
   }
+  // 16-bit V rows are read by transposing LDS reads, 32 bytes of each of 16
+  // rows per 16-dim slice: chunk c of row r sits at c ^ (2r mod CPR), which
+  // puts eight rows' chunk pairs in distinct bank groups
+  static __device__ __forceinline__ int v_chunk(int row, int c) {
+    return row * CPR + (c ^ ((2 * row) & (CPR - 1)));
+  }
   // s_waitcnt immediate: at most n vector memory operations outstanding, no
   // LDS/scalar operation outstanding (gfx9 fields: vmcnt [3:0] and [15:14],
   // expcnt [6:4] left at its maximum, lgkmcnt [11:8] = 0)
@@ -407,11 +413,59 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     }
   };
 
+  // V^T operand of each 16-dim slice j from the V registers of a pair: the
+  // 16-bit pairs (token t, token t+1) of dim 8n+j (n = lane's row of the
+  // tile) for tokens 4gq..4gq+3 of r0 and of r1
+  auto v_operand = [&](const BlockRegs<KV, D>& r0, const BlockRegs<KV, D>& r1, uint4 (&va)[L::DT]) {
+    if constexpr (KV == kFP8) {
+      // one byte permute gathers tokens t, t+1 at dims j, j+1; its two
+      // conversions are then the operand words of slices j and j+1
+#pragma unroll
+      for (int j = 0; j < L::DT; j += 2) {
+        const uint32_t b = j % 4;
+        const uint32_t sel = b | ((4 + b) << 8) | ((b + 1) << 16) | ((5 + b) << 24);
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const BlockRegs<KV, D>& r = q < 2 ? r0 : r1;
+          const int tk = (q & 1) * 2;
+          const uint32_t x = vword<L::VB>(r.v[tk], j / 4);
+          const uint32_t y = vword<L::VB>(r.v[tk + 1], j / 4);
+          const uint32_t w = __builtin_amdgcn_perm(y, x, sel);
+          lo[q] = fp8x2_to_16<QT, false>(w);
+          hi[q] = fp8x2_to_16<QT, true>(w);
+        }
+        va[j] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        va[j + 1] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      }
+    } else {
+      uint32_t v0[4][L::DT / 2], v1[4][L::DT / 2];
+      vvals(r0, v0);
+      vvals(r1, v1);
+#pragma unroll
+      for (int j = 0; j < L::DT; ++j) {
+        if (j & 1) {
+          va[j].x = pick16<true>(v0[0][j / 2], v0[1][j / 2]);
+          va[j].y = pick16<true>(v0[2][j / 2], v0[3][j / 2]);
+          va[j].z = pick16<true>(v1[0][j / 2], v1[1][j / 2]);
+          va[j].w = pick16<true>(v1[2][j / 2], v1[3][j / 2]);
+        } else {
+          va[j].x = pick16<false>(v0[0][j / 2], v0[1][j / 2]);
+          va[j].y = pick16<false>(v0[2][j / 2], v0[3][j / 2]);
+          va[j].z = pick16<false>(v1[0][j / 2], v1[1][j / 2]);
+          va[j].w = pick16<false>(v1[2][j / 2], v1[3][j / 2]);
+        }
+      }
+    }
+  };
+
   // online softmax and PV over a pair of blocks (32 tokens).  DENSE: both
   // blocks are whole and every column of the wave sees all 32 tokens, so no
   // score is masked and the scale folds into the exponent's argument (for a
   // positive factor the maximum of the products is the product of the maximum).
-  auto attend_pair = [&](auto dense_tag, const BlockRegs<KV, D>& r0, const BlockRegs<KV, D>& r1) {
+  // build_va(va) fills the V^T operand of the pair.
+  auto attend_pair = [&](auto dense_tag, const BlockRegs<KV, D>& r0, const BlockRegs<KV, D>& r1,
+                         auto&& build_va) {
     constexpr bool DENSE = decltype(dense_tag)::value;
     f32x4 s0[TPW], s1[TPW];
     scores(r0, s0);
@@ -473,49 +527,8 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
       split_weights<QT>(pw, pb_hi[t], pb_lo[t]);
     }
 
-    // V^T operand of each 16-dim slice j: the 16-bit pairs (token t, token t+1)
-    // of dim j for tokens 0..3 of r0 and of r1
     uint4 va[L::DT];
-    if constexpr (KV == kFP8) {
-      // one byte permute gathers tokens t, t+1 at dims j, j+1; its two
-      // conversions are then the operand words of slices j and j+1
-#pragma unroll
-      for (int j = 0; j < L::DT; j += 2) {
-        const uint32_t b = j % 4;
-        const uint32_t sel = b | ((4 + b) << 8) | ((b + 1) << 16) | ((5 + b) << 24);
-        uint32_t lo[4], hi[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const BlockRegs<KV, D>& r = q < 2 ? r0 : r1;
-          const int tk = (q & 1) * 2;
-          const uint32_t x = vword<L::VB>(r.v[tk], j / 4);
-          const uint32_t y = vword<L::VB>(r.v[tk + 1], j / 4);
-          const uint32_t w = __builtin_amdgcn_perm(y, x, sel);
-          lo[q] = fp8x2_to_16<QT, false>(w);
-          hi[q] = fp8x2_to_16<QT, true>(w);
-        }
-        va[j] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        va[j + 1] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      }
-    } else {
-      uint32_t v0[4][L::DT / 2], v1[4][L::DT / 2];
-      vvals(r0, v0);
-      vvals(r1, v1);
-#pragma unroll
-      for (int j = 0; j < L::DT; ++j) {
-        if (j & 1) {
-          va[j].x = pick16<true>(v0[0][j / 2], v0[1][j / 2]);
-          va[j].y = pick16<true>(v0[2][j / 2], v0[3][j / 2]);
-          va[j].z = pick16<true>(v1[0][j / 2], v1[1][j / 2]);
-          va[j].w = pick16<true>(v1[2][j / 2], v1[3][j / 2]);
-        } else {
-          va[j].x = pick16<false>(v0[0][j / 2], v0[1][j / 2]);
-          va[j].y = pick16<false>(v0[2][j / 2], v0[3][j / 2]);
-          va[j].z = pick16<false>(v1[0][j / 2], v1[1][j / 2]);
-          va[j].w = pick16<false>(v1[2][j / 2], v1[3][j / 2]);
-        }
-      }
-    }
+    build_va(va);
 #pragma unroll
     for (int j = 0; j < L::DT; ++j) {
 #pragma unroll
@@ -567,7 +580,8 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
           const int slot = (u + NP - 1) % NP;
           issue(nt_tag, 2 * nxt, buf[2 * slot]);
           issue(nt_tag, 2 * nxt + 1, buf[2 * slot + 1]);
-          attend_pair(dense_tag, buf[2 * u], buf[2 * u + 1]);
+          attend_pair(dense_tag, buf[2 * u], buf[2 * u + 1],
+                      [&](uint4 (&va)[L::DT]) { v_operand(buf[2 * u], buf[2 * u + 1], va); });
         }
       }
     };
@@ -590,6 +604,7 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     // own last column).
     using SL = StageLay<KV, D>;
     constexpr int S = kStages;
+    constexpr bool VTR = KV != kFP8;    // 16-bit V: transposing LDS reads
     const int np_item = (cnt_item + 1) / 2;
     const bool has_cols = wcol0 < it.ncols;
     const int np_w = has_cols ? (cnt + 1) / 2 : 0;
@@ -619,7 +634,7 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
         const int bi = g * 64 / SL::CHB;
         const int d = (g * 64) % SL::CHB + lane;
         const int row = d / SL::CPR, c = d % SL::CPR;
-        const int goff = (bi < 2 ? SL::k_chunk(row, c) : d) * 16;
+        const int goff = (bi < 2 ? SL::k_chunk(row, c) : (VTR ? SL::v_chunk(row, c) : d)) * 16;
         const int e = (bi & 1) ? ent[1] : ent[0];
         const size_t boff = (size_t)(uint32_t)max(e, 0) * L::BLKB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -635,8 +650,10 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
       const uint4* vb = stage + (2 + j) * SL::CHB;
 #pragma unroll
       for (int c = 0; c < L::KLD; ++c) r.k[c] = kb[SL::k_chunk(n, c * 4 + gq)];
+      if constexpr (!VTR) {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) r.v[i4] = VVec<L::VB>::lds(vb, (gq * 4 + i4) * L::ROWB + n * L::VB);
+        for (int i4 = 0; i4 < 4; ++i4) r.v[i4] = VVec<L::VB>::lds(vb, (gq * 4 + i4) * L::ROWB + n * L::VB);
+      }
       r.base = (blk_begin + 2 * q + j) * 16;
       r.limit = tokens(2 * q + j);
       r.ksc = 1.f;
@@ -644,6 +661,32 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
       if constexpr (KV == kFP8) {
         r.ksc = __int_as_float(entry(my_ks, q, j, u));
         r.vsc = __int_as_float(entry(my_vs, q, j, u));
+      }
+    };
+    // 16-bit V operand straight from the stage with transposing LDS reads:
+    // within each 16-lane group, lane d of the result gets element d%4 of the
+    // 8 bytes read by lanes 4k + d/4 (k = 0..3), so when lane (s, g) reads
+    // dims 16j + 4(s%4) .. +3 of token row 4g + s/4, lane (d, g) receives
+    // dim 16j + d of tokens 4g .. 4g+3: the A operand rows are the slice's 16
+    // dims (output row m of slice j is dim 16j + m) and the tokens line up
+    // with the weights' k slots, first block then second.
+    auto v_operand_tr = [&](const uint4* stage, uint4 (&va)[L::DT]) {
+      const int row = 4 * gq + (n >> 2);
+#pragma unroll
+      for (int j = 0; j < L::DT; ++j) {
+        uint32_t w[4];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const uint4* vb = stage + (2 + b) * SL::CHB;
+          const int c = 2 * j + ((n & 3) >> 1);
+          const int byte = SL::v_chunk(row, c) * 16 + 8 * (n & 1);
+          typedef short v4s __attribute__((ext_vector_type(4)));
+          const v4s t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)((__attribute__((address_space(3))) char*)vb + byte));
+          w[2 * b] = (uint32_t)(uint16_t)t[0] | ((uint32_t)(uint16_t)t[1] << 16);
+          w[2 * b + 1] = (uint32_t)(uint16_t)t[2] | ((uint32_t)(uint16_t)t[3] << 16);
+        }
+        va[j] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     };
     uint4* const stage[4] = {st0, st1, st2, st3};
@@ -673,7 +716,10 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
               BlockRegs<KV, D> r0, r1;
               from_stage(stage[u], q, 0, u, r0);
               from_stage(stage[u], q, 1, u, r1);
-              attend_pair(dense_tag, r0, r1);
+              attend_pair(dense_tag, r0, r1, [&](uint4 (&va)[L::DT]) {
+                if constexpr (VTR) v_operand_tr(stage[u], va);
+                else v_operand(r0, r1, va);
+              });
             }
           }
         }
@@ -726,6 +772,12 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     take(0);
   }
 
+  // head dim of output row 4gq+i4 of slice j: 16j + row where V came through
+  // transposing reads (16-bit prefill items), else 8*row + j
+  auto out_dim = [&](int j, int i4) {
+    if constexpr (!SPLIT && KV != kFP8) return 16 * j + gq * 4 + i4;
+    else return (gq * 4 + i4) * L::DT + j;
+  };
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     // this wave holds its columns' result over the partition: write it out
@@ -738,14 +790,14 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
 #pragma unroll
       for (int j = 0; j < L::DT; ++j)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) orow[(gq * 4 + i4) * L::DT + j] = to_out_bits<QT>(o[t][j][i4] * inv);
+        for (int i4 = 0; i4 < 4; ++i4) orow[out_dim(j, i4)] = to_out_bits<QT>(o[t][j][i4] * inv);
     } else {
       const size_t idx = rh * it.max_parts + it.part;
       float* po = p.part_o + idx * D;
 #pragma unroll
       for (int j = 0; j < L::DT; ++j)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) po[(gq * 4 + i4) * L::DT + j] = o[t][j][i4];
+        for (int i4 = 0; i4 < 4; ++i4) po[out_dim(j, i4)] = o[t][j][i4];
       if (gq == 0) {
         p.part_ml[idx * 2] = m[t];
         p.part_ml[idx * 2 + 1] = lsum[t];
