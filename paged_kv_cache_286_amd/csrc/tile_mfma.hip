@@ -19,11 +19,15 @@
 // column l%16, for each block of the pair) is, with the pair's contraction
 // index k = 8*(l/16) + i meaning token 4*(l/16) + i%4 of block i/4, exactly the
 // B layout the second product needs, so the softmax weights never leave their
-// lanes.  Head dims are permuted freely inside each contraction so that every
-// lane's operands are contiguous in memory: for S^T lane l reads D/4
-// consecutive dims of token l%16; for O^T the output dim of (tile j, row m) is
-// m * D/16 + j, so lane l reads D/16 consecutive dims of each of its tokens.  fp8 K/V are converted to the
-// query type in registers (exact: every e4m3 value is a bf16 and an f16), and
+// lanes.  Head dims are permuted freely inside each contraction so that the
+// operands come from contiguous memory: for S^T, K load c of lane l reads 16
+// bytes at 64c + 16(l/16) of token row l%16 (one load instruction covers a
+// 64-byte segment of 16 rows) and the query operand holds the same dims; for
+// O^T from registers the output dim of (tile j, row m) is m * D/16 + j, so
+// lane l reads D/16 consecutive dims of each of its tokens, and for O^T from
+// LDS through transposing reads (16-bit prefill items) it is 16j + m.  fp8 K/V
+// are converted to the query type in registers (exact: every e4m3 value is a
+// bf16 and an f16), and
 // the per-(block, head) scales are folded into the score (K) and the weight (V).
 // Only the softmax weights are rounded on the way into the MFMA.  With 16-bit
 // KV they enter as a 16-bit high part plus a 16-bit residual (two PV MFMAs per
@@ -213,13 +217,11 @@ struct TileItem {
 // one 16-column tile and the kTileWaves waves share the partition's blocks
 // (wave w takes blocks w, w + kTileWaves, ...), merged through LDS at the end.
 // !SPLIT (prefill chunks): the item is kTileWaves x TPW tiles of 16 columns,
-// wave w owns tiles w*TPW .. w*TPW+TPW-1 and walks every block up to its last
-// column's causal limit; the four waves read the same blocks at the same time
-// (one fetch beyond L1 serves them all) and each writes its own columns.  With
-// two tiles per wave a block's loads, fp8 conversions and the permutes that
-// bring V into the MFMA operand layout serve twice the matrix work.  K/V use ordinary (cached)
-// loads here: nontemporal loads for the decode items gained at most 1% with
-// fp8 K/V and cost 20% in steps that mix decodes with prefill chunks.
+// wave w owns tiles w*TPW .. w*TPW+TPW-1 and attends every block up to its
+// last column's causal limit; the workgroup stages the blocks in LDS once for
+// all four waves (st0..st3) and each wave writes its own columns.  With two
+// tiles per wave a block's operand reads and fp8 conversions serve twice the
+// matrix work.
 template <int KV, int QT, int D, bool SPLIT>
 __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& it, int group,
                                           float* sm_o, float* sm_m, float* sm_l, uint4* st0 = nullptr,
@@ -539,16 +541,17 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     }
   };
 
-  // register ring: NB/2 - 1 pairs are loading while the current pair is scored;
-  // pairs past the end (at most NB/2 - 1 per wave) are scored fully masked.
   // The wave's blocks rise in position, so the dense pairs (both blocks wholly
-  // at or before min_pos) form a prefix; it runs in a loop of its own, cut to a
-  // multiple of the ring's pairs so both loops use the same register slots.
+  // at or before min_pos) form a prefix of its block list.
   const int vis_blocks = (min_pos + 1) >> 4;   // blocks 0 .. vis_blocks-1 end at or before min_pos
   const int dense_blocks = min(cnt, max(0, vis_blocks - blk_begin - first + stride - 1) / stride);
   constexpr int NB = L::NBUF;
   constexpr int NP = NB / 2;
   if constexpr (SPLIT) {
+  // Decode items: a register ring in which NB/2 - 1 pairs are loading while
+  // the current pair is scored; pairs past the end (at most NB/2 - 1 per wave)
+  // are scored fully masked.  The dense prefix runs in a loop of its own, cut
+  // to a multiple of the ring's pairs so the loops use the same register slots.
   // Each block of a decode item is read by one wave only, so the blocks are
   // streamed past the caches (nontemporal loads), except the leading blocks
   // the caller marks as shared with other sequences of the step (a prefix
