@@ -326,10 +326,20 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
 
   float m[TPW], lsum[TPW];
   f32x4 o[TPW][L::DT];
+  // 16-bit prefill items: the running column sums come from one more MFMA
+  // pair per tile with an all-ones A operand (D[m][n] = sum over k of the
+  // weights, the same hi + lo weights the PV product uses), which moves eight
+  // vector additions per tile and pair onto the matrix unit; each output row
+  // then holds the sum, so no cross-lane reduction is needed at the end
+  constexpr bool ONES_SUM = !SPLIT && KV != kFP8;
+  f32x4 osum[TPW];
+  const uint4 ones = QT == kBF16 ? make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u)
+                                 : make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     m[t] = kMaxSeed;
     lsum[t] = 0.f;
+    osum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < L::DT; ++j) o[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -513,13 +523,19 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
         for (int i = 0; i < 8; ++i) pw[i] = ok[i] ? __builtin_amdgcn_exp2f(sv[i] - mn) : 0.f;
       }
       const float alpha = __builtin_amdgcn_exp2f(m[t] - mn);
+      if constexpr (ONES_SUM) {
+        // the column sums come out of the MFMA (below)
+        (void)ps;
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ps += pw[i];
-      lsum[t] = lsum[t] * alpha + ps;
+        for (int i = 0; i < 8; ++i) ps += pw[i];
+        lsum[t] = lsum[t] * alpha + ps;
+      }
       m[t] = mn;
       if (__any(alpha != 1.f)) {     // the reference rarely moves after the first blocks
 #pragma unroll
         for (int j = 0; j < L::DT; ++j) o[t][j] *= alpha;
+        if constexpr (ONES_SUM) osum[t] *= alpha;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -536,6 +552,12 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         o[t][j] = mfma32<QT>(va[j], pb_hi[t], o[t][j]);
+        if constexpr (ONES_SUM) {
+          if (j == 0) {
+            osum[t] = mfma32<QT>(ones, pb_hi[t], osum[t]);
+            osum[t] = mfma32<QT>(ones, pb_lo[t], osum[t]);
+          }
+        }
         if constexpr (KV != kFP8) o[t][j] = mfma32<QT>(va[j], pb_lo[t], o[t][j]);
       }
     }
@@ -634,7 +656,10 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
 #pragma unroll
       for (int k = 0; k < SL::LOADS; ++k) {
         const int g = k * kTileWaves + wave;
-        const int bi = g * 64 / SL::CHB;
+        // g * 64 / CHB, written so that it is a constant when a block spans
+        // all four waves' chunk groups (wave < 4)
+        constexpr int CPB = SL::CHB / 64;
+        const int bi = CPB == kTileWaves ? k : g / CPB;
         const int d = (g * 64) % SL::CHB + lane;
         const int row = d / SL::CPR, c = d % SL::CPR;
         const int goff = (bi < 2 ? SL::k_chunk(row, c) : (VTR ? SL::v_chunk(row, c) : d)) * 16;
@@ -735,7 +760,10 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
 
   // the column's running sum is spread over the 4 lane groups
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) lsum[t] = sum_xor32(sum_xor16(lsum[t]));
+  for (int t = 0; t < TPW; ++t) {
+    if constexpr (ONES_SUM) lsum[t] = osum[t][0];   // every output row holds the column sum
+    else lsum[t] = sum_xor32(sum_xor16(lsum[t]));
+  }
 
   if constexpr (SPLIT) {
     // Merge the four waves' partials of the same 16 columns in two rounds
