@@ -92,7 +92,9 @@ int env_int(const char* name, int dflt) {
 
 // Tokens per split-context partition: about 512 KiB (fp8: 1 MiB) of K+V per
 // workgroup, halved while a step of few, long rows would leave the chip
-// under-filled.
+// under-filled -- but not below 64 KiB per workgroup: a partition that short
+// saves less time than the merge launch it brings costs (a tiny step of 4
+// rows of at most 80 tokens runs unsplit, in two launches instead of three).
 int32_t part_tokens_for(const pkv_pool* pool, int32_t rows, int32_t wg_per_row, int32_t max_ctx) {
   const int forced = env_int("PKV_PART_TOKENS", 0);
   if (forced >= 16 && forced <= 4096 && forced % 16 == 0) return forced;
@@ -100,7 +102,7 @@ int32_t part_tokens_for(const pkv_pool* pool, int32_t rows, int32_t wg_per_row, 
   // fp8 workgroups run the longer MFMA ring; they amortise their start-up over more bytes
   int32_t pt = (pool->kv_dtype == PKV_FP8_E4M3 ? 1024 : 512) * 1024 / bytes_per_token;
   pt = std::min(4096, std::max(16, pt));
-  while (pt > 64) {
+  while (pt > 64 && (int64_t)(pt / 2) * bytes_per_token >= 64 * 1024) {
     const int64_t wgs = (int64_t)rows * wg_per_row * ((max_ctx + pt - 1) / pt);
     if (wgs >= 4 * 256) break;
     pt /= 2;

@@ -82,11 +82,16 @@ def test_step_validation():
     assert _step(_pool(kv_dtype=7)) == pk.PKV_ERR_DTYPE
     assert _step(_pool(kv_dtype="fp8_e4m3")) == pk.PKV_ERR_NULL       # scales missing
     assert _step(None) == pk.PKV_ERR_NULL
-    # a split step needs a workspace
-    assert pk.paged_attn_workspace_bytes(p, 4, 4, 4, 100, 1) > 0
-    assert _step(p) == pk.PKV_ERR_WORKSPACE
-    need = pk.paged_attn_workspace_bytes(p, 4, 4, 4, 100, 1)
-    assert _step(p, workspace=FAKE, workspace_bytes=need - 1) == pk.PKV_ERR_WORKSPACE
+    # a step this small runs unsplit: no workspace
+    assert pk.paged_attn_workspace_bytes(p, 4, 4, 4, 100, 1) == 0
+    # a split step needs a workspace (4 rows of up to 1000 tokens at head_dim 128
+    # split into partitions: 16 workgroups per partition would not fill the chip)
+    p2 = _pool(num_blocks=512, head_dim=128)
+    need = pk.paged_attn_workspace_bytes(p2, 4, 4, 4, 1000, 1)
+    assert need > 0
+    assert _step(p2, max_blocks_per_seq=64, max_context_len=1000) == pk.PKV_ERR_WORKSPACE
+    assert _step(p2, max_blocks_per_seq=64, max_context_len=1000, workspace=FAKE,
+                 workspace_bytes=need - 1) == pk.PKV_ERR_WORKSPACE
 
 
 def test_workspace_sizes():
