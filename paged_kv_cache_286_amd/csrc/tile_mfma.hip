@@ -917,8 +917,12 @@ __device__ __forceinline__ void chunk_wgs(const StepParams& p, int wg, int nwg, 
   const int per_entry = p.num_kv_heads * p.chunk_max_parts;
   const long long items = (long long)n_entries * per_entry;
   for (long long item = wg; item < items; item += nwg) {
-    const int e = (int)(item / per_entry);
-    const int rem = (int)(item - (long long)e * per_entry);
+    // entries are listed by rising column within each sequence, and a later
+    // column attends more keys: taking them last to first hands out the
+    // longest items first, so the launch does not end on a few long ones
+    const int eo = (int)(item / per_entry);
+    const int rem = (int)(item - (long long)eo * per_entry);
+    const int e = n_entries - 1 - eo;
     TileItem it;
     it.seq = uniform_load(p.chunk_entries + 2 * e);
     it.col0 = uniform_load(p.chunk_entries + 2 * e + 1);
