@@ -290,6 +290,7 @@ class DeviceEngine:
                  head_dim: int, dtype: str = "bf16", seed: int = 0, device: str = "cuda:0",
                  keep_host_mirror: bool = False, kv_from_tokens: bool = False):
         import torch
+        from .device import alloc_kv_pools
         self.torch = torch
         self.b = batcher
         self.Hq, self.Hkv, self.D = num_q_heads, num_kv_heads, head_dim
@@ -298,8 +299,7 @@ class DeviceEngine:
         nb, bs = batcher.bm.num_blocks, batcher.block_size
         tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
         self.tdt = tdt
-        self.k_pool = torch.zeros((nb, num_kv_heads, bs, head_dim), dtype=tdt, device=self.dev)
-        self.v_pool = torch.zeros_like(self.k_pool)
+        self.k_pool, self.v_pool = alloc_kv_pools((nb, num_kv_heads, bs, head_dim), tdt, self.dev)
         self.pool = pk.make_pool(nb, bs, num_kv_heads, head_dim, dtype)
         self.code = pk.DTYPE_CODES[dtype]
         self.gen = torch.Generator(device=self.dev)
