@@ -124,6 +124,41 @@ def test_small_steps_all_outputs(name):
     _check(wl, ds)
 
 
+def _random_case(seed):
+    """A seeded random small step: head layout, dtypes, lengths and query rows
+    (decodes, speculative-verify rows, prefill chunks, whole prompts) drawn
+    over what the library accepts."""
+    rng = np.random.default_rng(seed)
+    D = int(rng.choice([64, 128]))
+    kv = [W.BF16, W.F16, W.FP8][seed % 3]
+    qd = (W.BF16 if rng.integers(2) else W.F16) if kv == W.FP8 else kv
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
+    S = int(rng.integers(1, 10))
+    lens, qlens = [], []
+    for _ in range(S):
+        L = int(rng.choice([rng.integers(1, 64), rng.integers(64, 1200), rng.integers(1200, 5000)]))
+        kind = rng.integers(6)
+        if kind <= 2:
+            Q = 1
+        elif kind == 3:
+            Q = int(rng.integers(2, 9))           # verify rows
+        elif kind == 4:
+            Q = int(rng.integers(9, 200))         # a prefill chunk
+        else:
+            Q = L if L <= 200 else 1              # a whole short prompt
+        lens.append(L)
+        qlens.append(min(Q, L))
+    return dict(Hq=Hkv * G, Hkv=Hkv, D=D, kv=kv, qd=qd, lens=lens, qlens=qlens)
+
+
+@pytest.mark.parametrize("seed", range(1000, 1024))
+def test_random_steps_all_outputs(seed):
+    case = _random_case(seed)
+    wl = _small(seed=seed, **case)
+    _check(wl, _run(wl, f"random step seed={seed} G={case['Hq'] // case['Hkv']} qlens={case['qlens']}"))
+
+
 @pytest.mark.parametrize("part_tokens", [16, 64, 256, 4096])
 def test_partition_sizes(part_tokens, monkeypatch):
     monkeypatch.setenv("PKV_PART_TOKENS", str(part_tokens))
