@@ -20,9 +20,10 @@
 // index k = 8*(l/16) + i meaning token 4*(l/16) + i%4 of block i/4, exactly the
 // B layout the second product needs, so the softmax weights never leave their
 // lanes.  Head dims are permuted freely inside each contraction so that the
-// operands come from contiguous memory: for S^T, K load c of lane l reads 16
-// bytes at 64c + 16(l/16) of token row l%16 (one load instruction covers a
-// 64-byte segment of 16 rows) and the query operand holds the same dims; for
+// operands are contiguous runs: for S^T, K chunk c of lane l holds the 16
+// bytes at 64c + 16(l/16) of token row l%16 and the query operand holds the
+// same dims (decode items load K as whole lines and regroup it into these
+// chunks through LDS; prefill items read them from their LDS stages); for
 // O^T from registers the output dim of (tile j, row m) is m * D/16 + j, so
 // lane l reads D/16 consecutive dims of each of its tokens, and for O^T from
 // LDS through transposing reads (16-bit prefill items) it is 16j + m.  fp8 K/V
@@ -107,12 +108,10 @@ struct TileLay {
   static constexpr int BLKB = 16 * ROWB;        // bytes of one (block, head)
   static constexpr int KSTEPS = D / 32;         // 16x16x32 MFMA steps of the score product
   static constexpr int KB = D / 4 * ELT;        // K bytes per lane per block (D/4 dims)
-  static constexpr int KLD = KB / 16;           // 16-byte loads of K per lane
-  // K load c of lane group gq covers bytes c*64 + gq*16 of its token row, so
-  // one load instruction reads 64 contiguous bytes of each of the 16 rows (a
-  // whole 64-byte segment, not four 16-byte pieces of four); score step st
-  // contracts over the 8 dims starting at k_dim(st, gq), which the query
-  // operand of that step holds too
+  static constexpr int KLD = KB / 16;           // 16-byte chunks of K per lane
+  // K chunk c of lane group gq holds bytes c*64 + gq*16 of its token row;
+  // score step st contracts over the 8 dims starting at k_dim(st, gq), which
+  // the query operand of that step holds too
   static __host__ __device__ constexpr int k_dim(int st, int gq) {
     return ELT == 2 ? st * 32 + gq * 8 : (st / 2) * 64 + gq * 16 + (st % 2) * 8;
   }

@@ -104,3 +104,17 @@ def test_pre_append_pool_poisons_only_the_appended_slots():
     assert diff.sum() == 4
     out = oracle.kv_append(pre, wl.k_new, wl.slot_mapping, 16)
     assert np.array_equal(out, post)
+
+
+def test_kv_pools_share_one_allocation_with_a_gap():
+    from paged_kv_cache_286_amd.device import KV_POOL_GAP_BYTES, alloc_kv_pools
+    shape = (64, 4, 16, 64)
+    for dtype in (torch.bfloat16, torch.uint8):
+        k, v = alloc_kv_pools(shape, dtype, "cpu", 7)
+        assert k.shape == v.shape == shape and k.is_contiguous() and v.is_contiguous()
+        nbytes = k.numel() * k.element_size()
+        assert v.data_ptr() - k.data_ptr() == nbytes + KV_POOL_GAP_BYTES
+        assert KV_POOL_GAP_BYTES % 4096 == 0 and (KV_POOL_GAP_BYTES // 4096) % 2 == 1
+        assert int(k.min()) == int(k.max()) == 7 and int(v.min()) == 7
+        k.fill_(1)                      # the pools do not overlap
+        assert int(v.max()) == 7
