@@ -111,6 +111,14 @@ CONFIGS: Dict[str, Config] = {
         "64 decode seqs, ctx U[8192,32768], 64 q heads / 8 kv heads x 128, fp8-e4m3 K/V with a "
         "float32 scale per (block, kv head), bf16 q",
         64, 8, 128, 16, 131072, FP8, BF16, 5),
+    # not one of the five steps the metric is quoted on: the 7B decode step's lengths
+    # at a grouped-query head layout (32 query / 8 kv heads), which runs the 16-bit
+    # MFMA decode items
+    "gqa_decode": Config(
+        "gqa_decode",
+        "64 decode seqs, ctx U[128,4096], 32 q heads / 8 kv heads x 128, bf16, block 16, pool for "
+        "64x4096 tokens",
+        32, 8, 128, 16, 16384, BF16, BF16, 7),
     # not one of the five steps the metric is quoted on: the prefill tile alone, so
     # that its MFMA rate can be measured without decode rows hiding it
     "prefill_chunks": Config(
@@ -183,6 +191,13 @@ def make_plan(name: str) -> Plan:
         tables = _take_tables(lens, order, bs, 80 // bs)
         return Plan(cfg, lens.astype(np.int32), qlens.astype(np.int32), tables, 80 // bs)
     if name == "decode_7b":
+        lens = rng.integers(128, 4096, size=64, endpoint=True)
+        qlens = np.ones(64, dtype=np.int64)
+        order = rng.permutation(NB)
+        mb = 4096 // bs
+        return Plan(cfg, lens.astype(np.int32), qlens.astype(np.int32),
+                    _take_tables(lens, order, bs, mb), mb)
+    if name == "gqa_decode":
         lens = rng.integers(128, 4096, size=64, endpoint=True)
         qlens = np.ones(64, dtype=np.int64)
         order = rng.permutation(NB)

@@ -397,7 +397,7 @@ def _check_appended(wl, ds, n=64):
 
 
 @pytest.mark.parametrize("name", ["decode_7b", "long_tail", "mixed_prefill", "fp8_gqa_long",
-                                  "prefill_chunks"])
+                                  "prefill_chunks", "gqa_decode"])
 def test_full_size_workload_sampled(name):
     _say(f"[gpu] generating {name}")
     wl = W.generate(W.make_plan(name))
