@@ -89,7 +89,39 @@ def cpu_baseline(wl, seconds):
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"float64 numpy oracle, attention of the first {len(done)} of {p.num_seqs} "
                       f"sequences ({toks} context tokens, {toks * per_tok} KV bytes) in "
-                      f"{t_used:.1f} s on 1 thread of {platform.processor() or platform.machine()}"}
+                      f"{t_used:.1f} s on 1 thread of {cpu_model()}",
+            "host_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def copy_bandwidth(torch, mib=1024, reps=10):
+    """Bytes read + written per second by a plain device copy of `mib` MiB (torch's
+    copy kernel): a measured ceiling beside the 8 TB/s specification."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / reps
+    del src, dst
+    return 2 * n / (ms / 1e3) / 1e9
 
 
 def main():
@@ -202,6 +234,8 @@ def main():
                         "algorithmic_bytes_per_launch": alg["unique"]}
         roofline["l2_hit_rate"] = meas.get("tcc_hit_rate")
         roofline["mfma_busy"] = meas.get("mfma_busy_frac")
+    # a device copy's read + write rate on the same GPU, for reference
+    copy_gbs = copy_bandwidth(torch)
     cpu = None
     if not args.no_cpu_baseline:
         log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
@@ -236,6 +270,8 @@ def main():
         },
         "batch_steps_per_s": round(1000.0 / ms_per_step, 2),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "copy_gbs": round(copy_gbs, 1),
+        "pct_of_copy": round(100 * value / copy_gbs, 2),
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
