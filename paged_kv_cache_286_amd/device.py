@@ -108,6 +108,7 @@ class DeviceStep:
             plan.max_query_len)
         self.workspace = (torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
                           if self.ws_bytes else None)
+        self._bound, self._bound_key = None, None
 
     def poison_appended_slots(self) -> None:
         """Put the pools back in their pre-append state (appended slots hold NaN bits)."""
@@ -137,8 +138,34 @@ class DeviceStep:
             shared_blocks=self.shared_blocks)
 
     def step(self, stream=None) -> None:
-        self.append(stream)
-        self.attend(stream)
+        """append, then attend, with the two calls' arguments converted once per
+        stream (the buffers keep their addresses; after replacing one of the
+        buffer attributes, call rebind())."""
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        key = int(s.cuda_stream) if not isinstance(s, int) else s
+        if self._bound_key != key:
+            # both calls with their arguments converted once for this stream
+            self._bound = (self.bind_append(s), self.bind_attend(s))
+            self._bound_key = key
+        self._bound[0]()
+        self._bound[1]()
+
+    def rebind(self) -> None:
+        self._bound, self._bound_key = None, None
+
+    def bind_append(self, stream):
+        return pk.bind_paged_kv_append(self.pool, self.k_pool, self.v_pool, self.k_new, self.v_new,
+                                       self.kv_dtype, self.slot_mapping, len(self.wl.slot_mapping),
+                                       stream)
+
+    def bind_attend(self, stream):
+        plan, cfg = self.wl.plan, self.wl.cfg
+        return pk.bind_paged_attn_step(
+            self.pool, self.q, self.q_dtype, cfg.num_q_heads, self.k_pool, self.v_pool,
+            self.k_scale, self.v_scale, self.block_tables, plan.max_blocks_per_seq,
+            self.context_lens, self.query_lens, plan.num_seqs, plan.total_q_tokens,
+            plan.max_context_len, plan.max_query_len, float(self.wl.scale), self.out,
+            self.workspace, self.ws_bytes, stream, shared_blocks=self.shared_blocks)
 
     def out_bits(self) -> np.ndarray:
         return self.out.cpu().numpy().view(np.uint16)

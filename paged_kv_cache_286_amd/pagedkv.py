@@ -186,6 +186,42 @@ def paged_kv_append_quant(pool: PkvPool, k_pool, v_pool, k_scale, v_scale, k_new
         _ptr(slot_mapping), int(num_tokens), _stream(stream)))
 
 
+def bind_paged_kv_append(pool: PkvPool, k_pool, v_pool, k_new, v_new, new_dtype: int,
+                         slot_mapping, num_tokens: int, stream=None):
+    """paged_kv_append with its arguments converted once (tensor addresses read
+    now): the returned callable issues the same call again.  For a caller that
+    repeats one step on buffers that keep their addresses; it saves the
+    per-call argument conversion."""
+    return _bound("paged_kv_append", _lib.paged_kv_append,
+                  (_poolref(pool), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+                   int(new_dtype), _ptr(slot_mapping), int(num_tokens), _stream(stream)))
+
+
+def bind_paged_attn_step(pool: PkvPool, q, q_dtype: int, num_q_heads: int, k_pool, v_pool,
+                         k_scale, v_scale, block_tables, max_blocks_per_seq: int, context_lens,
+                         query_lens, num_seqs: int, total_q_tokens: int, max_context_len: int,
+                         max_query_len: int, scale: float, out, workspace, workspace_bytes: int,
+                         stream=None, shared_blocks=None):
+    """paged_attn_step with its arguments converted once; see bind_paged_kv_append."""
+    return _bound("paged_attn_step", _lib.paged_attn_step,
+                  (_poolref(pool), _ptr(q), int(q_dtype), int(num_q_heads), _ptr(k_pool),
+                   _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                   int(max_blocks_per_seq), _ptr(context_lens), _ptr(query_lens),
+                   _ptr(shared_blocks), int(num_seqs), int(total_q_tokens), int(max_context_len),
+                   int(max_query_len), float(scale), _ptr(out), _ptr(workspace),
+                   int(workspace_bytes), _stream(stream)))
+
+
+def _bound(name: str, fn, args):
+    # plain numbers become ctypes objects of the declared argument types up front
+    conv = tuple(t(a) if isinstance(a, (int, float)) and not isinstance(a, bool) else a
+                 for a, t in zip(args, fn.argtypes))
+
+    def call() -> None:
+        _check(name, fn(*conv))
+    return call
+
+
 def paged_attn_workspace_bytes(pool: PkvPool, num_seqs: int, num_q_heads: int,
                                total_q_tokens: int, max_context_len: int,
                                max_query_len: int) -> int:
