@@ -140,3 +140,18 @@ def test_library_shares_torchs_hip_runtime():
     maps = open("/proc/self/maps").read()
     hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(hip) == 1, hip
+
+
+def test_bound_calls_convert_once_and_report_errors():
+    # a bound call repeats the same C call; validation errors still raise
+    p = _pool()
+    call = pk.bind_paged_attn_step(p, FAKE, pk.PKV_BF16, 6, FAKE, FAKE, None, None, FAKE, 8, FAKE,
+                                   FAKE, 4, 4, 100, 1, 0.125, FAKE, None, 0)
+    for _ in range(2):
+        with pytest.raises(pk.PagedKVError) as e:
+            call()
+        assert e.value.status == pk.PKV_ERR_SHAPE          # 6 q heads over 4 kv heads
+    app = pk.bind_paged_kv_append(p, FAKE, FAKE, FAKE, FAKE, pk.PKV_F16, FAKE, 4)
+    with pytest.raises(pk.PagedKVError) as e:
+        app()
+    assert e.value.status == pk.PKV_ERR_DTYPE               # f16 rows into a bf16 pool
