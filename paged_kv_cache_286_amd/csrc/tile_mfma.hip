@@ -507,19 +507,22 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   // score is masked and the scale folds into the exponent's argument (for a
   // positive factor the maximum of the products is the product of the maximum).
   // build_va(va) fills the V^T operand of the pair.
+  // Order: every tile's maximum and rescale factor first, then the one
+  // (rarely taken) rescale branch, then per tile the weights and their PV
+  // products -- straight-line code in which one tile's exponentials can be
+  // issued between the other tile's matrix products.
   auto attend_pair = [&](auto dense_tag, const BlockRegs<KV, D>& r0, const BlockRegs<KV, D>& r1,
                          auto&& build_va) {
     constexpr bool DENSE = decltype(dense_tag)::value;
     f32x4 s0[TPW], s1[TPW];
     scores(r0, s0);
     scores(r1, s1);
-    uint4 pb_hi[TPW], pb_lo[TPW];
     const float c0 = p.scale_log2 * r0.ksc, c1 = p.scale_log2 * r1.ksc;
+    float mn[TPW], alpha[TPW];
+    bool ok[TPW][8];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      float pw[8];
-      float ps = 0.f;
-      float mx, mn;
+      float mx;
       if constexpr (DENSE) {
         float mx0 = s0[t][0], mx1 = s1[t][0];
 #pragma unroll
@@ -528,68 +531,73 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
           mx1 = fmaxf(mx1, s1[t][i]);
         }
         mx = max_xor32(max_xor16(fmaxf(mx0 * c0, mx1 * c1)));
-        mn = mx > m[t] + kLazyRescale ? mx : m[t];   // lazy reference maximum
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pw[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[t][i], c0, -mn));
-          pw[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[t][i], c1, -mn));
-        }
       } else {
-        float sv[8];
-        bool ok[8];
         mx = -__builtin_inff();
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int tk = gq * 4 + i4;
-          ok[i4] = col_ok[t] && tk < r0.limit && r0.base + tk <= pos[t];
-          ok[4 + i4] = col_ok[t] && tk < r1.limit && r1.base + tk <= pos[t];
-          sv[i4] = s0[t][i4] * c0;
-          sv[4 + i4] = s1[t][i4] * c1;
+          ok[t][i4] = col_ok[t] && tk < r0.limit && r0.base + tk <= pos[t];
+          ok[t][4 + i4] = col_ok[t] && tk < r1.limit && r1.base + tk <= pos[t];
+          mx = fmaxf(mx, ok[t][i4] ? s0[t][i4] * c0 : -__builtin_inff());
+          mx = fmaxf(mx, ok[t][4 + i4] ? s1[t][i4] * c1 : -__builtin_inff());
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, ok[i] ? sv[i] : -__builtin_inff());
         mx = max_xor32(max_xor16(mx));
-        mn = mx > m[t] + kLazyRescale ? mx : m[t];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pw[i] = ok[i] ? __builtin_amdgcn_exp2f(sv[i] - mn) : 0.f;
       }
-      const float alpha = __builtin_amdgcn_exp2f(m[t] - mn);
-      if constexpr (ONES_SUM) {
-        // the column sums come out of the MFMA (below)
-        (void)ps;
-      } else {
+      mn[t] = mx > m[t] + kLazyRescale ? mx : m[t];   // lazy reference maximum
+      alpha[t] = __builtin_amdgcn_exp2f(m[t] - mn[t]);
+    }
+    bool moved = false;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ps += pw[i];
-        lsum[t] = lsum[t] * alpha + ps;
-      }
-      m[t] = mn;
-      if (__any(alpha != 1.f)) {     // the reference rarely moves after the first blocks
+    for (int t = 0; t < TPW; ++t) moved = moved || alpha[t] != 1.f;
+    if (__any(moved)) {     // the reference rarely moves after the first blocks
 #pragma unroll
-        for (int j = 0; j < L::DT; ++j) o[t][j] *= alpha;
-        if constexpr (ONES_SUM) osum[t] *= alpha;
-      }
+      for (int t = 0; t < TPW; ++t) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pw[i] *= r0.vsc;
-        pw[4 + i] *= r1.vsc;
+        for (int j = 0; j < L::DT; ++j) o[t][j] *= alpha[t];
+        if constexpr (ONES_SUM) osum[t] *= alpha[t];
       }
-      split_weights<QT>(pw, pb_hi[t], pb_lo[t]);
     }
 
     uint4 va[L::DT];
     build_va(va);
 #pragma unroll
-    for (int j = 0; j < L::DT; ++j) {
+    for (int t = 0; t < TPW; ++t) {
+      float pw[8];
+      if constexpr (DENSE) {
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        o[t][j] = mfma32<QT>(va[j], pb_hi[t], o[t][j]);
-        if constexpr (ONES_SUM) {
-          if (j == 0) {
-            osum[t] = mfma32<QT>(ones, pb_hi[t], osum[t]);
-            osum[t] = mfma32<QT>(ones, pb_lo[t], osum[t]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          pw[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[t][i], c0, -mn[t]));
+          pw[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[t][i], c1, -mn[t]));
         }
-        if constexpr (KV != kFP8) o[t][j] = mfma32<QT>(va[j], pb_lo[t], o[t][j]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pw[i] = ok[t][i] ? __builtin_amdgcn_exp2f(s0[t][i] * c0 - mn[t]) : 0.f;
+          pw[4 + i] = ok[t][4 + i] ? __builtin_amdgcn_exp2f(s1[t][i] * c1 - mn[t]) : 0.f;
+        }
+      }
+      if constexpr (!ONES_SUM) {       // (else the column sums come out of the MFMA below)
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ps += pw[i];
+        lsum[t] = lsum[t] * alpha[t] + ps;
+      }
+      m[t] = mn[t];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pw[i] *= r0.vsc;
+        pw[4 + i] *= r1.vsc;
+      }
+      uint4 pb_hi, pb_lo;
+      split_weights<QT>(pw, pb_hi, pb_lo);
+      if constexpr (ONES_SUM) {
+        osum[t] = mfma32<QT>(ones, pb_hi, osum[t]);
+        osum[t] = mfma32<QT>(ones, pb_lo, osum[t]);
+      }
+#pragma unroll
+      for (int j = 0; j < L::DT; ++j) {
+        o[t][j] = mfma32<QT>(va[j], pb_hi, o[t][j]);
+        if constexpr (KV != kFP8) o[t][j] = mfma32<QT>(va[j], pb_lo, o[t][j]);
       }
     }
   };
