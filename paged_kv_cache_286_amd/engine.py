@@ -286,22 +286,43 @@ class DeviceEngine:
     a prefill.  The tables (bf16 / f16 bits) are kept in ``self.kv_tables``.
     """
 
+    # fp8 pools: the scale a block takes when its first row is written, per kv
+    # head (a fixed scale: N(0,1) rows reach the E4M3 limit of 448 only past 7)
+    FP8_BLOCK_SCALE = 1.0 / 64.0
+
     def __init__(self, batcher: ContinuousBatcher, num_q_heads: int, num_kv_heads: int,
                  head_dim: int, dtype: str = "bf16", seed: int = 0, device: str = "cuda:0",
-                 keep_host_mirror: bool = False, kv_from_tokens: bool = False):
+                 keep_host_mirror: bool = False, kv_from_tokens: bool = False,
+                 kv_dtype: Optional[str] = None):
+        """dtype: the query / new-row type (bf16 or f16).  kv_dtype: the pools'
+        type, dtype (default) or "fp8_e4m3" (rows quantised on append with a
+        scale per (block, kv head); no host mirror)."""
         import torch
         from .device import alloc_kv_pools
         self.torch = torch
         self.b = batcher
         self.Hq, self.Hkv, self.D = num_q_heads, num_kv_heads, head_dim
         self.dtype = dtype
+        self.kv_dtype = kv_dtype or dtype
+        self.fp8 = self.kv_dtype == "fp8_e4m3"
+        if self.kv_dtype not in (dtype, "fp8_e4m3"):
+            raise ValueError(f"kv_dtype {self.kv_dtype} with rows of {dtype}")
+        if self.fp8 and keep_host_mirror:
+            raise ValueError("no host mirror of fp8 pools: read the pools back instead")
         self.dev = torch.device(device)
         nb, bs = batcher.bm.num_blocks, batcher.block_size
         tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
         self.tdt = tdt
-        self.k_pool, self.v_pool = alloc_kv_pools((nb, num_kv_heads, bs, head_dim), tdt, self.dev)
-        self.pool = pk.make_pool(nb, bs, num_kv_heads, head_dim, dtype)
+        self.k_pool, self.v_pool = alloc_kv_pools((nb, num_kv_heads, bs, head_dim),
+                                                  torch.uint8 if self.fp8 else tdt, self.dev)
+        self.pool = pk.make_pool(nb, bs, num_kv_heads, head_dim, self.kv_dtype)
         self.code = pk.DTYPE_CODES[dtype]
+        self.k_scale = self.v_scale = self.new_block_scale = None
+        if self.fp8:
+            self.k_scale = torch.ones((nb, num_kv_heads), dtype=torch.float32, device=self.dev)
+            self.v_scale = torch.ones_like(self.k_scale)
+            self.new_block_scale = torch.full((num_kv_heads,), self.FP8_BLOCK_SCALE,
+                                              dtype=torch.float32, device=self.dev)
         self.gen = torch.Generator(device=self.dev)
         self.gen.manual_seed(seed)
         self.scale = float(np.float32(1.0 / np.sqrt(head_dim)))
@@ -342,11 +363,16 @@ class DeviceEngine:
         out = torch.empty_like(q)
         if len(batch.copies):
             pairs = torch.from_numpy(np.ascontiguousarray(batch.copies)).to(self.dev)
-            pk.paged_kv_copy_blocks(self.pool, self.k_pool, self.v_pool, None, None, pairs,
-                                    len(batch.copies), stream)
+            pk.paged_kv_copy_blocks(self.pool, self.k_pool, self.v_pool, self.k_scale,
+                                    self.v_scale, pairs, len(batch.copies), stream)
         slots = torch.from_numpy(batch.slot_mapping).to(self.dev)
-        pk.paged_kv_append(self.pool, self.k_pool, self.v_pool, k_new, v_new, self.code, slots,
-                           rows, stream)
+        if self.fp8:
+            pk.paged_kv_append_quant(self.pool, self.k_pool, self.v_pool, self.k_scale,
+                                     self.v_scale, k_new, v_new, self.code, self.new_block_scale,
+                                     self.new_block_scale, slots, rows, stream)
+        else:
+            pk.paged_kv_append(self.pool, self.k_pool, self.v_pool, k_new, v_new, self.code, slots,
+                               rows, stream)
         tables = torch.from_numpy(batch.block_tables).to(self.dev)
         ctx = torch.from_numpy(batch.context_lens).to(self.dev)
         ql = torch.from_numpy(batch.query_lens).to(self.dev)
@@ -356,9 +382,10 @@ class DeviceEngine:
         shared = None
         if batch.shared_blocks is not None and batch.shared_blocks.any():
             shared = torch.from_numpy(batch.shared_blocks).to(self.dev)
-        pk.paged_attn_step(self.pool, q, self.code, self.Hq, self.k_pool, self.v_pool, None, None,
-                           tables, self.b.max_blocks, ctx, ql, S, rows, max_ctx, max_q, self.scale,
-                           out, ws, ws_bytes, stream, shared_blocks=shared)
+        pk.paged_attn_step(self.pool, q, self.code, self.Hq, self.k_pool, self.v_pool,
+                           self.k_scale, self.v_scale, tables, self.b.max_blocks, ctx, ql, S, rows,
+                           max_ctx, max_q, self.scale, out, ws, ws_bytes, stream,
+                           shared_blocks=shared)
         if self.mirror is not None:
             kb = k_new.view(torch.int16).cpu().numpy().view(np.uint16)
             vb = v_new.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -369,5 +396,5 @@ class DeviceEngine:
             for r, sl in enumerate(batch.slot_mapping):
                 mk[sl // bs, :, sl % bs, :] = kb[r]
                 mv[sl // bs, :, sl % bs, :] = vb[r]
-        self.last = (q, out, ws)
+        self.last = (q, out, ws, k_new, v_new)
         return q, out

@@ -150,3 +150,60 @@ def test_copy_blocks_bit_exact_with_scales():
         k[dst], v[dst], ks[dst], vs[dst] = k[src], v[src], ks[src], vs[src]
     assert np.array_equal(gk.cpu().numpy(), k) and np.array_equal(gv.cpu().numpy(), v)
     assert np.array_equal(gks.cpu().numpy(), ks) and np.array_equal(gvs.cpu().numpy(), vs)
+
+
+def test_engine_fp8_pools_quantise_on_append_and_match_oracle():
+    # fp8 pools: each step's copy-on-write copies and quantising append leave the
+    # pools and scales the oracle's quantiser gives bit for bit, and the step's
+    # attention over those bytes matches the oracle within the fp8 tolerance
+    Hq, Hkv, D, nb = 8, 2, 128, 64
+    b = ContinuousBatcher(num_blocks=nb, max_seqs=6, token_budget=80, max_blocks_per_seq=32)
+    rng = np.random.default_rng(9)
+    rid = 0
+    for i in range(8):
+        b.submit(Request(rid, prompt=int(rng.integers(1, 90)), output=int(rng.integers(1, 30)),
+                         arrival=int(rng.integers(0, 15))))
+        rid += 1
+    b.submit(Request(rid, prompt=60, output=20, arrival=0))
+    parent = rid
+    rid += 1
+    for i in range(2):
+        b.submit(Request(rid, prompt=64, output=10, arrival=2, parent=parent, shared=37))
+        rid += 1
+    eng = DeviceEngine(b, Hq, Hkv, D, "bf16", seed=4, kv_dtype="fp8_e4m3")
+    read = lambda t: t.cpu().numpy()
+    prev = [read(eng.k_pool), read(eng.v_pool), read(eng.k_scale), read(eng.v_scale)]
+    init = np.full(Hkv, np.float32(eng.FP8_BLOCK_SCALE))
+    steps = copies = 0
+    worst = 0.0
+    while not b.idle() and steps < 400:
+        batch = b.plan()
+        steps += 1
+        res = eng.run(batch)
+        if res is None:
+            continue
+        torch.cuda.synchronize()
+        copies += len(batch.copies)
+        q, out, _, k_new, v_new = eng.last
+        kp, vp, ks, vs = (x.copy() for x in prev)
+        for src, dst in batch.copies:
+            kp[dst], vp[dst], ks[dst], vs[dst] = kp[src], vp[src], ks[src], vs[src]
+        bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+        kp, ks = oracle.kv_append_quant(kp, ks, bits(k_new), "bf16", batch.slot_mapping, 16, init)
+        vp, vs = oracle.kv_append_quant(vp, vs, bits(v_new), "bf16", batch.slot_mapping, 16, init)
+        cur = [read(eng.k_pool), read(eng.v_pool), read(eng.k_scale), read(eng.v_scale)]
+        for got, want, what in zip(cur, (kp, vp, ks, vs), ("K pool", "V pool", "K scales", "V scales")):
+            assert np.array_equal(got, want), f"step {batch.step}: {what} differ from the oracle"
+        ref = oracle.paged_attention(bits(q), cur[0], cur[1], batch.block_tables, batch.context_lens,
+                                     batch.query_lens, eng.scale, 16, "fp8_e4m3", "bf16",
+                                     cur[2], cur[3])
+        want = np.concatenate([ref[i] for i in range(len(batch.seq_ids))])
+        got = oracle.decode_bits(bits(out), "bf16")
+        err = float(np.max(np.abs(got - want)))
+        worst = max(worst, err)
+        assert err <= 5e-2, f"step {batch.step}: max err {err}"
+        prev = cur
+    b.flush()
+    print(f"[gpu] fp8 engine: {steps} steps, {copies} block copies, max|err| {worst:.3g}", flush=True)
+    assert b.idle() and len(b.done) == rid
+    assert copies > 0
