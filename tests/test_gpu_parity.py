@@ -460,3 +460,26 @@ def test_append_quant_bit_exact_whole_pool(new_dtype):
     torch.cuda.synchronize()
     rk2, _ = oracle.kv_append_quant(pool_k, ks, kbits, new_dtype, slots, bs, None)
     assert np.array_equal(gk2.cpu().numpy(), rk2)
+
+
+@pytest.mark.parametrize("seed", [1003, 1007, 1013, 1014, 1020])
+def test_no_writes_outside_workspace_and_output(seed):
+    # the step writes only its output rows and the first paged_attn_workspace_bytes
+    # bytes of the workspace: guard bytes after both stay as they were
+    case = _random_case(seed)
+    wl = _small(seed=seed, **case)
+    ds = _device_step(wl)
+    guard = 1 << 16
+    n = ds.ws_bytes
+    ws = torch.full((n + guard,), 0xAB, dtype=torch.uint8, device="cuda:0")
+    ds.workspace = ws[:n] if n else None
+    out_full = torch.full((ds.out.shape[0] + 4,) + tuple(ds.out.shape[1:]), 0x5A5A,
+                          dtype=ds.out.dtype, device="cuda:0")
+    ds.out = out_full[:ds.out.shape[0]]
+    _say(f"[gpu] guard bytes seed={seed}: workspace {n} B, {ds.out.shape[0]} rows")
+    ds.append()
+    ds.attend()
+    torch.cuda.synchronize()
+    assert bool((ws[n:] == 0xAB).all()), "a write past the workspace"
+    assert bool((out_full[ds.out.shape[0]:] == 0x5A5A).all()), "a write past the output rows"
+    _check(wl, ds)
