@@ -61,6 +61,8 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--reuse", default="parent", choices=["none", "parent", "cache"],
                     help="how shared-prompt requests reuse it")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8_e4m3"],
+                    help="KV pool type (fp8: quantised on append, a scale per block and kv head)")
     ap.add_argument("--dry-run", action="store_true", help="plan on the host only, no GPU")
     args = ap.parse_args(argv)
 
@@ -93,7 +95,7 @@ def main(argv=None):
     if not args.dry_run:
         import torch
         eng = DeviceEngine(b, args.heads, args.kv_heads, args.head_dim, "bf16", seed=args.seed,
-                           kv_from_tokens=args.reuse == "cache")
+                           kv_from_tokens=args.reuse == "cache", kv_dtype=args.kv)
         stream = torch.cuda.current_stream()
         torch.cuda.synchronize()
     host_s = 0.0
