@@ -483,3 +483,17 @@ def test_no_writes_outside_workspace_and_output(seed):
     assert bool((ws[n:] == 0xAB).all()), "a write past the workspace"
     assert bool((out_full[ds.out.shape[0]:] == 0x5A5A).all()), "a write past the output rows"
     _check(wl, ds)
+
+
+def test_repeated_steps_bit_identical():
+    # the same step run again gives the same bits (every reduction has a fixed
+    # order; the decode items' K regrouping through LDS included): the 7B
+    # decode lengths at 32 query / 8 kv heads, bf16, three times
+    wl = W.generate(W.make_plan("gqa_decode"))
+    ds = _run(wl, "gqa_decode repeated")
+    first = ds.out.clone()
+    for r in range(2):
+        ds.out.fill_(0)
+        ds.step()
+        torch.cuda.synchronize()
+        assert torch.equal(ds.out, first), f"run {r + 2} differs from the first"
