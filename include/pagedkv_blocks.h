@@ -16,7 +16,10 @@
  *     block carrying a reference count;
  *   - "Copy-on-Write": writing into a block whose reference count is above one
  *     first copies it to a fresh block, and only the writer's table changes
- *     (this is also how several samples of one prompt diverge);
+ *     (this is also how several samples of one prompt diverge).  With the
+ *     prefix cache on, a block that is the value of a key is copied before
+ *     any write into it even when its writer is its only reader: a key names
+ *     the block's exact tokens, so a cached block never changes;
  *   - "What the Scheduler Does": a sequence is admitted only if enough blocks
  *     are free; a sequence can be preempted by releasing its blocks.
  *

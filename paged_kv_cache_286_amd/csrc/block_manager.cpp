@@ -107,6 +107,12 @@ int32_t take_block(pkv_block_manager* bm) {
   return b;
 }
 
+// A block that is the value of a prefix-cache key holds exactly the tokens
+// its key names, so no sequence may write into it: a sequence whose partial
+// last block is such a block (it shared a parent's full block part-way) copies
+// it before appending, even when it is the block's only reader.
+bool is_cached(const pkv_block_manager* bm, int32_t b) { return bm->caching && bm->in_cache[b]; }
+
 // a block dropped by one reader
 void drop_block(pkv_block_manager* bm, int32_t b) {
   if (--bm->ref[b] > 0) return;
@@ -159,7 +165,7 @@ int simulate(const pkv_block_manager* bm, const int64_t* seqs, const int32_t* co
     if (s.len % bm->block_size != 0 && !s.last_private) {
       const int32_t last = it->second.blocks[s.len / bm->block_size];
       const int32_t r = bm->ref[last] + ref_delta[last];
-      if (r > 1) {
+      if (r > 1 || is_cached(bm, last)) {
         ++need;
         ++cow;
         ref_delta[last] -= 1;
@@ -372,9 +378,9 @@ int pkv_bm_append(pkv_block_manager* bm, const int64_t* seqs, const int32_t* cou
     if (counts[i] == 0) continue;
     if (s.len % bs != 0) {
       int32_t& last = s.blocks[s.len / bs];
-      if (bm->ref[last] > 1) {
+      if (bm->ref[last] > 1 || is_cached(bm, last)) {
         const int32_t fresh = take_block(bm);
-        bm->ref[last] -= 1;
+        drop_block(bm, last);
         copies[2 * nc] = last;
         copies[2 * nc + 1] = fresh;
         ++nc;

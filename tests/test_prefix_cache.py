@@ -201,3 +201,33 @@ def test_random_traffic_against_a_plain_model():
     assert bm.free_blocks == 4096
     st = bm.cache_stats()
     assert st["evictable"] == st["cached"] and st["evictions"] == 0
+
+
+def test_child_sharing_a_cached_block_part_way_copies_it_after_the_parent_leaves():
+    # A child shares 20 tokens of a parent whose two full blocks are keyed, so
+    # the child's partial last block is the parent's cached block 1.  Once the
+    # parent is released the child is that block's only reader, yet the block
+    # is still the value of a key: appending must copy it first ("Copy-on-Write"),
+    # or a later request with the parent's prompt would read the child's row.
+    bm = pk.BlockManager(16, BS, prefix_cache=True)
+    prompt = np.arange(100, 132, dtype=np.int32)            # 32 tokens: two full blocks
+    assert bm.add_prompt(1, prompt) == 0
+    slots, copies = bm.append([1], [32])
+    parent_blocks = sorted(set((slots // BS).tolist()))
+    assert len(copies) == 0 and bm.cache_stats()["cached"] == 2
+    bm.add(2, parent=1, shared_tokens=20)
+    bm.release(1)
+    blk1 = int(slots[16] // BS)
+    assert bm.refcount(blk1) == 1
+    assert bm.blocks_needed([2], [1]) == 1                  # the copy
+    slots2, copies2 = bm.append([2], [1])
+    assert copies2.tolist() == [[blk1, int(slots2[0]) // BS]]
+    assert int(slots2[0]) // BS not in parent_blocks and int(slots2[0]) % BS == 4
+    # the parent's prompt still finds both blocks, untouched
+    got = bm.add_prompt(3, np.concatenate([prompt, [7]]).astype(np.int32))
+    assert got == 32
+    t, lens = bm.tables([3], 4)
+    assert t[0, :2].tolist() == [int(slots[0] // BS), blk1]
+    bm.release(2)
+    bm.release(3)
+    assert bm.free_blocks == 16
