@@ -38,7 +38,9 @@
  *   append slots distinct.  Kernels skip any address that would fall outside
  *   the pools (so a violation gives wrong numbers, not a memory fault).
  *   Calls are reentrant; calls that share output buffers on concurrent streams
- *   race.
+ *   race.  The only process-wide settings are the plan override
+ *   (pkv_set_plan_override) and kernel timing (pkv_timing_*), both meant for
+ *   tests and measurement.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -174,6 +176,33 @@ int paged_attn_step(const pkv_pool* pool,
                     int32_t max_context_len, int32_t max_query_len,
                     float scale, void* out,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* pkv_set_plan_override -- force parts of the launch plan that the library
+ * otherwise derives from the host scalars of a step (a testing and tuning
+ * hook: every choice gives the same results up to rounding order).
+ *   part_tokens        tokens per split-context partition of decode rows;
+ *   chunk_part_tokens  tokens per partition of prefill-chunk rows;
+ *                      each 0 (library's choice) or a multiple of 16 in [16, 4096];
+ *   small_q            sequences with query_len <= small_q run as decode items
+ *                      (applied only where small_q * (num_q_heads / num_kv_heads)
+ *                      <= 16); 0 = library's choice, at most 16;
+ *   decode_on_mfma     1: decode rows on the MFMA tile kernel, 0: decode-only
+ *                      steps run them on the VALU kernel (steps with prefill
+ *                      chunks keep fp8 and grouped-query decode rows on the
+ *                      MFMA tiles), -1 = library's choice.
+ * o == NULL restores every default.  Returns PKV_ERR_SHAPE (and changes
+ * nothing) for an out-of-range field.  The setting is process-wide and applies
+ * to every later paged_attn_workspace_bytes and paged_attn_step call; set it
+ * while no other thread is calling the library, and size the workspace after
+ * setting it (a step whose plan needs more workspace than it was given
+ * returns PKV_ERR_WORKSPACE). */
+typedef struct pkv_plan_override {
+  int32_t part_tokens;
+  int32_t chunk_part_tokens;
+  int32_t small_q;
+  int32_t decode_on_mfma;
+} pkv_plan_override;
+int pkv_set_plan_override(const pkv_plan_override* o);
 
 /* pkv_status_string -- static text for a status code (never NULL). */
 const char* pkv_status_string(int status);

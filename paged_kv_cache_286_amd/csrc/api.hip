@@ -1,9 +1,8 @@
 // C ABI of libpagedkv: argument validation, the launch plan of a step, the
 // workspace carve-up and optional per-kernel event timing.  See
 // include/pagedkv.h for the contract of every entry point.
-#include <stdlib.h>
-
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -84,10 +83,16 @@ hipError_t timed_launch(int kind, hipStream_t stream, F&& launch) {
 // ---------------------------------------------------------------------------
 // the plan of a step
 // ---------------------------------------------------------------------------
-int env_int(const char* name, int dflt) {
-  const char* s = getenv(name);
-  if (s == nullptr || *s == 0) return dflt;
-  return atoi(s);
+// Forced plan choices (pkv_set_plan_override); 0 / -1 = the library's own.
+struct PlanOverride {
+  std::atomic<int32_t> part_tokens{0};
+  std::atomic<int32_t> chunk_part_tokens{0};
+  std::atomic<int32_t> small_q{0};
+  std::atomic<int32_t> decode_on_mfma{-1};
+};
+PlanOverride& plan_override() {
+  static PlanOverride o;
+  return o;
 }
 
 // Tokens per split-context partition: about 512 KiB (fp8: 1 MiB) of K+V per
@@ -96,8 +101,8 @@ int env_int(const char* name, int dflt) {
 // saves less time than the merge launch it brings costs (a tiny step of 4
 // rows of at most 80 tokens runs unsplit, in two launches instead of three).
 int32_t part_tokens_for(const pkv_pool* pool, int32_t rows, int32_t wg_per_row, int32_t max_ctx) {
-  const int forced = env_int("PKV_PART_TOKENS", 0);
-  if (forced >= 16 && forced <= 4096 && forced % 16 == 0) return forced;
+  const int forced = plan_override().part_tokens.load(std::memory_order_relaxed);
+  if (forced != 0) return forced;
   const int32_t bytes_per_token = 2 * pool->head_dim * elem_bytes(pool->kv_dtype);
   // fp8 workgroups run the longer MFMA ring; they amortise their start-up over more bytes
   int32_t pt = (pool->kv_dtype == PKV_FP8_E4M3 ? 1024 : 512) * 1024 / bytes_per_token;
@@ -123,7 +128,7 @@ struct Layout {
 // blocks shared by the workgroup's four waves; longer prefill chunks become
 // chunk entries of chunk_entry_cols columns.
 int32_t small_q_for(int32_t group) {
-  const int forced = env_int("PKV_SMALL_Q", 0);
+  const int forced = plan_override().small_q.load(std::memory_order_relaxed);
   if (forced >= 1 && forced * group <= 16) return forced;
   return group <= 16 ? std::max(1, 16 / group) : 1;
 }
@@ -139,7 +144,7 @@ int32_t heads_per_wg_for(int32_t group) {
 // and fp8 decode rows run on the MFMA tile kernel, where the group's heads fill
 // the columns of a 16x16 tile and K/V are read once for all of them.
 bool decode_on_mfma_for(const pkv_pool* pool, int32_t group) {
-  const int forced = env_int("PKV_DECODE_MFMA", -1);
+  const int forced = plan_override().decode_on_mfma.load(std::memory_order_relaxed);
   if (forced == 0 || forced == 1) return forced == 1;
   return pool->kv_dtype == PKV_FP8_E4M3 || group > 2;
 }
@@ -156,8 +161,8 @@ int32_t round16(int64_t x) { return (int32_t)((x + 15) / 16 * 16); }
 constexpr int32_t kFewSeqs = 8;
 int32_t chunk_part_tokens_for(int32_t group, int32_t num_kv_heads, int32_t max_ctx, int32_t max_q,
                               int32_t cols, int32_t num_seqs) {
-  const int forced = env_int("PKV_CHUNK_PART_TOKENS", 0);
-  if (forced >= 16 && forced <= 4096 && forced % 16 == 0) return forced;
+  const int forced = plan_override().chunk_part_tokens.load(std::memory_order_relaxed);
+  if (forced != 0) return forced;
   const int64_t tiles = ((int64_t)max_q * group + cols - 1) / cols;
   const int64_t items = tiles * num_kv_heads;
   const int64_t want = num_seqs <= kFewSeqs ? 512 : 256;
@@ -422,6 +427,26 @@ int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_
   if (e == hipSuccess && merge)
     e = timed_launch(PKV_KERNEL_REDUCE, s, [&] { return pkv::launch_reduce(p, plan, s); });
   return hip_status(e);
+}
+
+int pkv_set_plan_override(const pkv_plan_override* o) {
+  PlanOverride& po = plan_override();
+  if (o == nullptr) {
+    po.part_tokens = 0;
+    po.chunk_part_tokens = 0;
+    po.small_q = 0;
+    po.decode_on_mfma = -1;
+    return PKV_OK;
+  }
+  auto tokens_ok = [](int32_t t) { return t == 0 || (t >= 16 && t <= 4096 && t % 16 == 0); };
+  if (!tokens_ok(o->part_tokens) || !tokens_ok(o->chunk_part_tokens)) return PKV_ERR_SHAPE;
+  if (o->small_q < 0 || o->small_q > 16) return PKV_ERR_SHAPE;
+  if (o->decode_on_mfma < -1 || o->decode_on_mfma > 1) return PKV_ERR_SHAPE;
+  po.part_tokens = o->part_tokens;
+  po.chunk_part_tokens = o->chunk_part_tokens;
+  po.small_q = o->small_q;
+  po.decode_on_mfma = o->decode_on_mfma;
+  return PKV_OK;
 }
 
 int pkv_timing_enable(int32_t capacity) {

@@ -45,6 +45,21 @@ def shared_prefix_blocks(tables: np.ndarray, context_lens: np.ndarray) -> np.nda
     return run.astype(np.int32)
 
 
+def check_slots_injective(slot_mapping, num_slots: int) -> None:
+    """Raise ValueError unless the in-pool slots of an append are distinct.
+
+    Page "Serving LLMs with vLLM", section "Growing During Decode": each new
+    token takes a slot of its own.  Two rows aimed at one slot would race in
+    the append kernel (whichever lands last wins), so the host refuses such a
+    step before anything is enqueued.  Negative slots and slots past the pool
+    are skipped rows and may repeat."""
+    s = np.asarray(slot_mapping, dtype=np.int64)
+    s = s[(s >= 0) & (s < int(num_slots))]
+    if s.size != np.unique(s).size:
+        vals, counts = np.unique(s, return_counts=True)
+        raise ValueError(f"slot_mapping names slot {int(vals[counts > 1][0])} more than once")
+
+
 # Gap between the K and the V pool when both come from one allocation.  Two
 # separate large allocations put block b's K and V slices at the same address
 # modulo 2 MiB, where they contend for the same HBM banks; starting V 4 KiB
@@ -68,6 +83,19 @@ def alloc_kv_pools(shape, dtype, device, fill=0):
 
 class DeviceStep:
     """Device buffers of one step plus the two ABI calls that run it."""
+
+    # buffers whose addresses the bound calls of step() hold: assigning any of
+    # them drops the bound calls, so the next step() converts the new addresses
+    _BOUND_BUFFERS = frozenset((
+        "k_pool", "v_pool", "k_scale", "v_scale", "block_tables", "context_lens", "query_lens",
+        "shared_blocks", "q", "out", "k_new", "v_new", "slot_mapping", "workspace", "ws_bytes",
+        "pool"))
+
+    def __setattr__(self, name, value):
+        if name in DeviceStep._BOUND_BUFFERS:
+            object.__setattr__(self, "_bound", None)
+            object.__setattr__(self, "_bound_key", None)
+        object.__setattr__(self, name, value)
 
     def __init__(self, wl: Workload, device: str = "cuda:0", upload_chunk_blocks: int = 8192):
         self.wl = wl
@@ -96,6 +124,7 @@ class DeviceStep:
         self.q = _bits_tensor(wl.q, self.device)
         self.out = torch.full_like(self.q, _poison_value(0x7FC0 if cfg.q_dtype == "bf16" else 0x7E00,
                                                          torch.int16))
+        check_slots_injective(wl.slot_mapping, cfg.num_blocks * cfg.block_size)
         self.k_new = _bits_tensor(wl.k_new, self.device)
         self.v_new = _bits_tensor(wl.v_new, self.device)
         self.slot_mapping = torch.from_numpy(wl.slot_mapping).to(self.device)
@@ -139,8 +168,7 @@ class DeviceStep:
 
     def step(self, stream=None) -> None:
         """append, then attend, with the two calls' arguments converted once per
-        stream (the buffers keep their addresses; after replacing one of the
-        buffer attributes, call rebind())."""
+        stream (replacing a buffer attribute drops the converted calls)."""
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
         key = int(s.cuda_stream) if not isinstance(s, int) else s
         if self._bound_key != key:

@@ -35,6 +35,7 @@ from typing import Dict, List, Optional
 import numpy as np
 
 from . import pagedkv as pk
+from .device import check_slots_injective
 
 
 @dataclasses.dataclass
@@ -292,11 +293,11 @@ class DeviceEngine:
 
     def __init__(self, batcher: ContinuousBatcher, num_q_heads: int, num_kv_heads: int,
                  head_dim: int, dtype: str = "bf16", seed: int = 0, device: str = "cuda:0",
-                 keep_host_mirror: bool = False, kv_from_tokens: bool = False,
+                 kv_from_tokens: bool = False,
                  kv_dtype: Optional[str] = None):
         """dtype: the query / new-row type (bf16 or f16).  kv_dtype: the pools'
         type, dtype (default) or "fp8_e4m3" (rows quantised on append with a
-        scale per (block, kv head); no host mirror)."""
+        scale per (block, kv head))."""
         import torch
         from .device import alloc_kv_pools
         self.torch = torch
@@ -307,8 +308,6 @@ class DeviceEngine:
         self.fp8 = self.kv_dtype == "fp8_e4m3"
         if self.kv_dtype not in (dtype, "fp8_e4m3"):
             raise ValueError(f"kv_dtype {self.kv_dtype} with rows of {dtype}")
-        if self.fp8 and keep_host_mirror:
-            raise ValueError("no host mirror of fp8 pools: read the pools back instead")
         self.dev = torch.device(device)
         nb, bs = batcher.bm.num_blocks, batcher.block_size
         tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
@@ -334,10 +333,6 @@ class DeviceEngine:
             self.kv_tables = (ek.view(torch.int16).numpy().view(np.uint16),
                               ev.view(torch.int16).numpy().view(np.uint16))
             self._ek, self._ev = ek.to(self.dev), ev.to(self.dev)
-        self.mirror = None
-        if keep_host_mirror:
-            self.mirror = (np.zeros((nb, num_kv_heads, bs, head_dim), np.uint16),
-                           np.zeros((nb, num_kv_heads, bs, head_dim), np.uint16))
         self.last = None
 
     def run(self, batch: StepBatch, stream=None):
@@ -365,6 +360,7 @@ class DeviceEngine:
             pairs = torch.from_numpy(np.ascontiguousarray(batch.copies)).to(self.dev)
             pk.paged_kv_copy_blocks(self.pool, self.k_pool, self.v_pool, self.k_scale,
                                     self.v_scale, pairs, len(batch.copies), stream)
+        check_slots_injective(batch.slot_mapping, self.b.bm.num_blocks * self.b.block_size)
         slots = torch.from_numpy(batch.slot_mapping).to(self.dev)
         if self.fp8:
             pk.paged_kv_append_quant(self.pool, self.k_pool, self.v_pool, self.k_scale,
@@ -386,15 +382,5 @@ class DeviceEngine:
                            self.k_scale, self.v_scale, tables, self.b.max_blocks, ctx, ql, S, rows,
                            max_ctx, max_q, self.scale, out, ws, ws_bytes, stream,
                            shared_blocks=shared)
-        if self.mirror is not None:
-            kb = k_new.view(torch.int16).cpu().numpy().view(np.uint16)
-            vb = v_new.view(torch.int16).cpu().numpy().view(np.uint16)
-            mk, mv = self.mirror
-            for src, dst in batch.copies:
-                mk[dst], mv[dst] = mk[src], mv[src]
-            bs = self.b.block_size
-            for r, sl in enumerate(batch.slot_mapping):
-                mk[sl // bs, :, sl % bs, :] = kb[r]
-                mv[sl // bs, :, sl % bs, :] = vb[r]
         self.last = (q, out, ws, k_new, v_new)
         return q, out

@@ -46,13 +46,19 @@ EXPORTS = ("paged_kv_append", "paged_attn_workspace_bytes", "paged_attn_step",
            "pkv_bm_blocks_needed", "pkv_bm_append", "pkv_bm_release", "pkv_bm_length",
            "pkv_bm_tables", "paged_kv_copy_blocks", "paged_kv_append_quant",
            "pkv_bm_enable_prefix_cache", "pkv_bm_add_prompt", "pkv_bm_extend_tokens",
-           "pkv_bm_cache_stats", "pkv_prefix_keys", "pkv_bm_shared_prefix")
+           "pkv_bm_cache_stats", "pkv_prefix_keys", "pkv_bm_shared_prefix",
+           "pkv_set_plan_override")
 
 
 class PkvPool(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32)]
+
+
+class PkvPlanOverride(ctypes.Structure):
+    _fields_ = [("part_tokens", ctypes.c_int32), ("chunk_part_tokens", ctypes.c_int32),
+                ("small_q", ctypes.c_int32), ("decode_on_mfma", ctypes.c_int32)]
 
 
 class PagedKVError(RuntimeError):
@@ -123,6 +129,8 @@ _lib.paged_kv_append_quant.argtypes = [_POOLP, _P, _P, _P, _P, _P, _P, _I, _P, _
 _lib.paged_kv_append_quant.restype = ctypes.c_int
 _lib.paged_kv_copy_blocks.argtypes = [_POOLP, _P, _P, _P, _P, _P, _I, _P]
 _lib.paged_kv_copy_blocks.restype = ctypes.c_int
+_lib.pkv_set_plan_override.argtypes = [ctypes.POINTER(PkvPlanOverride)]
+_lib.pkv_set_plan_override.restype = ctypes.c_int
 _lib.pkv_timing_enable.argtypes = [_I]
 _lib.pkv_timing_enable.restype = ctypes.c_int
 _lib.pkv_timing_disable.argtypes = []
@@ -191,10 +199,12 @@ def bind_paged_kv_append(pool: PkvPool, k_pool, v_pool, k_new, v_new, new_dtype:
     """paged_kv_append with its arguments converted once (tensor addresses read
     now): the returned callable issues the same call again.  For a caller that
     repeats one step on buffers that keep their addresses; it saves the
-    per-call argument conversion."""
+    per-call argument conversion.  The callable holds references to the objects
+    it was given, so their memory cannot be freed while it exists."""
     return _bound("paged_kv_append", _lib.paged_kv_append,
                   (_poolref(pool), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
-                   int(new_dtype), _ptr(slot_mapping), int(num_tokens), _stream(stream)))
+                   int(new_dtype), _ptr(slot_mapping), int(num_tokens), _stream(stream)),
+                  (pool, k_pool, v_pool, k_new, v_new, slot_mapping, stream))
 
 
 def bind_paged_attn_step(pool: PkvPool, q, q_dtype: int, num_q_heads: int, k_pool, v_pool,
@@ -209,16 +219,21 @@ def bind_paged_attn_step(pool: PkvPool, q, q_dtype: int, num_q_heads: int, k_poo
                    int(max_blocks_per_seq), _ptr(context_lens), _ptr(query_lens),
                    _ptr(shared_blocks), int(num_seqs), int(total_q_tokens), int(max_context_len),
                    int(max_query_len), float(scale), _ptr(out), _ptr(workspace),
-                   int(workspace_bytes), _stream(stream)))
+                   int(workspace_bytes), _stream(stream)),
+                  (pool, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens,
+                   query_lens, shared_blocks, out, workspace, stream))
 
 
-def _bound(name: str, fn, args):
+def _bound(name: str, fn, args, keep):
     # plain numbers become ctypes objects of the declared argument types up front
     conv = tuple(t(a) if isinstance(a, (int, float)) and not isinstance(a, bool) else a
                  for a, t in zip(args, fn.argtypes))
 
     def call() -> None:
         _check(name, fn(*conv))
+    # the buffers (and the pool struct and stream) whose addresses were taken
+    # stay allocated as long as the callable exists
+    call.keep = keep
     return call
 
 
@@ -241,6 +256,14 @@ def paged_attn_step(pool: PkvPool, q, q_dtype: int, num_q_heads: int, k_pool, v_
         _ptr(context_lens), _ptr(query_lens), _ptr(shared_blocks), int(num_seqs), int(total_q_tokens),
         int(max_context_len), int(max_query_len), float(scale), _ptr(out), _ptr(workspace),
         int(workspace_bytes), _stream(stream)))
+
+
+def pkv_set_plan_override(part_tokens: int = 0, chunk_part_tokens: int = 0, small_q: int = 0,
+                          decode_on_mfma: int = -1) -> None:
+    """Force parts of the launch plan (process-wide); the defaults restore the
+    library's own choices."""
+    o = PkvPlanOverride(int(part_tokens), int(chunk_part_tokens), int(small_q), int(decode_on_mfma))
+    _check("pkv_set_plan_override", _lib.pkv_set_plan_override(ctypes.byref(o)))
 
 
 def pkv_last_hip_error() -> int:

@@ -155,3 +155,27 @@ def test_bound_calls_convert_once_and_report_errors():
     with pytest.raises(pk.PagedKVError) as e:
         app()
     assert e.value.status == pk.PKV_ERR_DTYPE               # f16 rows into a bf16 pool
+
+
+def test_plan_override_is_validated_and_changes_the_layout():
+    big = pk.make_pool(16384, 16, 32, 128, "bf16")
+    default = pk.paged_attn_workspace_bytes(big, 64, 32, 64, 4096, 1)
+    try:
+        for bad in (dict(part_tokens=8), dict(part_tokens=4112), dict(part_tokens=24),
+                    dict(chunk_part_tokens=-16), dict(small_q=17), dict(small_q=-1),
+                    dict(decode_on_mfma=2), dict(decode_on_mfma=-2)):
+            with pytest.raises(pk.PagedKVError) as e:
+                pk.pkv_set_plan_override(**bad)
+            assert e.value.status == pk.PKV_ERR_SHAPE, bad
+        # a rejected override changed nothing
+        assert pk.paged_attn_workspace_bytes(big, 64, 32, 64, 4096, 1) == default
+        # 4096-token partitions: a 4096-token context is one partition, no partials
+        pk.pkv_set_plan_override(part_tokens=4096)
+        assert pk.paged_attn_workspace_bytes(big, 64, 32, 64, 4096, 1) == 0
+        # 16-token partitions: 256 of them per (row, head), (m, l) + 128 floats each
+        pk.pkv_set_plan_override(part_tokens=16)
+        n16 = pk.paged_attn_workspace_bytes(big, 64, 32, 64, 4096, 1)
+        assert n16 >= 64 * 32 * 256 * (2 + 128) * 4
+    finally:
+        pk.pkv_set_plan_override()
+    assert pk.paged_attn_workspace_bytes(big, 64, 32, 64, 4096, 1) == default

@@ -1,7 +1,8 @@
-"""The continuous-batching loop driving the kernels: every step's attention
-output equals the oracle computed on a host mirror of the pools (which the
-test keeps by replaying the step's copy-on-write copies and appended rows),
-and, with the prefix cache on, on K/V rebuilt from each sequence's tokens."""
+"""The continuous-batching loop driving the kernels: after every step the
+device pools equal, bit for bit, the pools the test rebuilds on the host from
+the step's copy-on-write copies and the oracle's append, and the step's
+attention output equals the oracle computed on those pools; with the prefix
+cache on, it equals the oracle on K/V rebuilt from each sequence's tokens."""
 import numpy as np
 import pytest
 import torch
@@ -31,7 +32,10 @@ def test_engine_steps_match_oracle(case):
     for i in range(3):                                 # samples sharing the parent's prompt
         b.submit(Request(rid, prompt=75, output=12, arrival=3, parent=parent, shared=37))
         rid += 1
-    eng = DeviceEngine(b, Hq, Hkv, D, "bf16", seed=3, keep_host_mirror=True)
+    eng = DeviceEngine(b, Hq, Hkv, D, "bf16", seed=3)
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    # the host's expected pools: the device pools start as zeros
+    mk, mv = np.zeros((nb, Hkv, 16, D), np.uint16), np.zeros((nb, Hkv, 16, D), np.uint16)
     steps = copies = preempts = 0
     worst = 0.0
     while not b.idle() and steps < 400:
@@ -44,9 +48,15 @@ def test_engine_steps_match_oracle(case):
             continue
         q, out = res
         torch.cuda.synchronize()
-        qb = q.view(torch.int16).cpu().numpy().view(np.uint16)
-        ob = oracle.decode_bits(out.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
-        mk, mv = eng.mirror
+        _, _, _, k_new, v_new = eng.last
+        for src, dst in batch.copies:                  # copy-on-write, then the append
+            mk[dst], mv[dst] = mk[src], mv[src]
+        mk = oracle.kv_append(mk, bits(k_new), batch.slot_mapping, 16)
+        mv = oracle.kv_append(mv, bits(v_new), batch.slot_mapping, 16)
+        assert np.array_equal(bits(eng.k_pool), mk), f"step {batch.step}: K pool differs"
+        assert np.array_equal(bits(eng.v_pool), mv), f"step {batch.step}: V pool differs"
+        qb = bits(q)
+        ob = oracle.decode_bits(bits(out), "bf16")
         ref = oracle.paged_attention(qb, mk, mv, batch.block_tables, batch.context_lens,
                                      batch.query_lens, eng.scale, 16, "bf16", "bf16")
         want = np.concatenate([ref[i] for i in range(len(batch.seq_ids))])

@@ -1,9 +1,12 @@
 """GPU parity: libpagedkv (through its C ABI) against the float64 CPU oracle.
 
-Small steps are compared element by element over every output; the five
+Small steps are compared element by element over every output.  The
 full-size step workloads (the launch configurations the benchmark times) are
-compared on sampled sequences the oracle computes one by one.  Appends are
-compared bit for bit over whole pools.
+compared on every sequence and head the oracle can compute in seconds: all
+of them for the 16-bit decode and mixed steps, every sequence at a query head
+of every kv head (and every head of the longest sequence) for the fp8
+grouped-query step, three heads of every prompt row for the prefill step.
+Appends are compared bit for bit over whole pools.
 """
 import os
 import sys
@@ -24,6 +27,14 @@ TOL = {W.F16: (2e-3, 1e-2), W.BF16: (2e-3, 1e-2), W.FP8: (5e-2, 0.0)}
 def _say(msg):
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+@pytest.fixture
+def plan():
+    """Sets the library's plan override for one test and restores the defaults after it."""
+    from paged_kv_cache_286_amd import pagedkv as pk
+    yield pk.pkv_set_plan_override
+    pk.pkv_set_plan_override()
 
 
 def _device_step(wl):
@@ -160,8 +171,8 @@ def test_random_steps_all_outputs(seed):
 
 
 @pytest.mark.parametrize("part_tokens", [16, 64, 256, 4096])
-def test_partition_sizes(part_tokens, monkeypatch):
-    monkeypatch.setenv("PKV_PART_TOKENS", str(part_tokens))
+def test_partition_sizes(part_tokens, plan):
+    plan(part_tokens=part_tokens)
     wl = _small(seed=7, **SMALL["mha_bf16_d128_ragged"])
     ds = _run(wl, f"mha_bf16 part_tokens={part_tokens}")
     _check(wl, ds)
@@ -172,17 +183,17 @@ def test_partition_sizes(part_tokens, monkeypatch):
 @pytest.mark.parametrize("path", ["0", "1"])
 @pytest.mark.parametrize("name", ["mha_bf16_d128_ragged", "gqa4_bf16_d128", "fp8_gqa8_bf16q_d128",
                                   "mha_f16_d64", "fp8_mha_f16q_d64", "gqa16_bf16_d128"])
-def test_decode_paths_forced(name, path, monkeypatch):
+def test_decode_paths_forced(name, path, plan):
     # "0": the VALU decode kernel, "1": the MFMA tile kernel, for the same inputs
-    monkeypatch.setenv("PKV_DECODE_MFMA", path)
+    plan(decode_on_mfma=int(path))
     wl = _small(seed=sorted(SMALL).index(name) + 300, **SMALL[name])
     _check(wl, _run(wl, f"{name} decode_mfma={path}"))
 
 
 @pytest.mark.parametrize("small_q", ["1", "2"])
-def test_multi_row_routing_forced(small_q, monkeypatch):
+def test_multi_row_routing_forced(small_q, plan):
     # sequences with <= small_q rows run as decode items, longer ones as chunk entries
-    monkeypatch.setenv("PKV_SMALL_Q", small_q)
+    plan(small_q=int(small_q))
     for name in ("specdec_mha_bf16_d128", "specdec_gqa4_fp8_d128", "chunk_bf16_d128"):
         wl = _small(seed=sorted(SMALL).index(name) + 500, **SMALL[name])
         _check(wl, _run(wl, f"{name} small_q={small_q}"))
@@ -200,11 +211,11 @@ def test_mixed_step_decode_verify_and_prefill_rows(kv):
 
 
 @pytest.mark.parametrize("chunk_pt", ["0", "64"])
-def test_uniform_prompt_steps(chunk_pt, monkeypatch):
+def test_uniform_prompt_steps(chunk_pt, plan):
     # every sequence a whole prompt (or one chunk) of the same length: the merge
     # launch is skipped only when no chunk row is split ("0": the library's own
     # partition; "64": forced splits, so partitions must be merged)
-    monkeypatch.setenv("PKV_CHUNK_PART_TOKENS", chunk_pt)
+    plan(chunk_part_tokens=int(chunk_pt))
     for lens, qlens in (([700, 700], [700, 700]), ([2560], [512]), ([300, 300, 300], [300, 300, 300])):
         cfg = W.Config("uni", "uni", 8, 8, 128, 16, 400, W.BF16, W.BF16, 17)
         wl = W.generate(W.custom_plan(cfg, lens, qlens, 17))
@@ -212,8 +223,8 @@ def test_uniform_prompt_steps(chunk_pt, monkeypatch):
 
 
 @pytest.mark.parametrize("chunk_pt", [64, 256, 1024])
-def test_chunk_partition_sizes(chunk_pt, monkeypatch):
-    monkeypatch.setenv("PKV_CHUNK_PART_TOKENS", str(chunk_pt))
+def test_chunk_partition_sizes(chunk_pt, plan):
+    plan(chunk_part_tokens=chunk_pt)
     for name in ("chunk_bf16_d128", "chunk_gqa4_fp8_d128", "chunk_f16_d64"):
         wl = _small(seed=sorted(SMALL).index(name) + 400, **SMALL[name])
         _check(wl, _run(wl, f"{name} chunk_part_tokens={chunk_pt}"))
@@ -403,10 +414,16 @@ def test_full_size_workload_sampled(name):
     wl = W.generate(W.make_plan(name))
     ds = _run(wl, name)
     _check_appended(wl, ds)
-    seqs = _sample_seqs(wl.plan)
+    p = wl.plan
+    seqs = list(range(p.num_seqs))          # every sequence of the step
     heads = None
     if name == "fp8_gqa_long":
-        heads = [0, 1, 7, 8, 31, 40, 63]
+        # every sequence at one query head in each of the 8 kv heads' groups
+        # (q head h reads kv head h // 8), then all 64 heads of the longest one
+        heads = [0, 9, 18, 27, 36, 45, 54, 63]
+        assert sorted({h // (p.cfg.num_q_heads // p.cfg.num_kv_heads) for h in heads}) == \
+            list(range(p.cfg.num_kv_heads))
+        _check(wl, ds, seqs=[int(np.argmax(p.context_lens))])
     if name == "prefill_chunks":            # every row of all four prompts, three heads
         heads = [0, 13, 31]
     _check(wl, ds, seqs=seqs, heads=heads)

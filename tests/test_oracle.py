@@ -292,6 +292,38 @@ def test_physical_relabelling_is_bit_identical(kv_dtype):
         assert np.array_equal(base[i], moved[i])
 
 
+@pytest.mark.parametrize("kv_dtype", [oracle.BF16, oracle.FP8])
+def test_head_subset_equals_the_full_call_at_gqa_8(kv_dtype):
+    # paged_attention(heads=H) computes only the listed query heads (the sampled
+    # full-size GPU checks use it).  At 16 query / 2 kv heads (8:1) each listed
+    # head must equal the same head of the full call bit for bit and the masked
+    # full-matrix brute force within 1e-12, and every other head stays NaN: a
+    # wrong head-to-kv-head mapping in the subset path (h % Hkv, h // Hkv, ...)
+    # reads the other kv head's K/V and fails.
+    from paged_kv_cache_286_amd import workloads as W
+    cfg = W.Config("t", "t", 16, 2, 16, 4, 64, kv_dtype, oracle.BF16, 41)
+    lens, qlens = [13, 5, 27, 9, 16], [1, 2, 4, 1, 16]
+    wl = W.generate(W.custom_plan(cfg, lens, qlens, 41))
+    p = wl.plan
+    full = _run_oracle(wl)
+    starts = np.concatenate([[0], np.cumsum(qlens)])
+    for heads in ([0], [7, 8], [15, 1, 9], [3, 12], list(range(16))):
+        sub = O.paged_attention(wl.q, wl.k.dense(), wl.v.dense(), p.block_tables, p.context_lens,
+                                p.query_lens, wl.scale, cfg.block_size, kv_dtype, oracle.BF16,
+                                wl.k_scale, wl.v_scale, heads=heads)
+        others = [h for h in range(16) if h not in heads]
+        for i in full:
+            assert np.array_equal(sub[i][:, heads], full[i][:, heads])
+            assert np.isnan(sub[i][:, others]).all()
+            K = O.sequence_kv(wl.k.dense(), wl.k_scale, p.block_tables[i], lens[i], 4, kv_dtype)
+            V = O.sequence_kv(wl.v.dense(), wl.v_scale, p.block_tables[i], lens[i], 4, kv_dtype)
+            q = oracle.decode_bits(wl.q[starts[i]:starts[i + 1]], oracle.BF16)
+            ref = _brute(q, K, V, float(np.float32(wl.scale)), 16)
+            np.testing.assert_allclose(sub[i][:, heads], ref[:, heads], rtol=0, atol=1e-12)
+    # the two kv heads hold different values, so the mapping is observable
+    assert not np.array_equal(full[2][:, 0], full[2][:, 8])
+
+
 def test_shared_prefix_blocks_equal_copied_blocks():
     wl = _bits_problem(22, shared=3)
     base = _run_oracle(wl)
