@@ -17,6 +17,7 @@ import glob
 import json
 import os
 import platform
+import statistics
 import sys
 import time
 
@@ -65,32 +66,84 @@ def attention_flops(plan):
     return 4 * D * H * pairs
 
 
-def cpu_baseline(wl, seconds):
-    """Time the CPU oracle on a bounded prefix of the step's sequences (single BLAS thread)."""
-    import numpy as np
+# The oracle as it stands, timed on the host's cores: the workload is generated
+# first, then a pool of worker processes is forked from this process before it
+# has touched the GPU (the workers inherit the arrays and only read them).
+_CPU_WL = None
+
+
+def _oracle_seqs(seqs):
+    """Worker: the oracle's attention for some sequences of the step (one BLAS thread)."""
     import oracle
-    from paged_kv_cache_286_amd import workloads as W
     from threadpoolctl import threadpool_limits
+    wl = _CPU_WL
+    p, cfg = wl.plan, wl.cfg
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.paged_attention(wl.q, wl.k, wl.v, p.block_tables, p.context_lens, p.query_lens,
+                               wl.scale, cfg.block_size, cfg.kv_dtype, cfg.q_dtype,
+                               wl.k_scale, wl.v_scale, seqs=seqs)
+        return time.perf_counter() - t0
+
+
+# The GPU box gives one GPU's job a share of 16 cores, whatever the machine has.
+CPU_POOL_CAP = 16
+
+
+def cpu_baseline(wl, seconds, single_seconds):
+    """Time the float64 oracle on the host: the whole step's attention spread over
+    N worker processes (N = usable cores, each with one BLAS thread), repeated
+    until about `seconds` of wall time have passed; plus, when single_seconds > 0,
+    one thread on a prefix of the step's sequences."""
+    import multiprocessing as mp
+    import numpy as np
+    from paged_kv_cache_286_amd import workloads as W
+    global _CPU_WL
+    _CPU_WL = wl
     p, cfg = wl.plan, wl.cfg
     per_tok = W.kv_bytes_per_token(cfg)
-    done, t_used, toks = [], 0.0, 0
-    with threadpool_limits(limits=1):
-        for i in range(p.num_seqs):
+    host_cores = len(os.sched_getaffinity(0))
+    n = max(1, min(host_cores, CPU_POOL_CAP, p.num_seqs))
+    # longest-first greedy split of the sequences over n workers, by attention work
+    work = p.context_lens.astype(np.int64) * p.query_lens.astype(np.int64)
+    groups, load = [[] for _ in range(n)], [0] * n
+    for i in np.argsort(-work, kind="stable").tolist():
+        k = load.index(min(load))
+        groups[k].append(i)
+        load[k] += int(work[i])
+    groups = [g for g in groups if g]
+    step_bytes = W.algorithmic_kv_bytes(p)["unique"]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(len(groups)) as pool:
+        pool.map(_oracle_seqs, [[g[0]] for g in groups])          # workers up, code paged in
+        rounds, wall = 0, 0.0
+        while rounds == 0 or wall < seconds:
             t0 = time.perf_counter()
-            oracle.paged_attention(wl.q, wl.k, wl.v, p.block_tables, p.context_lens, p.query_lens,
-                                   wl.scale, cfg.block_size, cfg.kv_dtype, cfg.q_dtype,
-                                   wl.k_scale, wl.v_scale, seqs=[i])
-            t_used += time.perf_counter() - t0
-            done.append(i)
+            pool.map(_oracle_seqs, groups, chunksize=1)
+            wall += time.perf_counter() - t0
+            rounds += 1
+    gbs = rounds * step_bytes / wall / 1e9
+    out = {"value": round(gbs, 4), "unit": "GB/s", "cores": len(groups), "kind": "oracle",
+           "sample": f"float64 numpy oracle: attention of the whole step ({p.num_seqs} sequences, "
+                     f"{step_bytes} algorithmic KV bytes) {rounds} time(s) in {wall:.1f} s "
+                     f"of wall time, sequences split over {len(groups)} worker processes with "
+                     f"one BLAS thread each, on {cpu_model()}",
+           "steps_per_s": round(rounds / wall, 4),
+           "host_cores": host_cores, "cpu_model": cpu_model()}
+    if single_seconds > 0:
+        done, t_used, toks = 0, 0.0, 0
+        for i in range(p.num_seqs):
+            t_used += _oracle_seqs([i])
+            done += 1
             toks += int(p.context_lens[i])
-            if t_used >= seconds:
+            if t_used >= single_seconds:
                 break
-    gbs = toks * per_tok / t_used / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 numpy oracle, attention of the first {len(done)} of {p.num_seqs} "
-                      f"sequences ({toks} context tokens, {toks * per_tok} KV bytes) in "
-                      f"{t_used:.1f} s on 1 thread of {cpu_model()}",
-            "host_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+        out["single_core"] = {
+            "value": round(toks * per_tok / t_used / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "sample": f"the first {done} of {p.num_seqs} sequences ({toks} context tokens) in "
+                      f"{t_used:.1f} s on one thread"}
+    _CPU_WL = None
+    return out
 
 
 def cpu_model():
@@ -130,7 +183,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_7b")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall time of the CPU oracle baseline on its worker pool")
+    ap.add_argument("--cpu-single-seconds", type=float, default=5.0,
+                    help="CPU time of the one-thread oracle figure (tiny and 7B decode steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the steps without per-kernel events")
@@ -145,13 +201,14 @@ def main():
         sys.exit(2)
 
     import torch
-    from paged_kv_cache_286_amd import pagedkv as pk          # raises if the library is not built
     from paged_kv_cache_286_amd import workloads as W
-    from paged_kv_cache_286_amd.device import DeviceStep
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
+    # The CPU leg forks worker processes.  torch's CPU thread pool (which the
+    # generator's bf16 / fp8 rounding would start) is not safe to fork: a child
+    # then blocked forever on a lock one of those threads held.  One intra-op
+    # thread keeps the pool from being created.
+    torch_threads = torch.get_num_threads()
+    torch.set_num_threads(1)
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
@@ -167,7 +224,22 @@ def main():
     wl = W.generate(W.make_plan(args.workload))
     p, cfg = wl.plan, wl.cfg
     alg = W.algorithmic_kv_bytes(p)
-    log(f"generated in {time.time() - t0:.1f} s; uploading")
+    log(f"generated in {time.time() - t0:.1f} s")
+    # the CPU leg forks its workers now, before this process initialises the GPU
+    cpu = None
+    if not args.no_cpu_baseline:
+        single = args.cpu_single_seconds if args.workload in ("tiny_decode", "decode_7b") else 0.0
+        log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s on the pool"
+            + (f", ~{single:.0f} s on one thread)" if single else ")"))
+        cpu = cpu_baseline(wl, args.cpu_seconds, single)
+    torch.set_num_threads(torch_threads)
+
+    from paged_kv_cache_286_amd import pagedkv as pk          # raises if the library is not built
+    from paged_kv_cache_286_amd.device import DeviceStep
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    log("uploading")
     ds = DeviceStep(wl, "cuda:0")
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -176,16 +248,22 @@ def main():
         ds.step(stream)
     torch.cuda.synchronize()
 
+    # K steps, each between a pair of events on the launch stream: the median
+    # of the K step times is the step time; the mean and the whole region's
+    # rate are reported beside it
     log(f"timing {args.steps} steps")
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        starts[i].record(stream)
         ds.step(stream)
-    stop.record(stream)
+        stops[i].record(stream)
     torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(stop) / args.steps
+    step_ms = sorted(a.elapsed_time(b) for a, b in zip(starts, stops))
+    ms_per_step = statistics.median(step_ms)
+    ms_mean = sum(step_ms) / len(step_ms)
+    ms_region = starts[0].elapsed_time(stops[-1]) / args.steps
 
     # Per-kernel durations: the same number of steps again, every library launch
     # bracketed by a pair of hipEvents on the launch stream.  Kept out of the
@@ -236,10 +314,6 @@ def main():
         roofline["mfma_busy"] = meas.get("mfma_busy_frac")
     # a device copy's read + write rate on the same GPU, for reference
     copy_gbs = copy_bandwidth(torch)
-    cpu = None
-    if not args.no_cpu_baseline:
-        log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(wl, args.cpu_seconds)
 
     line = {
         "metric": METRIC,
@@ -249,6 +323,11 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_stat": "median of the K steps, each between a pair of HIP events",
+        "ms_per_step_mean": round(ms_mean, 5),
+        "ms_per_step_p10_p90": [round(step_ms[len(step_ms) // 10], 5),
+                                round(step_ms[(9 * len(step_ms)) // 10], 5)],
+        "ms_per_step_region": round(ms_region, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
