@@ -36,7 +36,8 @@
  *   block ids in [0, num_blocks), context_lens[i] >= 1 and
  *   <= max_blocks_per_seq * block_size, 1 <= query_lens[i] <= context_lens[i],
  *   append slots distinct.  Kernels skip any address that would fall outside
- *   the pools (so a violation gives wrong numbers, not a memory fault).
+ *   the pools (so a violation gives wrong numbers, not a memory fault); the
+ *   checks build (below) records violations of the attention step's metadata.
  *   Calls are reentrant; calls that share output buffers on concurrent streams
  *   race.  The only process-wide settings are the plan override
  *   (pkv_set_plan_override) and kernel timing (pkv_timing_*), both meant for
@@ -203,6 +204,33 @@ typedef struct pkv_plan_override {
   int32_t decode_on_mfma;
 } pkv_plan_override;
 int pkv_set_plan_override(const pkv_plan_override* o);
+
+/* ---- checks build ----
+ * libpagedkv_checks.so is this library built with PKV_CHECKS: the same entry
+ * points and kernels, plus a validation kernel that paged_attn_step launches
+ * first.  It reads the step's device-resident metadata -- context_lens,
+ * query_lens and every block_tables entry a context reaches -- against the
+ * contract above ("Blocks and Block Tables": a table entry names a block of
+ * the pool; "Attention Over Scattered Blocks": a context fits its table and
+ * query rows sit at its end) and writes a record into the first
+ * PKV_CHECK_RECORD_BYTES bytes of the workspace (paged_attn_workspace_bytes
+ * counts them, so a workspace is always needed):
+ *   int32 [0] code (pkv_violation), [1] sequence, [2] table column (-1 for a
+ *   length), [3] offending value, [4] number of violations found.
+ * When several are found, which one is recorded is unspecified.  The step
+ * then runs as in the ordinary build (the attention kernels skip what the
+ * contract rules out, so other sequences' rows are unaffected).  The record is
+ * valid once the stream has passed the step.  pkv_checks_enabled() returns 1
+ * in the checks build and 0 in the ordinary one. */
+#define PKV_CHECK_RECORD_BYTES 20
+typedef enum pkv_violation {
+  PKV_VIOLATION_NONE = 0,
+  PKV_VIOLATION_BLOCK_ID = 1,      /* an entry within ceil(L/16) outside [0, num_blocks) */
+  PKV_VIOLATION_CONTEXT_LEN = 2,   /* L < 1, L > max_blocks_per_seq * 16 or L > max_context_len */
+  PKV_VIOLATION_QUERY_LEN = 3,     /* Q < 1, Q > L or Q > max_query_len */
+  PKV_VIOLATION_TOTAL_ROWS = 4     /* sum of query_lens != total_q_tokens (sequence -1) */
+} pkv_violation;
+int pkv_checks_enabled(void);
 
 /* pkv_status_string -- static text for a status code (never NULL). */
 const char* pkv_status_string(int status);

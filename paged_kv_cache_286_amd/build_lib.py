@@ -4,7 +4,9 @@
 
 Every ``csrc/*.hip`` (device and host) and ``csrc/*.cpp`` (host only) file is
 compiled by hipcc into ``_build/`` in parallel and the objects are linked into
-``libpagedkv.so``.  The build always runs
+``libpagedkv.so``; ``libpagedkv_checks.so`` links the same objects with
+``api.hip`` compiled again with ``PKV_CHECKS`` (contract checks of the attention
+step's metadata, for debugging).  The build always runs
 (no staleness check), so a changed source is always picked up.
 """
 from __future__ import annotations
@@ -20,6 +22,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpagedkv.so")
+# the same library with the contract checks of paged_attn_step compiled in
+CHECKS_LIB = os.path.join(HERE, "libpagedkv_checks.so")
+# the one source the checks build compiles differently
+CHECKS_SRC = "api.hip"
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -36,9 +42,11 @@ def hipcc() -> str:
     return path if os.path.exists(path) else (shutil.which("hipcc") or "hipcc")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(HERE, "..", "include"), "-c", src, "-o", obj]
+def _compile(src: str, checks: bool = False) -> str:
+    stem = os.path.splitext(os.path.basename(src))[0] + ("_checks" if checks else "")
+    obj = os.path.join(BUILD, stem + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, *(["-DPKV_CHECKS"] if checks else []),
+           "-I", os.path.join(HERE, "..", "include"), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
@@ -48,17 +56,23 @@ def _compile(src: str) -> str:
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    jobs = max(1, min(8, len(srcs), os.cpu_count() or 1))
+    checks_src = os.path.join(CSRC, CHECKS_SRC)
+    jobs = max(1, min(8, len(srcs) + 1, os.cpu_count() or 1))
     with cf.ThreadPoolExecutor(jobs) as ex:
+        fut_checks = ex.submit(_compile, checks_src, True)
         objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB} from {len(srcs)} sources", flush=True)
+        obj_checks = fut_checks.result()
+    for lib, lib_objs in ((LIB, objs),
+                          (CHECKS_LIB, [obj_checks if s == checks_src else o
+                                        for s, o in zip(srcs, objs)])):
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *lib_objs]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stderr}")
+        os.replace(tmp, lib)
+        if verbose:
+            print(f"built {lib} from {len(srcs)} sources", flush=True)
     return LIB
 
 

@@ -115,6 +115,14 @@ int32_t part_tokens_for(const pkv_pool* pool, int32_t rows, int32_t wg_per_row, 
   return pt;
 }
 
+// The checks build (compiled with PKV_CHECKS) keeps its violation record in the
+// first kCheckBytes of the workspace.
+#ifdef PKV_CHECKS
+constexpr size_t kCheckBytes = 256;
+#else
+constexpr size_t kCheckBytes = 0;
+#endif
+
 struct Layout {
   size_t q_start_off = 0, row_seq_off = 0, chunk_count_off = 0, chunk_entries_off = 0;
   size_t ml_off = 0, o_off = 0, total = 0;
@@ -186,7 +194,7 @@ Layout layout_for(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads, i
   // (the tiles per kv head of small-query sequences only add columns, not blocks)
   lay.part_tokens = part_tokens_for(pool, num_seqs, wg_per_row, max_ctx);
   lay.max_parts = (max_ctx + lay.part_tokens - 1) / lay.part_tokens;
-  size_t off = 0;
+  size_t off = kCheckBytes;
   if (max_q > 1) {
     lay.small_q = lay.decode_on_mfma ? small_q_for(group) : 1;
     lay.chunk_cols = pkv::chunk_entry_cols(pool->kv_dtype);
@@ -334,14 +342,14 @@ size_t paged_attn_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_
   return layout_for(pool, num_seqs, num_q_heads, total_q_tokens, max_context_len, max_query_len).total;
 }
 
-int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_t num_q_heads,
-                    const void* k_pool, const void* v_pool, const float* k_scale,
-                    const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                    const int32_t* context_lens, const int32_t* query_lens,
-                    const int32_t* shared_blocks, int32_t num_seqs,
-                    int32_t total_q_tokens, int32_t max_context_len, int32_t max_query_len,
-                    float scale, void* out, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_t num_q_heads,
+                     const void* k_pool, const void* v_pool, const float* k_scale,
+                     const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, const int32_t* query_lens,
+                     const int32_t* shared_blocks, int32_t num_seqs,
+                     int32_t total_q_tokens, int32_t max_context_len, int32_t max_query_len,
+                     float scale, void* out, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   int st = check_step_scalars(pool, q_dtype, num_q_heads, max_blocks_per_seq, num_seqs,
                               total_q_tokens, max_context_len, max_query_len);
   if (st != PKV_OK) return st;
@@ -408,6 +416,9 @@ int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_
   // decode-only steps pick the VALU or MFMA decode kernel.
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
+  if (kCheckBytes > 0)
+    e = pkv::launch_check(p, reinterpret_cast<int32_t*>(ws), max_context_len, max_query_len, s);
+  if (e != hipSuccess) return hip_status(e);
   if (multi) {
     e = timed_launch(PKV_KERNEL_PROLOGUE, s, [&] { return pkv::launch_prologue(p, s); });
     if (e == hipSuccess)
@@ -428,6 +439,22 @@ int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_
     e = timed_launch(PKV_KERNEL_REDUCE, s, [&] { return pkv::launch_reduce(p, plan, s); });
   return hip_status(e);
 }
+
+int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_t num_q_heads,
+                    const void* k_pool, const void* v_pool, const float* k_scale,
+                    const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, const int32_t* query_lens,
+                    const int32_t* shared_blocks, int32_t num_seqs,
+                    int32_t total_q_tokens, int32_t max_context_len, int32_t max_query_len,
+                    float scale, void* out, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return attn_step(pool, q, q_dtype, num_q_heads, k_pool, v_pool, k_scale, v_scale, block_tables,
+                   max_blocks_per_seq, context_lens, query_lens, shared_blocks, num_seqs,
+                   total_q_tokens, max_context_len, max_query_len, scale, out, workspace,
+                   workspace_bytes, stream);
+}
+
+int pkv_checks_enabled(void) { return kCheckBytes > 0 ? 1 : 0; }
 
 int pkv_set_plan_override(const pkv_plan_override* o) {
   PlanOverride& po = plan_override();

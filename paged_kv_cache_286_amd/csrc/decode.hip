@@ -176,8 +176,70 @@ __global__ __launch_bounds__(1024) void step_prologue_kernel(StepParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// contract checks (launched by the checks build only)
+// ---------------------------------------------------------------------------
+// The device-resident metadata of a step against the contract of
+// paged_attn_step (page "Serving LLMs with vLLM", sections "Blocks and Block
+// Tables" and "Attention Over Scattered Blocks": every table entry a context
+// reaches names a block of the pool; a context fits its table; query rows sit
+// at the end of their context).  One workgroup clears the record, then reads
+// every length and every table entry a context reaches; the first violation
+// it meets (in no particular order) is recorded with its sequence, index and
+// value, and all are counted.  It only reads metadata, never the pools.
+// rec: [0] code, [1] sequence, [2] index (table column; -1 for lengths),
+// [3] offending value, [4] number of violations.
+__global__ __launch_bounds__(1024) void step_check_kernel(StepParams p, int32_t* rec,
+                                                          int32_t max_ctx, int32_t max_q) {
+  __shared__ int32_t rows;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    rec[0] = kViolationNone;
+    rec[1] = -1;
+    rec[2] = -1;
+    rec[3] = 0;
+    rec[4] = 0;
+    rows = 0;
+  }
+  __syncthreads();
+  auto flag = [&](int code, int seq, int index, int value) {
+    atomicAdd(&rec[4], 1);
+    if (atomicCAS(&rec[0], kViolationNone, code) == kViolationNone) {
+      rec[1] = seq;
+      rec[2] = index;
+      rec[3] = value;
+    }
+  };
+  const int table_cap = p.max_blocks * 16;
+  for (int i = tid; i < p.num_seqs; i += blockDim.x) {
+    const int L = p.ctx_lens[i];
+    const int Q = p.q_lens[i];
+    atomicAdd(&rows, Q);
+    if (L < 1 || L > table_cap || L > max_ctx) flag(kViolationContextLen, i, -1, L);
+    else if (Q < 1 || Q > L || Q > max_q) flag(kViolationQueryLen, i, -1, Q);
+  }
+  const long long entries = (long long)p.num_seqs * p.max_blocks;
+  for (long long e = tid; e < entries; e += blockDim.x) {
+    const int i = (int)(e / p.max_blocks);
+    const int j = (int)(e - (long long)i * p.max_blocks);
+    const int L = p.ctx_lens[i];
+    if (L < 1 || L > table_cap || j >= (L + 15) / 16) continue;
+    const int b = p.tables[e];
+    if (b < 0 || b >= p.num_blocks) flag(kViolationBlockId, i, j, b);
+  }
+  __syncthreads();
+  if (tid == 0 && rows != p.total_q) flag(kViolationTotalRows, -1, -1, rows);
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+hipError_t launch_check(const StepParams& p, int32_t* record, int32_t max_ctx, int32_t max_q,
+                        hipStream_t stream) {
+  (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
+  hipLaunchKernelGGL(step_check_kernel, dim3(1), dim3(1024), 0, stream, p, record, max_ctx, max_q);
+  return hipGetLastError();
+}
+
 hipError_t launch_prologue(const StepParams& p, hipStream_t stream) {
   (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
   hipLaunchKernelGGL(step_prologue_kernel, dim3(1), dim3(1024), 0, stream, p);

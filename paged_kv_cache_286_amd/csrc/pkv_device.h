@@ -25,6 +25,13 @@ constexpr float kMaxSeed = -1.0e30f;
 // a score passes the reference by more than this.
 constexpr float kLazyRescale = 8.0f;
 
+// violation codes of the checks build (same values as pkv_violation)
+constexpr int kViolationNone = 0;
+constexpr int kViolationBlockId = 1;
+constexpr int kViolationContextLen = 2;
+constexpr int kViolationQueryLen = 3;
+constexpr int kViolationTotalRows = 4;
+
 // ---------------------------------------------------------------------------
 // parameters of one paged_attn_step, as the kernels see them
 // ---------------------------------------------------------------------------

@@ -37,6 +37,8 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_append_quant(const AppendArgs& a, int new_dtype, float* k_scale, float* v_scale,
                                const float* k_init, const float* v_init, hipStream_t stream);
 hipError_t launch_prologue(const StepParams& p, hipStream_t stream);
+hipError_t launch_check(const StepParams& p, int32_t* record, int32_t max_ctx, int32_t max_q,
+                        hipStream_t stream);
 hipError_t launch_decode(const StepParams& p, const StepPlan& plan, hipStream_t stream);
 hipError_t launch_decode_mfma(const StepParams& p, const StepPlan& plan, hipStream_t stream);
 hipError_t launch_step_mfma(const StepParams& p, const StepPlan& plan, hipStream_t stream);

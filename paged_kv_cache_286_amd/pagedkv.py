@@ -47,7 +47,7 @@ EXPORTS = ("paged_kv_append", "paged_attn_workspace_bytes", "paged_attn_step",
            "pkv_bm_tables", "paged_kv_copy_blocks", "paged_kv_append_quant",
            "pkv_bm_enable_prefix_cache", "pkv_bm_add_prompt", "pkv_bm_extend_tokens",
            "pkv_bm_cache_stats", "pkv_prefix_keys", "pkv_bm_shared_prefix",
-           "pkv_set_plan_override")
+           "pkv_set_plan_override", "pkv_checks_enabled")
 
 
 class PkvPool(ctypes.Structure):
@@ -74,71 +74,94 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _POOLP = ctypes.POINTER(PkvPool)
 
-_lib.paged_kv_append.argtypes = [_POOLP, _P, _P, _P, _P, _I, _P, _I, _P]
-_lib.paged_kv_append.restype = ctypes.c_int
-_lib.paged_attn_workspace_bytes.argtypes = [_POOLP, _I, _I, _I, _I, _I]
-_lib.paged_attn_workspace_bytes.restype = ctypes.c_size_t
-_lib.paged_attn_step.argtypes = [_POOLP, _P, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I,
-                                 _I, _I, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
-_lib.paged_attn_step.restype = ctypes.c_int
-_lib.pkv_status_string.argtypes = [ctypes.c_int]
-_lib.pkv_status_string.restype = ctypes.c_char_p
-_lib.pkv_kernel_name.argtypes = [_I]
-_lib.pkv_kernel_name.restype = ctypes.c_char_p
-_lib.pkv_last_hip_error.argtypes = []
-_lib.pkv_last_hip_error.restype = ctypes.c_int
-_lib.pkv_last_hip_error_string.argtypes = []
-_lib.pkv_last_hip_error_string.restype = ctypes.c_char_p
 _I64 = ctypes.c_int64
 _BM = ctypes.c_void_p
 _I32P = ctypes.POINTER(ctypes.c_int32)
 _I64P = ctypes.POINTER(ctypes.c_int64)
-_lib.pkv_bm_create.argtypes = [_I, _I]
-_lib.pkv_bm_create.restype = _BM
-_lib.pkv_bm_destroy.argtypes = [_BM]
-_lib.pkv_bm_destroy.restype = None
-_lib.pkv_bm_free_blocks.argtypes = [_BM]
-_lib.pkv_bm_free_blocks.restype = ctypes.c_int32
-_lib.pkv_bm_refcount.argtypes = [_BM, _I]
-_lib.pkv_bm_refcount.restype = ctypes.c_int32
-_lib.pkv_bm_add.argtypes = [_BM, _I64, _I64, _I]
-_lib.pkv_bm_add.restype = ctypes.c_int
-_lib.pkv_bm_blocks_needed.argtypes = [_BM, _I64P, _I32P, _I, _I32P]
-_lib.pkv_bm_blocks_needed.restype = ctypes.c_int
-_lib.pkv_bm_append.argtypes = [_BM, _I64P, _I32P, _I, _I32P, _I32P, _I, _I32P]
-_lib.pkv_bm_append.restype = ctypes.c_int
-_lib.pkv_bm_release.argtypes = [_BM, _I64]
-_lib.pkv_bm_release.restype = ctypes.c_int
-_lib.pkv_bm_length.argtypes = [_BM, _I64, _I32P]
-_lib.pkv_bm_length.restype = ctypes.c_int
-_lib.pkv_bm_tables.argtypes = [_BM, _I64P, _I, _I, _I32P, _I32P]
-_lib.pkv_bm_tables.restype = ctypes.c_int
-_lib.pkv_bm_shared_prefix.argtypes = [_BM, _I64P, _I, _I32P]
-_lib.pkv_bm_shared_prefix.restype = ctypes.c_int
-_lib.pkv_bm_enable_prefix_cache.argtypes = [_BM]
-_lib.pkv_bm_enable_prefix_cache.restype = ctypes.c_int
-_lib.pkv_bm_add_prompt.argtypes = [_BM, _I64, _I32P, _I, _I32P]
-_lib.pkv_bm_add_prompt.restype = ctypes.c_int
-_lib.pkv_bm_extend_tokens.argtypes = [_BM, _I64, _I32P, _I]
-_lib.pkv_bm_extend_tokens.restype = ctypes.c_int
-_lib.pkv_bm_cache_stats.argtypes = [_BM, ctypes.POINTER(ctypes.c_int64)]
-_lib.pkv_bm_cache_stats.restype = ctypes.c_int
-_lib.pkv_prefix_keys.argtypes = [_I32P, _I, _I, ctypes.POINTER(ctypes.c_uint64)]
-_lib.pkv_prefix_keys.restype = ctypes.c_int
-_lib.paged_kv_append_quant.argtypes = [_POOLP, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _P]
-_lib.paged_kv_append_quant.restype = ctypes.c_int
-_lib.paged_kv_copy_blocks.argtypes = [_POOLP, _P, _P, _P, _P, _P, _I, _P]
-_lib.paged_kv_copy_blocks.restype = ctypes.c_int
-_lib.pkv_set_plan_override.argtypes = [ctypes.POINTER(PkvPlanOverride)]
-_lib.pkv_set_plan_override.restype = ctypes.c_int
-_lib.pkv_timing_enable.argtypes = [_I]
-_lib.pkv_timing_enable.restype = ctypes.c_int
-_lib.pkv_timing_disable.argtypes = []
-_lib.pkv_timing_disable.restype = ctypes.c_int
-_lib.pkv_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int64)]
-_lib.pkv_timing_collect.restype = ctypes.c_int
-_lib.pkv_timing_get.argtypes = [_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
-_lib.pkv_timing_get.restype = ctypes.c_int
+
+
+def _declare(lib):
+    """Argument and result types of every exported function of a loaded library."""
+    lib.paged_kv_append.argtypes = [_POOLP, _P, _P, _P, _P, _I, _P, _I, _P]
+    lib.paged_kv_append.restype = ctypes.c_int
+    lib.paged_attn_workspace_bytes.argtypes = [_POOLP, _I, _I, _I, _I, _I]
+    lib.paged_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.paged_attn_step.argtypes = [_POOLP, _P, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I,
+                                     _I, _I, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+    lib.paged_attn_step.restype = ctypes.c_int
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_kernel_name.argtypes = [_I]
+    lib.pkv_kernel_name.restype = ctypes.c_char_p
+    lib.pkv_last_hip_error.argtypes = []
+    lib.pkv_last_hip_error.restype = ctypes.c_int
+    lib.pkv_last_hip_error_string.argtypes = []
+    lib.pkv_last_hip_error_string.restype = ctypes.c_char_p
+    lib.pkv_bm_create.argtypes = [_I, _I]
+    lib.pkv_bm_create.restype = _BM
+    lib.pkv_bm_destroy.argtypes = [_BM]
+    lib.pkv_bm_destroy.restype = None
+    lib.pkv_bm_free_blocks.argtypes = [_BM]
+    lib.pkv_bm_free_blocks.restype = ctypes.c_int32
+    lib.pkv_bm_refcount.argtypes = [_BM, _I]
+    lib.pkv_bm_refcount.restype = ctypes.c_int32
+    lib.pkv_bm_add.argtypes = [_BM, _I64, _I64, _I]
+    lib.pkv_bm_add.restype = ctypes.c_int
+    lib.pkv_bm_blocks_needed.argtypes = [_BM, _I64P, _I32P, _I, _I32P]
+    lib.pkv_bm_blocks_needed.restype = ctypes.c_int
+    lib.pkv_bm_append.argtypes = [_BM, _I64P, _I32P, _I, _I32P, _I32P, _I, _I32P]
+    lib.pkv_bm_append.restype = ctypes.c_int
+    lib.pkv_bm_release.argtypes = [_BM, _I64]
+    lib.pkv_bm_release.restype = ctypes.c_int
+    lib.pkv_bm_length.argtypes = [_BM, _I64, _I32P]
+    lib.pkv_bm_length.restype = ctypes.c_int
+    lib.pkv_bm_tables.argtypes = [_BM, _I64P, _I, _I, _I32P, _I32P]
+    lib.pkv_bm_tables.restype = ctypes.c_int
+    lib.pkv_bm_shared_prefix.argtypes = [_BM, _I64P, _I, _I32P]
+    lib.pkv_bm_shared_prefix.restype = ctypes.c_int
+    lib.pkv_bm_enable_prefix_cache.argtypes = [_BM]
+    lib.pkv_bm_enable_prefix_cache.restype = ctypes.c_int
+    lib.pkv_bm_add_prompt.argtypes = [_BM, _I64, _I32P, _I, _I32P]
+    lib.pkv_bm_add_prompt.restype = ctypes.c_int
+    lib.pkv_bm_extend_tokens.argtypes = [_BM, _I64, _I32P, _I]
+    lib.pkv_bm_extend_tokens.restype = ctypes.c_int
+    lib.pkv_bm_cache_stats.argtypes = [_BM, ctypes.POINTER(ctypes.c_int64)]
+    lib.pkv_bm_cache_stats.restype = ctypes.c_int
+    lib.pkv_prefix_keys.argtypes = [_I32P, _I, _I, ctypes.POINTER(ctypes.c_uint64)]
+    lib.pkv_prefix_keys.restype = ctypes.c_int
+    lib.paged_kv_append_quant.argtypes = [_POOLP, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _P]
+    lib.paged_kv_append_quant.restype = ctypes.c_int
+    lib.paged_kv_copy_blocks.argtypes = [_POOLP, _P, _P, _P, _P, _P, _I, _P]
+    lib.paged_kv_copy_blocks.restype = ctypes.c_int
+    lib.pkv_set_plan_override.argtypes = [ctypes.POINTER(PkvPlanOverride)]
+    lib.pkv_set_plan_override.restype = ctypes.c_int
+    lib.pkv_timing_enable.argtypes = [_I]
+    lib.pkv_timing_enable.restype = ctypes.c_int
+    lib.pkv_timing_disable.argtypes = []
+    lib.pkv_timing_disable.restype = ctypes.c_int
+    lib.pkv_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int64)]
+    lib.pkv_timing_collect.restype = ctypes.c_int
+    lib.pkv_timing_get.argtypes = [_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    lib.pkv_timing_get.restype = ctypes.c_int
+    lib.pkv_checks_enabled.argtypes = []
+    lib.pkv_checks_enabled.restype = ctypes.c_int
+    return lib
+
+
+_lib = _declare(_lib)
+CHECKS_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv_checks.so")
+_checks_lib = None
+
+
+def checks_library():
+    """libpagedkv_checks.so (the build with the attention step's contract
+    checks), loaded once; pass it as ``lib=`` to the calls below."""
+    global _checks_lib
+    if _checks_lib is None:
+        if not os.path.exists(CHECKS_LIB_PATH):
+            raise ImportError(f"{CHECKS_LIB_PATH} is not built")
+        _checks_lib = _declare(ctypes.CDLL(CHECKS_LIB_PATH))
+    return _checks_lib
 
 
 def _ptr(x) -> Optional[int]:
@@ -179,8 +202,8 @@ def pkv_kernel_name(kind: int) -> str:
 
 
 def paged_kv_append(pool: PkvPool, k_pool, v_pool, k_new, v_new, new_dtype: int,
-                    slot_mapping, num_tokens: int, stream=None) -> None:
-    _check("paged_kv_append", _lib.paged_kv_append(
+                    slot_mapping, num_tokens: int, stream=None, lib=None) -> None:
+    _check("paged_kv_append", (lib or _lib).paged_kv_append(
         _poolref(pool), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), int(new_dtype),
         _ptr(slot_mapping), int(num_tokens), _stream(stream)))
 
@@ -239,8 +262,8 @@ def _bound(name: str, fn, args, keep):
 
 def paged_attn_workspace_bytes(pool: PkvPool, num_seqs: int, num_q_heads: int,
                                total_q_tokens: int, max_context_len: int,
-                               max_query_len: int) -> int:
-    return int(_lib.paged_attn_workspace_bytes(_poolref(pool), int(num_seqs), int(num_q_heads),
+                               max_query_len: int, lib=None) -> int:
+    return int((lib or _lib).paged_attn_workspace_bytes(_poolref(pool), int(num_seqs), int(num_q_heads),
                                                int(total_q_tokens), int(max_context_len),
                                                int(max_query_len)))
 
@@ -249,8 +272,8 @@ def paged_attn_step(pool: PkvPool, q, q_dtype: int, num_q_heads: int, k_pool, v_
                     k_scale, v_scale, block_tables, max_blocks_per_seq: int, context_lens,
                     query_lens, num_seqs: int, total_q_tokens: int, max_context_len: int,
                     max_query_len: int, scale: float, out, workspace, workspace_bytes: int,
-                    stream=None, shared_blocks=None) -> None:
-    _check("paged_attn_step", _lib.paged_attn_step(
+                    stream=None, shared_blocks=None, lib=None) -> None:
+    _check("paged_attn_step", (lib or _lib).paged_attn_step(
         _poolref(pool), _ptr(q), int(q_dtype), int(num_q_heads), _ptr(k_pool), _ptr(v_pool),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), int(max_blocks_per_seq),
         _ptr(context_lens), _ptr(query_lens), _ptr(shared_blocks), int(num_seqs), int(total_q_tokens),
@@ -264,6 +287,10 @@ def pkv_set_plan_override(part_tokens: int = 0, chunk_part_tokens: int = 0, smal
     library's own choices."""
     o = PkvPlanOverride(int(part_tokens), int(chunk_part_tokens), int(small_q), int(decode_on_mfma))
     _check("pkv_set_plan_override", _lib.pkv_set_plan_override(ctypes.byref(o)))
+
+
+def pkv_checks_enabled(lib=None) -> bool:
+    return bool((lib or _lib).pkv_checks_enabled())
 
 
 def pkv_last_hip_error() -> int:

@@ -179,3 +179,21 @@ def test_plan_override_is_validated_and_changes_the_layout():
     finally:
         pk.pkv_set_plan_override()
     assert pk.paged_attn_workspace_bytes(big, 64, 32, 64, 4096, 1) == default
+
+
+def test_checks_build_exports_the_same_boundary_and_reserves_its_record():
+    lib = pk.checks_library()
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+    assert pk.pkv_checks_enabled(lib) and not pk.pkv_checks_enabled()
+    p = _pool()
+    # the record needs a workspace even where the ordinary build needs none
+    assert pk.paged_attn_workspace_bytes(p, 4, 4, 4, 100, 1) == 0
+    assert pk.paged_attn_workspace_bytes(p, 4, 4, 4, 100, 1, lib=lib) == 256
+    big = pk.make_pool(16384, 16, 32, 128, "bf16")
+    n = pk.paged_attn_workspace_bytes(big, 64, 32, 64, 4096, 1)
+    assert pk.paged_attn_workspace_bytes(big, 64, 32, 64, 4096, 1, lib=lib) == n + 256
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.paged_attn_step(p, FAKE, pk.PKV_BF16, 4, FAKE, FAKE, None, None, FAKE, 8, FAKE, FAKE, 4,
+                           4, 100, 1, 0.125, FAKE, None, 0, lib=lib)
+    assert e.value.status == pk.PKV_ERR_WORKSPACE
