@@ -67,7 +67,8 @@ typedef enum pkv_status {
   PKV_ERR_DTYPE = 3,        /* dtype code unknown or combination not allowed */
   PKV_ERR_WORKSPACE = 4,    /* workspace missing or smaller than paged_attn_workspace_bytes */
   PKV_ERR_UNSUPPORTED = 5,  /* valid request this build has no kernel for */
-  PKV_ERR_HIP = 6           /* the HIP runtime refused a launch */
+  PKV_ERR_HIP = 6,          /* the HIP runtime refused a launch */
+  PKV_ERR_SCRATCH = 7       /* paged_attn_step_noalloc: the step needs more than its scratch */
 } pkv_status;
 
 /* Shape of one layer's K and V pools (host struct).
@@ -231,6 +232,32 @@ typedef enum pkv_violation {
   PKV_VIOLATION_TOTAL_ROWS = 4     /* sum of query_lens != total_q_tokens (sequence -1) */
 } pkv_violation;
 int pkv_checks_enabled(void);
+
+/* paged_attn_step_noalloc -- paged_attn_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments, kernels and results, but no
+ * workspace argument.  The workspace lives in a device array inside the
+ * library, paged_attn_scratch_bytes() (64 MiB) long, of which every device the
+ * library runs on holds one copy until the process ends; the call itself
+ * allocates nothing.  A step whose paged_attn_workspace_bytes exceeds it
+ * returns PKV_ERR_SCRATCH before anything is enqueued.  Every call on a device
+ * shares that device's array and nothing in it needs to start at zero, so
+ * calls on one device whose executions overlap (different streams, or
+ * different host threads) race and give wrong results: serialise them (one
+ * stream) or use paged_attn_step with a workspace per stream. */
+int paged_attn_step_noalloc(const pkv_pool* pool,
+                            const void* q, int32_t q_dtype, int32_t num_q_heads,
+                            const void* k_pool, const void* v_pool,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, const int32_t* query_lens,
+                            const int32_t* shared_blocks,
+                            int32_t num_seqs, int32_t total_q_tokens,
+                            int32_t max_context_len, int32_t max_query_len,
+                            float scale, void* out, void* stream);
+
+/* paged_attn_scratch_bytes -- size of paged_attn_step_noalloc's device scratch. */
+size_t paged_attn_scratch_bytes(void);
 
 /* pkv_status_string -- static text for a status code (never NULL). */
 const char* pkv_status_string(int status);

@@ -242,6 +242,48 @@ int check_step_scalars(const pkv_pool* pool, int32_t q_dtype, int32_t num_q_head
   return PKV_OK;
 }
 
+// ---------------------------------------------------------------------------
+// the no-allocation entry point's workspace
+// ---------------------------------------------------------------------------
+// paged_attn_step_noalloc keeps its workspace in this array: each device the
+// library runs on holds its own copy from the moment the library's code is
+// loaded on it until the process ends.  In host code `scratch` only names the
+// symbol; its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// ever handed to kernels.  64 MiB covers every decode and mixed step of the
+// 7B shape here (a 640-row mixed step needs 41 MiB).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchAddresses {
+  std::mutex mu;
+  void* ptr[kMaxDevices] = {};
+};
+ScratchAddresses& scratch_addresses() {
+  static ScratchAddresses a;
+  return a;
+}
+
+// this device's scratch address, looked up on the first call on the device
+int device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return PKV_ERR_UNSUPPORTED;
+  ScratchAddresses& a = scratch_addresses();
+  std::lock_guard<std::mutex> g(a.mu);
+  if (a.ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr) return hip_status(hipErrorInvalidSymbol);
+    a.ptr[dev] = p;
+  }
+  *out = a.ptr[dev];
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -255,6 +297,8 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_UNSUPPORTED: return "no kernel for this shape in this build";
     case PKV_ERR_HIP: return "the HIP runtime refused a launch";
+    case PKV_ERR_SCRATCH:
+      return "the step needs more workspace than paged_attn_step_noalloc's device scratch holds";
     default: return "unknown status";
   }
 }
@@ -342,6 +386,8 @@ size_t paged_attn_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_
   return layout_for(pool, num_seqs, num_q_heads, total_q_tokens, max_context_len, max_query_len).total;
 }
 
+// paged_attn_step and paged_attn_step_noalloc: the second takes its workspace
+// from this device's scratch array instead of the caller's.
 static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_t num_q_heads,
                      const void* k_pool, const void* v_pool, const float* k_scale,
                      const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -349,7 +395,7 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
                      const int32_t* shared_blocks, int32_t num_seqs,
                      int32_t total_q_tokens, int32_t max_context_len, int32_t max_query_len,
                      float scale, void* out, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+                     bool use_scratch, void* stream) {
   int st = check_step_scalars(pool, q_dtype, num_q_heads, max_blocks_per_seq, num_seqs,
                               total_q_tokens, max_context_len, max_query_len);
   if (st != PKV_OK) return st;
@@ -361,6 +407,12 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
 
   const Layout lay = layout_for(pool, num_seqs, num_q_heads, total_q_tokens, max_context_len,
                                 max_query_len);
+  if (use_scratch) {
+    if (lay.total > kScratchBytes) return PKV_ERR_SCRATCH;
+    st = device_scratch(&workspace);
+    if (st != PKV_OK) return st;
+    workspace_bytes = kScratchBytes;
+  }
   if (lay.total > 0 && (workspace == nullptr || workspace_bytes < lay.total)) return PKV_ERR_WORKSPACE;
 
   StepPlan plan;
@@ -451,8 +503,24 @@ int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_
   return attn_step(pool, q, q_dtype, num_q_heads, k_pool, v_pool, k_scale, v_scale, block_tables,
                    max_blocks_per_seq, context_lens, query_lens, shared_blocks, num_seqs,
                    total_q_tokens, max_context_len, max_query_len, scale, out, workspace,
-                   workspace_bytes, stream);
+                   workspace_bytes, false, stream);
 }
+
+int paged_attn_step_noalloc(const pkv_pool* pool, const void* q, int32_t q_dtype,
+                            int32_t num_q_heads, const void* k_pool, const void* v_pool,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, const int32_t* query_lens,
+                            const int32_t* shared_blocks, int32_t num_seqs,
+                            int32_t total_q_tokens, int32_t max_context_len,
+                            int32_t max_query_len, float scale, void* out, void* stream) {
+  return attn_step(pool, q, q_dtype, num_q_heads, k_pool, v_pool, k_scale, v_scale, block_tables,
+                   max_blocks_per_seq, context_lens, query_lens, shared_blocks, num_seqs,
+                   total_q_tokens, max_context_len, max_query_len, scale, out, nullptr, 0, true,
+                   stream);
+}
+
+size_t paged_attn_scratch_bytes(void) { return kScratchBytes; }
 
 int pkv_checks_enabled(void) { return kCheckBytes > 0 ? 1 : 0; }
 

@@ -33,7 +33,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 DTYPE_CODES = {"f16": PKV_F16, "bf16": PKV_BF16, "fp8_e4m3": PKV_FP8_E4M3}
 (PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_WORKSPACE,
- PKV_ERR_UNSUPPORTED, PKV_ERR_HIP) = range(7)
+ PKV_ERR_UNSUPPORTED, PKV_ERR_HIP, PKV_ERR_SCRATCH) = range(8)
 (PKV_KERNEL_APPEND, PKV_KERNEL_PROLOGUE, PKV_KERNEL_DECODE, PKV_KERNEL_REDUCE,
  PKV_KERNEL_STEP_MFMA, PKV_KERNEL_DECODE_MFMA, PKV_KERNEL_KINDS) = range(7)
 
@@ -47,7 +47,8 @@ EXPORTS = ("paged_kv_append", "paged_attn_workspace_bytes", "paged_attn_step",
            "pkv_bm_tables", "paged_kv_copy_blocks", "paged_kv_append_quant",
            "pkv_bm_enable_prefix_cache", "pkv_bm_add_prompt", "pkv_bm_extend_tokens",
            "pkv_bm_cache_stats", "pkv_prefix_keys", "pkv_bm_shared_prefix",
-           "pkv_set_plan_override", "pkv_checks_enabled")
+           "pkv_set_plan_override", "pkv_checks_enabled", "paged_attn_step_noalloc",
+           "paged_attn_scratch_bytes")
 
 
 class PkvPool(ctypes.Structure):
@@ -143,6 +144,11 @@ def _declare(lib):
     lib.pkv_timing_collect.restype = ctypes.c_int
     lib.pkv_timing_get.argtypes = [_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     lib.pkv_timing_get.restype = ctypes.c_int
+    lib.paged_attn_step_noalloc.argtypes = [_POOLP, _P, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P,
+                                            _I, _I, _I, _I, ctypes.c_float, _P, _P]
+    lib.paged_attn_step_noalloc.restype = ctypes.c_int
+    lib.paged_attn_scratch_bytes.argtypes = []
+    lib.paged_attn_scratch_bytes.restype = ctypes.c_size_t
     lib.pkv_checks_enabled.argtypes = []
     lib.pkv_checks_enabled.restype = ctypes.c_int
     return lib
@@ -287,6 +293,22 @@ def pkv_set_plan_override(part_tokens: int = 0, chunk_part_tokens: int = 0, smal
     library's own choices."""
     o = PkvPlanOverride(int(part_tokens), int(chunk_part_tokens), int(small_q), int(decode_on_mfma))
     _check("pkv_set_plan_override", _lib.pkv_set_plan_override(ctypes.byref(o)))
+
+
+def paged_attn_step_noalloc(pool: PkvPool, q, q_dtype: int, num_q_heads: int, k_pool, v_pool,
+                            k_scale, v_scale, block_tables, max_blocks_per_seq: int, context_lens,
+                            query_lens, num_seqs: int, total_q_tokens: int, max_context_len: int,
+                            max_query_len: int, scale: float, out, stream=None,
+                            shared_blocks=None, lib=None) -> None:
+    _check("paged_attn_step_noalloc", (lib or _lib).paged_attn_step_noalloc(
+        _poolref(pool), _ptr(q), int(q_dtype), int(num_q_heads), _ptr(k_pool), _ptr(v_pool),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), int(max_blocks_per_seq),
+        _ptr(context_lens), _ptr(query_lens), _ptr(shared_blocks), int(num_seqs), int(total_q_tokens),
+        int(max_context_len), int(max_query_len), float(scale), _ptr(out), _stream(stream)))
+
+
+def paged_attn_scratch_bytes(lib=None) -> int:
+    return int((lib or _lib).paged_attn_scratch_bytes())
 
 
 def pkv_checks_enabled(lib=None) -> bool:

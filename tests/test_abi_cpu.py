@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert pk.pkv_status_string(0) == "ok"
-    for s in range(1, 7):
+    for s in range(1, 8):
         assert pk.pkv_status_string(s) not in ("ok", "unknown status")
     assert pk.pkv_status_string(99) == "unknown status"
     assert pk.pkv_kernel_name(pk.PKV_KERNEL_DECODE).startswith("decode")
