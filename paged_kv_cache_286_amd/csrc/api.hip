@@ -238,7 +238,8 @@ int check_step_scalars(const pkv_pool* pool, int32_t q_dtype, int32_t num_q_head
   if ((int64_t)max_ctx > (int64_t)max_blocks * pool->block_size) return PKV_ERR_SHAPE;
   if (num_seqs > 0 && max_q == 1 && total_q != num_seqs) return PKV_ERR_SHAPE;
   if (num_seqs > 0 && max_q > 1 && (int64_t)total_q < (int64_t)num_seqs + max_q - 1) return PKV_ERR_SHAPE;
-  if (total_q > 65535) return PKV_ERR_UNSUPPORTED;   // grid y limit of the decode kernel
+  // one-dimensional grids of (head group, row) and (head group, sequence) workgroups
+  if ((int64_t)total_q * num_q_heads > INT32_MAX) return PKV_ERR_UNSUPPORTED;
   return PKV_OK;
 }
 

@@ -9,10 +9,11 @@
 // sequence sits in block table[t / 16] at offset t % 16.
 //
 // Work decomposition (one workgroup = NW wave64s):
-//   grid.x  group of `GB` query heads that share one kv head,
-//   grid.y  sequence (only sequences with one query row; prefill chunks go to
-//           the MFMA chunk kernel),
-//   grid.z  split-context partition of part_tokens tokens.
+//   grid.x  group of `GB` query heads that share one kv head (fastest), then
+//           sequence (only sequences with one query row; prefill chunks go to
+//           the MFMA chunk kernel) -- one dimension, so the sequence count is
+//           not held to grid.y's 65,535,
+//   grid.y  split-context partition of part_tokens tokens.
 // The hardware deals workgroups to the 8 XCDs round-robin by linear id, so the
 // fastest grid dimension must not be one along which the work per workgroup
 // changes: heads (equal work) go first and partitions (the last ones are often
@@ -36,7 +37,9 @@ namespace pkv {
 
 template <int KV, int QT, int D, int GB>
 __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) {
-  decode_valu_wg<KV, QT, D, GB>(p, blockIdx.x, blockIdx.y, blockIdx.z);
+  const int nx = p.num_q_heads / GB;
+  const int seq = blockIdx.x / nx;
+  decode_valu_wg<KV, QT, D, GB>(p, blockIdx.x - seq * nx, seq, blockIdx.y);
 }
 
 // Merge the partitions of every (row, query head) whose context was split.
@@ -45,13 +48,14 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) 
 // takes HPW heads of one row, one wave each: in steps with prefill chunks,
 // whose rows mostly have nothing to merge, kMultiReduceHeads per workgroup cut
 // the workgroups that only check and leave; decode steps keep one head per
-// workgroup.
+// workgroup.  grid.x = head group (fastest), then row.
 constexpr int kMultiReduceHeads = 4;
 template <int QT, int D, int HPW>
 __global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
-  const int h = blockIdx.x * HPW + (HPW > 1 ? (int)(threadIdx.x >> 6) : 0);
+  const int ng = (p.num_q_heads + HPW - 1) / HPW;
+  const int row = blockIdx.x / ng;
+  const int h = (blockIdx.x - row * ng) * HPW + (HPW > 1 ? (int)(threadIdx.x >> 6) : 0);
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.y;
   if (h >= p.num_q_heads) return;
   int L, pt;
   if (p.row_seq != nullptr) {
@@ -248,8 +252,7 @@ hipError_t launch_prologue(const StepParams& p, hipStream_t stream) {
 
 template <int KV, int QT, int D>
 static hipError_t decode_by_group(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
-  const dim3 grid((uint32_t)(p.num_q_heads / plan.heads_per_wg), (uint32_t)p.num_seqs,
-                  (uint32_t)p.max_parts);
+  const dim3 grid((uint32_t)(p.num_q_heads / plan.heads_per_wg * p.num_seqs), (uint32_t)p.max_parts);
   const dim3 block(kWaves * 64);
   (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
   switch (plan.heads_per_wg) {
@@ -305,10 +308,10 @@ hipError_t launch_reduce(const StepParams& p, const StepPlan& plan, hipStream_t 
   (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
   if (p.row_seq != nullptr) {
     constexpr int H = kMultiReduceHeads;
-    const dim3 grid((uint32_t)((p.num_q_heads + H - 1) / H), (uint32_t)p.total_q);
+    const dim3 grid((uint32_t)((p.num_q_heads + H - 1) / H * p.total_q));
     reduce_typed<H>(p, plan, grid, stream);
   } else {
-    reduce_typed<1>(p, plan, dim3((uint32_t)p.num_q_heads, (uint32_t)p.total_q), stream);
+    reduce_typed<1>(p, plan, dim3((uint32_t)(p.num_q_heads * p.total_q)), stream);
   }
   return hipGetLastError();
 }

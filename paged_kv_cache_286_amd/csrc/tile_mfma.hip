@@ -952,7 +952,8 @@ __device__ __forceinline__ void chunk_wgs(const StepParams& p, int wg, int nwg, 
   }
 }
 
-// Decode rows only: grid (kv head x column tiles, sequence, partition).
+// Decode rows only: grid.x = kv head x column tile (fastest), then sequence;
+// grid.y = partition.
 template <int KV, int QT, int D>
 __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(StepParams p) {
   __shared__ float sm_o[2 * 16 * D];
@@ -961,7 +962,9 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
   // each wave's K regrouping area: two blocks' K slices
   __shared__ uint4 sm_k[kTileWaves * 2 * TileLay<KV, D>::BLKB / 16];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  decode_wg<KV, QT, D>(p, blockIdx.x, blockIdx.y, blockIdx.z, sm_o, sm_m, sm_l,
+  const int nx = p.num_kv_heads * ((p.small_q * (p.num_q_heads / p.num_kv_heads) + 15) / 16);
+  const int seq = blockIdx.x / nx;
+  decode_wg<KV, QT, D>(p, blockIdx.x - seq * nx, seq, blockIdx.y, sm_o, sm_m, sm_l,
                        sm_k + wave * 2 * TileLay<KV, D>::BLKB / 16);
 }
 
@@ -1062,7 +1065,7 @@ static hipError_t launch_tile_typed(bool step, int vgb, const StepParams& p, con
 
 hipError_t launch_decode_mfma(const StepParams& p, const StepPlan& plan, hipStream_t stream) {
   const int tiles = (p.small_q * plan.group + 15) / 16;
-  const dim3 grid((uint32_t)(p.num_kv_heads * tiles), (uint32_t)p.num_seqs, (uint32_t)p.max_parts);
+  const dim3 grid((uint32_t)(p.num_kv_heads * tiles * p.num_seqs), (uint32_t)p.max_parts);
   return launch_tile_typed(false, 0, p, plan, grid, 0, 0, 0, stream);
 }
 

@@ -514,3 +514,35 @@ def test_repeated_steps_bit_identical():
         ds.step()
         torch.cuda.synchronize()
         assert torch.equal(ds.out, first), f"run {r + 2} differs from the first"
+
+
+def test_more_rows_than_a_grid_y_dimension_holds(plan):
+    # Rows and sequences sit in one-dimensional grids: 70,000 decode sequences
+    # (16-token partitions forced, so the merge kernel runs over all of them)
+    # and one 66,000-row prompt, both past 65,535.
+    rng = np.random.default_rng(5)
+    lens = rng.integers(1, 49, 70000).tolist()
+    wl = _small(Hq=1, Hkv=1, D=64, kv=W.F16, qd=W.F16, lens=lens, seed=81, extra_blocks=9)
+    plan(part_tokens=16)
+    ds = _run(wl, "70,000 decode sequences, 16-token partitions")
+    p = wl.plan
+    assert p.num_seqs > 65535
+    seqs = sorted({0, 1, 65534, 65535, 65536, 69999} | set(rng.integers(0, 70000, 40).tolist()))
+    _check(wl, ds, seqs=seqs)
+    out = oracle.decode_bits(ds.out_bits(), W.F16)
+    assert np.isfinite(out).all()
+    plan()
+    cfg = W.Config("rows", "rows", 1, 1, 64, 16, 66000 // 16 + 9, W.BF16, W.BF16, 82)
+    wl = W.generate(W.custom_plan(cfg, [66000], [66000], 82))
+    ds = _run(wl, "one 66,000-row prompt")
+    got = oracle.decode_bits(ds.out_bits(), W.BF16)
+    assert np.isfinite(got).all()
+    # row r of the prompt sees keys 0..r: the oracle's decode over the first r + 1 tokens
+    rows = sorted({0, 15, 16, 4095, 4096, 65534, 65535, 65536, 65999} |
+                  set(rng.integers(0, 66000, 24).tolist()))
+    t = wl.plan.block_tables
+    for r in rows:
+        ref = oracle.paged_attention(wl.q[r:r + 1], wl.k, wl.v, t, np.array([r + 1]), np.array([1]),
+                                     wl.scale, 16, W.BF16, W.BF16)[0]
+        ok = oracle.tolerance_ok(got[r:r + 1], ref, *TOL[W.BF16])
+        assert ok.all(), f"row {r}: {(~ok).sum()} elements out of tolerance"
