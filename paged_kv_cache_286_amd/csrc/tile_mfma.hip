@@ -57,6 +57,44 @@ __device__ __forceinline__ f32x4 mfma32(uint4 a, uint4 b, f32x4 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// D[16x16] += A[16x128] B[128x16] on fp8 E4M3 bytes: lane l holds 32 bytes of
+// row l%16 of A and of column l%16 of B, with the same contraction indices in
+// the same byte positions for A and B (so any consistent assignment of head
+// dims to (lane group, byte) gives the dot product); D as in mfma32.  The
+// E8M0 block scales are 127, i.e. 1.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma_fp8_128(uint4 a0, uint4 a1, uint4 b0, uint4 b1, f32x4 c) {
+  const i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const i32x8 b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// four floats -> four E4M3 bytes (round to nearest even), a in the lowest byte
+__device__ __forceinline__ uint32_t f32x4_to_fp8x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// Query values as two fp8 operands whose sum is the value times 2^s: x (already
+// scaled) -> hi = fp8(x), lo = fp8(x - hi).  A 16-bit float has at most 8
+// significant bits and hi keeps the top 4 (rounded), so x - hi is an exact
+// float32 with at most 4 significant bits and lo = x - hi exactly, unless it
+// falls below the fp8 normal range (|x - hi| < 2^-6; s puts the column's
+// largest |x| in [128, 256), so only parts more than 2^13 below it lose bits).
+__device__ __forceinline__ void split_fp8(const float (&x)[16], uint4& hi, uint4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = f32x4_to_fp8x4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+    const auto b01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h[i], false);
+    const auto b23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h[i], true);
+    l[i] = f32x4_to_fp8x4(x[4 * i] - b01[0], x[4 * i + 1] - b01[1], x[4 * i + 2] - b23[0],
+                          x[4 * i + 3] - b23[1]);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
 // two fp8 bytes (low or high half of w) -> two 16-bit values of type QT, packed
 template <int QT, bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_16(uint32_t w) {
@@ -107,6 +145,9 @@ struct TileLay {
   static constexpr int ROWB = D * ELT;          // bytes of a token row of one head
   static constexpr int BLKB = 16 * ROWB;        // bytes of one (block, head)
   static constexpr int KSTEPS = D / 32;         // 16x16x32 MFMA steps of the score product
+  // fp8 K at head_dim 128: scores on the fp8 16x16x128 MFMA straight from the
+  // stored bytes (the query split into two fp8 parts), no K conversions
+  static constexpr bool F8MMA = KV == kFP8 && D == 128;
   static constexpr int KB = D / 4 * ELT;        // K bytes per lane per block (D/4 dims)
   static constexpr int KLD = KB / 16;           // 16-byte chunks of K per lane
   // K chunk c of lane group gq holds bytes c*64 + gq*16 of its token row;
@@ -259,13 +300,53 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   // Q^T operand of score step st: the 8 dims of this column's query that the
   // K operand of the same step holds (zero for unused columns)
   uint4 qb[TPW][L::KSTEPS];
+  // F8MMA: the fp8 operands (hi, lo) of q * 2^s[t] over the dims the lane's K
+  // chunks hold (16gq .. 16gq+15 and 64+16gq .. +15), and qs[t] = 2^-s[t],
+  // which scales the scores back; s[t] puts the column's largest |q| in
+  // [128, 256), inside the fp8 range.  qs is 1 on the other paths.
+  uint4 qh[TPW][2], ql[TPW][2];
+  float qs[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const uint16_t* qrow =
         reinterpret_cast<const uint16_t*>(p.q) + ((size_t)row[t] * p.num_q_heads + head[t]) * D;
+    qs[t] = 1.f;
+    if constexpr (L::F8MMA) {
+      float x[2][16];
 #pragma unroll
-    for (int st = 0; st < L::KSTEPS; ++st)
-      qb[t][st] = col_ok[t] ? *reinterpret_cast<const uint4*>(qrow + L::k_dim(st, gq)) : make_uint4(0, 0, 0, 0);
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+          const uint4 raw = col_ok[t] ? *reinterpret_cast<const uint4*>(qrow + 64 * c + 16 * gq + 8 * h8)
+                                      : make_uint4(0, 0, 0, 0);
+          float f[8];
+          if constexpr (QT == kBF16) unpack16<kBF16>(raw, f);
+          else unpack16<kF16>(raw, f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[c][8 * h8 + e] = f[e];
+        }
+      float amax = 0.f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[c][e]));
+      amax = max_xor32(max_xor16(amax));            // the column's 4 lane groups
+      int ex;
+      (void)frexpf(amax, &ex);                      // amax = f * 2^ex, f in [0.5, 1)
+      const int sh = 8 - ex;
+      const float up = ldexpf(1.f, sh);
+      qs[t] = ldexpf(1.f, -sh);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[c][e] *= up;   // exact: a power of two
+        split_fp8(x[c], qh[t][c], ql[t][c]);
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < L::KSTEPS; ++st)
+        qb[t][st] = col_ok[t] ? *reinterpret_cast<const uint4*>(qrow + L::k_dim(st, gq)) : make_uint4(0, 0, 0, 0);
+    }
   }
 
   // this wave's blocks: blk_begin + first + stride * i, i < cnt
@@ -412,6 +493,14 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   auto scores = [&](const BlockRegs<KV, D>& r, f32x4 (&s)[TPW]) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (L::F8MMA) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        s[t] = mfma_fp8_128(r.k[0], r.k[1], qh[t][0], qh[t][1], s[t]);
+        s[t] = mfma_fp8_128(r.k[0], r.k[1], ql[t][0], ql[t][1], s[t]);
+      }
+      return;
+    }
 #pragma unroll
     for (int st = 0; st < L::KSTEPS; ++st) {
       uint4 a;
@@ -517,11 +606,11 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     f32x4 s0[TPW], s1[TPW];
     scores(r0, s0);
     scores(r1, s1);
-    const float c0 = p.scale_log2 * r0.ksc, c1 = p.scale_log2 * r1.ksc;
     float mn[TPW], alpha[TPW];
     bool ok[TPW][8];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
+      const float c0 = p.scale_log2 * qs[t] * r0.ksc, c1 = p.scale_log2 * qs[t] * r1.ksc;
       float mx;
       if constexpr (DENSE) {
         float mx0 = s0[t][0], mx1 = s1[t][0];
@@ -562,6 +651,7 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     build_va(va);
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
+      const float c0 = p.scale_log2 * qs[t] * r0.ksc, c1 = p.scale_log2 * qs[t] * r1.ksc;
       float pw[8];
       if constexpr (DENSE) {
 #pragma unroll
