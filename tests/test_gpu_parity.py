@@ -502,14 +502,16 @@ def test_no_writes_outside_workspace_and_output(seed):
     _check(wl, ds)
 
 
-def test_repeated_steps_bit_identical():
-    # the same step run again gives the same bits (every reduction has a fixed
-    # order; the decode items' K regrouping through LDS included): the 7B
-    # decode lengths at 32 query / 8 kv heads, bf16, three times
-    wl = W.generate(W.make_plan("gqa_decode"))
-    ds = _run(wl, "gqa_decode repeated")
+@pytest.mark.parametrize("name", ["gqa_decode", "decode_7b", "fp8_gqa_long"])
+def test_repeated_steps_bit_identical(name):
+    # the same step run again gives the same bits: every reduction has a fixed
+    # order (the decode items' K regrouping through LDS included), and the
+    # partitions of a split row are merged in partition order by whichever of
+    # their workgroups arrives last, reading the others' partials coherently
+    wl = W.generate(W.make_plan(name))
+    ds = _run(wl, f"{name} repeated")
     first = ds.out.clone()
-    for r in range(2):
+    for r in range(4):
         ds.out.fill_(0)
         ds.step()
         torch.cuda.synchronize()
