@@ -36,6 +36,14 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-file additions.  The MFMA tile kernels never compute with a NaN (slots
+# past a context or outside the pool read as zeros, masked scores are selected
+# to -inf), so they are compiled without NaN semantics: every fmaxf after a
+# cross-lane swap otherwise carries an extra v_max that only quiets NaNs
+# (8 of the 146 vector instructions of a prefill tile's block pair).
+FILE_FLAGS = {"tile_mfma.hip": ["-fno-honor-nans"]}
+
+
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     path = os.path.join(rocm, "bin", "hipcc")
@@ -45,7 +53,8 @@ def hipcc() -> str:
 def _compile(src: str, checks: bool = False) -> str:
     stem = os.path.splitext(os.path.basename(src))[0] + ("_checks" if checks else "")
     obj = os.path.join(BUILD, stem + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, *(["-DPKV_CHECKS"] if checks else []),
+    cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []),
+           *(["-DPKV_CHECKS"] if checks else []),
            "-I", os.path.join(HERE, "..", "include"), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
