@@ -76,11 +76,11 @@ __device__ __forceinline__ uint32_t f32x4_to_fp8x4(float a, float b, float c, fl
 }
 
 // Query values as two fp8 operands whose sum is the value times 2^s: x (already
-// scaled) -> hi = fp8(x), lo = fp8(x - hi).  A 16-bit float has at most 8
-// significant bits and hi keeps the top 4 (rounded), so x - hi is an exact
-// float32 with at most 4 significant bits and lo = x - hi exactly, unless it
-// falls below the fp8 normal range (|x - hi| < 2^-6; s puts the column's
-// largest |x| in [128, 256), so only parts more than 2^13 below it lose bits).
+// scaled) -> hi = fp8(x), lo = fp8(x - hi).  A bfloat16 has 8 significant
+// bits and hi keeps the top 4 (rounded), so x - hi is an exact float32 with at
+// most 4 significant bits and lo = x - hi exactly, unless it falls below the
+// fp8 normal range (|x - hi| < 2^-6; s puts the column's largest |x| in
+// [128, 256), so only parts more than 2^13 below it lose bits).
 __device__ __forceinline__ void split_fp8(const float (&x)[16], uint4& hi, uint4& lo) {
   uint32_t h[4], l[4];
 #pragma unroll
@@ -145,9 +145,12 @@ struct TileLay {
   static constexpr int ROWB = D * ELT;          // bytes of a token row of one head
   static constexpr int BLKB = 16 * ROWB;        // bytes of one (block, head)
   static constexpr int KSTEPS = D / 32;         // 16x16x32 MFMA steps of the score product
-  // fp8 K at head_dim 128: scores on the fp8 16x16x128 MFMA straight from the
-  // stored bytes (the query split into two fp8 parts), no K conversions
-  static constexpr bool F8MMA = KV == kFP8 && D == 128;
+  // fp8 K at head_dim 128 with bf16 queries: scores on the fp8 16x16x128 MFMA
+  // straight from the stored bytes (the query split exactly into two fp8
+  // parts), no K conversions.  An f16 query has 11 significant bits, more
+  // than two E4M3 parts hold, so f16 queries keep the conversion path.
+  template <int QT>
+  static constexpr bool f8mma() { return KV == kFP8 && D == 128 && QT == kBF16; }
   static constexpr int KB = D / 4 * ELT;        // K bytes per lane per block (D/4 dims)
   static constexpr int KLD = KB / 16;           // 16-byte chunks of K per lane
   // K chunk c of lane group gq holds bytes c*64 + gq*16 of its token row;
@@ -300,7 +303,7 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   // Q^T operand of score step st: the 8 dims of this column's query that the
   // K operand of the same step holds (zero for unused columns)
   uint4 qb[TPW][L::KSTEPS];
-  // F8MMA: the fp8 operands (hi, lo) of q * 2^s[t] over the dims the lane's K
+  // fp8 scores (f8mma): the fp8 operands (hi, lo) of q * 2^s[t] over the dims the lane's K
   // chunks hold (16gq .. 16gq+15 and 64+16gq .. +15), and qs[t] = 2^-s[t],
   // which scales the scores back; s[t] puts the column's largest |q| in
   // [128, 256), inside the fp8 range.  qs is 1 on the other paths.
@@ -311,7 +314,7 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     const uint16_t* qrow =
         reinterpret_cast<const uint16_t*>(p.q) + ((size_t)row[t] * p.num_q_heads + head[t]) * D;
     qs[t] = 1.f;
-    if constexpr (L::F8MMA) {
+    if constexpr (L::template f8mma<QT>()) {
       float x[2][16];
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -493,7 +496,7 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   auto scores = [&](const BlockRegs<KV, D>& r, f32x4 (&s)[TPW]) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (L::F8MMA) {
+    if constexpr (L::template f8mma<QT>()) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         s[t] = mfma_fp8_128(r.k[0], r.k[1], qh[t][0], qh[t][1], s[t]);

@@ -98,6 +98,7 @@ SMALL = {
     "fp8_gqa8_bf16q_d128": dict(Hq=16, Hkv=2, D=128, kv=W.FP8, qd=W.BF16,
                                 lens=_rng.integers(1, 5000, 8).tolist()),
     "fp8_mha_f16q_d64": dict(Hq=4, Hkv=4, D=64, kv=W.FP8, qd=W.F16, lens=[3, 16, 17, 300, 1200]),
+    "fp8_gqa8_f16q_d128": dict(Hq=16, Hkv=2, D=128, kv=W.FP8, qd=W.F16, lens=[1, 40, 700, 2600]),
     "fp8_gqa4_bf16q_d64": dict(Hq=8, Hkv=2, D=64, kv=W.FP8, qd=W.BF16, lens=[1, 31, 777]),
     "chunk_bf16_d128": dict(Hq=4, Hkv=4, D=128, kv=W.BF16, qd=W.BF16, lens=[40, 300, 700, 33],
                             qlens=[1, 37, 129, 33]),
@@ -548,3 +549,20 @@ def test_more_rows_than_a_grid_y_dimension_holds(plan):
                                      wl.scale, 16, W.BF16, W.BF16)[0]
         ok = oracle.tolerance_ok(got[r:r + 1], ref, *TOL[W.BF16])
         assert ok.all(), f"row {r}: {(~ok).sum()} elements out of tolerance"
+
+
+@pytest.mark.parametrize("qd", [W.BF16, W.F16])
+def test_fp8_scores_with_query_dims_over_five_decades(qd):
+    # fp8 scores at head_dim 128 run on the fp8 MFMA with each query column
+    # scaled by a power of two and split into two fp8 parts; query dims whose
+    # magnitudes span 1e-3 .. 1e2 within one column (and columns of very
+    # different sizes) still match the oracle, in decode and prefill rows
+    rng = np.random.default_rng(77)
+    lens, qlens = [900, 33, 2100, 300], [1, 33, 1, 120]
+    cfg = W.Config("wide", "wide", 16, 2, 128, 16, 260, W.FP8, qd, 77)
+    wl = W.generate(W.custom_plan(cfg, lens, qlens, 77))
+    q = oracle.decode_bits(wl.q, qd).astype(np.float32)
+    q *= (10.0 ** rng.uniform(-3, 2, size=(1, 1, 128))).astype(np.float32)
+    q *= (10.0 ** rng.uniform(-1, 1, size=(q.shape[0], q.shape[1], 1))).astype(np.float32)
+    wl.q = W.round_to_bits(q, qd)
+    _check(wl, _run(wl, f"fp8 scores, wide-range {qd} queries"))
