@@ -566,3 +566,43 @@ def test_fp8_scores_with_query_dims_over_five_decades(qd):
     q *= (10.0 ** rng.uniform(-1, 1, size=(q.shape[0], q.shape[1], 1))).astype(np.float32)
     wl.q = W.round_to_bits(q, qd)
     _check(wl, _run(wl, f"fp8 scores, wide-range {qd} queries"))
+
+
+def _spread_magnitudes(wl, seed, k_decades, v_decades):
+    """K/V of a generated step with magnitudes spread over decades: factors
+    10^U(lo, hi) per (block, head, slot) on 16-bit pools (rounded again), per
+    (block, head) on fp8 pools' scales (bytes kept).  The step's appended rows
+    are re-read from the pools."""
+    rng = np.random.default_rng(seed)
+    cfg = wl.cfg
+    for store, scales, (lo, hi) in ((wl.k, wl.k_scale, k_decades), (wl.v, wl.v_scale, v_decades)):
+        if cfg.kv_dtype == W.FP8:
+            scales *= (10.0 ** rng.uniform(lo, hi, scales.shape)).astype(np.float32)
+            continue
+        x = oracle.decode_bits(store.blocks, cfg.kv_dtype).astype(np.float32)
+        f = (10.0 ** rng.uniform(lo, hi, x.shape[:3] + (1,))).astype(np.float32)
+        bits = W.round_to_bits(x * f, cfg.kv_dtype)
+        store.blocks[...] = np.where(store.blocks == store.poison, store.blocks, bits)
+    rows = np.searchsorted(wl.k.used_ids, wl.append_block)
+    wl.k_new = np.ascontiguousarray(wl.k.blocks[rows, :, wl.append_offset, :])
+    wl.v_new = np.ascontiguousarray(wl.v.blocks[rows, :, wl.append_offset, :])
+    return wl
+
+
+@pytest.mark.parametrize("kv", [W.BF16, W.FP8])
+@pytest.mark.parametrize("scale_mul", [1.0, 20.0, 1e-3])
+def test_kv_magnitudes_over_decades_and_extreme_softmax_scales(kv, scale_mul):
+    # keys and values whose sizes vary over decades (16-bit: K and V per token
+    # over 4; fp8: K per block scale over 6, V scales at most their generated
+    # size over 3 -- the fp8 tolerance is absolute, and a bf16 output near 40
+    # is already 0.125 from its neighbours), with the softmax scale as given,
+    # 20x (nearly one-hot weights) or 1/1000 (nearly flat): decode, verify and
+    # prefill rows, MHA 16-bit and 8:1 fp8, against the oracle
+    lens, qlens = [700, 90, 2300, 400, 1500, 64], [1, 90, 1, 5, 1, 64]
+    Hq, Hkv = (8, 8) if kv == W.BF16 else (16, 2)
+    nb = sum(-(-L // 16) for L in lens) + 13
+    cfg = W.Config("mag", "mag", Hq, Hkv, 128, 16, nb, kv, W.BF16, 91)
+    wl = _spread_magnitudes(W.generate(W.custom_plan(cfg, lens, qlens, 91)), 92,
+                            (-2, 2) if kv == W.BF16 else (-3, 3), (-2, 2) if kv == W.BF16 else (-3, 0))
+    wl.scale = np.float32(wl.scale * scale_mul)
+    _check(wl, _run(wl, f"magnitudes over decades kv={kv} scale x{scale_mul}"))
