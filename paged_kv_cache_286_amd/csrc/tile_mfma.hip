@@ -336,7 +336,9 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
       amax = max_xor32(max_xor16(amax));            // the column's 4 lane groups
       int ex;
       (void)frexpf(amax, &ex);                      // amax = f * 2^ex, f in [0.5, 1)
-      const int sh = 8 - ex;
+      // (at most 2^100: a column whose largest |q| is below 2^-92 -- subnormal
+      // bf16 included -- scores ~0 either way, and 2^(8 - ex) would overflow)
+      const int sh = min(8 - ex, 100);
       const float up = ldexpf(1.f, sh);
       qs[t] = ldexpf(1.f, -sh);
 #pragma unroll

@@ -564,6 +564,8 @@ def test_fp8_scores_with_query_dims_over_five_decades(qd):
     q = oracle.decode_bits(wl.q, qd).astype(np.float32)
     q *= (10.0 ** rng.uniform(-3, 2, size=(1, 1, 128))).astype(np.float32)
     q *= (10.0 ** rng.uniform(-1, 1, size=(q.shape[0], q.shape[1], 1))).astype(np.float32)
+    if qd == W.BF16:
+        q[:, 3, :] *= np.float32(1e-39 / 4)     # one head's queries subnormal (bf16 keeps them)
     wl.q = W.round_to_bits(q, qd)
     _check(wl, _run(wl, f"fp8 scores, wide-range {qd} queries"))
 
