@@ -239,7 +239,8 @@ int pkv_checks_enabled(void);
  * workspace argument.  The workspace lives in a device array inside the
  * library, paged_attn_scratch_bytes() (64 MiB) long, of which every device the
  * library runs on holds one copy until the process ends; the call itself
- * allocates nothing.  A step whose paged_attn_workspace_bytes exceeds it
+ * allocates nothing.  The array used is that of the device `stream` belongs
+ * to (the current device for the null stream).  A step whose paged_attn_workspace_bytes exceeds it
  * returns PKV_ERR_SCRATCH before anything is enqueued.  Every call on a device
  * shares that device's array and nothing in it needs to start at zero, so
  * calls on one device whose executions overlap (different streams, or

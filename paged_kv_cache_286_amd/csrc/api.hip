@@ -267,16 +267,31 @@ ScratchAddresses& scratch_addresses() {
 }
 
 // this device's scratch address, looked up on the first call on the device
-int device_scratch(void** out) {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
+// The scratch array of the device `stream` runs on (the current device for
+// the null stream).  The first call on a device makes that device current for
+// the symbol lookup, then restores the caller's device.
+int device_scratch(void* stream, void** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return hip_status(e);
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t d = -1;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &d);
+    if (e != hipSuccess) return hip_status(e);
+    dev = d;
+  }
   if (dev < 0 || dev >= kMaxDevices) return PKV_ERR_UNSUPPORTED;
   ScratchAddresses& a = scratch_addresses();
   std::lock_guard<std::mutex> g(a.mu);
   if (a.ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
     if (e != hipSuccess) return hip_status(e);
     if (p == nullptr) return hip_status(hipErrorInvalidSymbol);
     a.ptr[dev] = p;
@@ -410,7 +425,7 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
                                 max_query_len);
   if (use_scratch) {
     if (lay.total > kScratchBytes) return PKV_ERR_SCRATCH;
-    st = device_scratch(&workspace);
+    st = device_scratch(stream, &workspace);
     if (st != PKV_OK) return st;
     workspace_bytes = kScratchBytes;
   }

@@ -21,14 +21,17 @@ def _step(Hq, Hkv, kv, lens, qlens, seed):
     return W.generate(W.custom_plan(cfg, lens, qlens, seed))
 
 
-def _both(wl):
+def _both(wl, side_stream=False):
     from paged_kv_cache_286_amd.device import DeviceStep
     p, cfg = wl.plan, wl.cfg
     print(f"[gpu] noalloc: seqs={p.num_seqs} rows={p.total_q_tokens} max_ctx={p.max_context_len} "
           f"kv={cfg.kv_dtype} Hq={cfg.num_q_heads} Hkv={cfg.num_kv_heads} workspace={0}", flush=True)
     ds = DeviceStep(wl)
     assert 0 < ds.ws_bytes <= pk.paged_attn_scratch_bytes()
-    s = torch.cuda.current_stream()
+    # the scratch is that of the stream's device, for torch's default stream
+    # and for a stream of its own alike
+    s = torch.cuda.Stream() if side_stream else torch.cuda.current_stream()
+    torch.cuda.synchronize()
     ds.append(s)
     ds.attend(s)
     torch.cuda.synchronize()
@@ -54,7 +57,7 @@ def test_noalloc_matches_the_workspace_entry_point_twice():
     # a mixed step (chunk rows and split decode rows), then a smaller split
     # grouped-query fp8 decode step on the same scratch
     _both(_step(8, 8, W.BF16, [50, 700, 1300, 90, 2500, 16, 3100], [1, 1, 300, 1, 1, 16, 1], 71))
-    _both(_step(16, 2, W.FP8, [3000, 200, 2047], [1, 1, 1], 72))
+    _both(_step(16, 2, W.FP8, [3000, 200, 2047], [1, 1, 1], 72), side_stream=True)
 
 
 def test_noalloc_refuses_a_step_beyond_its_scratch():
