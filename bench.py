@@ -86,7 +86,8 @@ def _oracle_seqs(seqs):
         return time.perf_counter() - t0
 
 
-# The GPU machine gives one GPU's job a share of 16 cores, whatever the machine has.
+# At most this many worker processes: a one-GPU job on a shared host is given
+# a share of 16 cores, whatever the machine reports.
 CPU_POOL_CAP = 16
 
 
