@@ -161,7 +161,8 @@ size_t paged_attn_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_
  *   num_seqs, total_q_tokens, max_context_len, max_query_len  host copies of
  *                   len(context_lens), sum(query_lens), max(context_lens), max(query_lens);
  *                   they size the launch grids and must bound the device values.
- *   scale           softmax scale (typically 1/sqrt(head_dim)).
+ *   scale           softmax scale, finite and >= 0 (typically 1/sqrt(head_dim));
+ *                   otherwise PKV_ERR_SHAPE.
  *   out             [total_q_tokens][num_q_heads][head_dim], q_dtype, rounded to nearest even.
  *   workspace       device scratch of at least paged_attn_workspace_bytes(...) bytes
  *                   (may be NULL when that is 0); clobbered.

@@ -3,6 +3,7 @@
 // include/pagedkv.h for the contract of every entry point.
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <mutex>
 #include <vector>
 
@@ -420,6 +421,9 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
     return PKV_ERR_NULL;
   if (pool->kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_SHAPE;
+  // the tile kernels take a block's largest scaled score as the largest raw
+  // score times the scale, which holds for a finite scale >= 0
+  if (!std::isfinite(scale) || scale < 0.f) return PKV_ERR_SHAPE;
 
   const Layout lay = layout_for(pool, num_seqs, num_q_heads, total_q_tokens, max_context_len,
                                 max_query_len);

@@ -75,6 +75,8 @@ def test_step_validation():
     assert _step(p, total_q_tokens=5) == pk.PKV_ERR_SHAPE            # max_query_len 1 => 4 rows
     assert _step(p, max_query_len=3, total_q_tokens=5) == pk.PKV_ERR_SHAPE
     assert _step(p, q=FAKE + 2) == pk.PKV_ERR_SHAPE                   # misaligned
+    for bad in (-0.125, float("nan"), float("inf")):                # scale finite and >= 0
+        assert _step(p, scale=bad) == pk.PKV_ERR_SHAPE
     assert _step(_pool(block_size=8)) == pk.PKV_ERR_UNSUPPORTED
     # (block, kv head) slice indices must fit an int32
     assert _step(_pool(num_blocks=2**26, num_kv_heads=64), num_q_heads=64) == pk.PKV_ERR_SHAPE

@@ -592,14 +592,15 @@ def _spread_magnitudes(wl, seed, k_decades, v_decades):
 
 
 @pytest.mark.parametrize("kv", [W.BF16, W.FP8])
-@pytest.mark.parametrize("scale_mul", [1.0, 20.0, 1e-3])
+@pytest.mark.parametrize("scale_mul", [1.0, 20.0, 1e-3, 0.0])
 def test_kv_magnitudes_over_decades_and_extreme_softmax_scales(kv, scale_mul):
     # keys and values whose sizes vary over decades (16-bit: K and V per token
     # over 4; fp8: K per block scale over 6, V scales at most their generated
     # size over 3 -- the fp8 tolerance is absolute, and a bf16 output near 40
     # is already 0.125 from its neighbours), with the softmax scale as given,
-    # 20x (nearly one-hot weights) or 1/1000 (nearly flat): decode, verify and
-    # prefill rows, MHA 16-bit and 8:1 fp8, against the oracle
+    # 20x (nearly one-hot weights), 1/1000 (nearly flat) or 0 (every visible key
+    # weighs the same): decode, verify and prefill rows, MHA 16-bit and 8:1 fp8,
+    # against the oracle
     lens, qlens = [700, 90, 2300, 400, 1500, 64], [1, 90, 1, 5, 1, 64]
     Hq, Hkv = (8, 8) if kv == W.BF16 else (16, 2)
     nb = sum(-(-L // 16) for L in lens) + 13
