@@ -120,6 +120,17 @@ SMALL = {
                                   lens=[40, 900, 1700, 300, 64], qlens=[4, 3, 2, 9, 1]),
     "specdec_gqa8_bf16_d64": dict(Hq=16, Hkv=2, D=64, kv=W.BF16, qd=W.BF16,
                                   lens=[33, 500, 2100], qlens=[2, 3, 1]),
+    # one kv head for 32 query heads: a decode row fills two 16-column tiles
+    "mqa32_bf16_d128": dict(Hq=32, Hkv=1, D=128, kv=W.BF16, qd=W.BF16, lens=[1, 17, 900, 2600]),
+    "mqa32_fp8_d128": dict(Hq=32, Hkv=1, D=128, kv=W.FP8, qd=W.BF16, lens=[3, 1000, 4100]),
+    # prefill rows at 16 query heads per kv head (a chunk entry covers 8 rows x 16 heads)
+    "chunk_gqa16_bf16_d64": dict(Hq=32, Hkv=2, D=64, kv=W.BF16, qd=W.BF16, lens=[70, 600, 9],
+                                 qlens=[70, 33, 1]),
+    "chunk_mqa8_f16_d128": dict(Hq=8, Hkv=1, D=128, kv=W.F16, qd=W.F16, lens=[300, 45, 1000],
+                                qlens=[129, 45, 2]),
+    # a 16-column tile holds half of one row's 32 query heads
+    "chunk_mqa32_bf16_d128": dict(Hq=32, Hkv=1, D=128, kv=W.BF16, qd=W.BF16, lens=[150, 600, 20],
+                                  qlens=[150, 7, 1]),
 }
 
 
