@@ -602,7 +602,7 @@ def _spread_magnitudes(wl, seed, k_decades, v_decades):
     return wl
 
 
-@pytest.mark.parametrize("kv", [W.BF16, W.FP8])
+@pytest.mark.parametrize("kv", [W.BF16, W.F16, W.FP8])
 @pytest.mark.parametrize("scale_mul", [1.0, 20.0, 1e-3, 0.0])
 def test_kv_magnitudes_over_decades_and_extreme_softmax_scales(kv, scale_mul):
     # keys and values whose sizes vary over decades (16-bit: K and V per token
@@ -613,10 +613,10 @@ def test_kv_magnitudes_over_decades_and_extreme_softmax_scales(kv, scale_mul):
     # weighs the same): decode, verify and prefill rows, MHA 16-bit and 8:1 fp8,
     # against the oracle
     lens, qlens = [700, 90, 2300, 400, 1500, 64], [1, 90, 1, 5, 1, 64]
-    Hq, Hkv = (8, 8) if kv == W.BF16 else (16, 2)
+    Hq, Hkv = (16, 2) if kv == W.FP8 else (8, 8)
     nb = sum(-(-L // 16) for L in lens) + 13
-    cfg = W.Config("mag", "mag", Hq, Hkv, 128, 16, nb, kv, W.BF16, 91)
+    cfg = W.Config("mag", "mag", Hq, Hkv, 128, 16, nb, kv, W.F16 if kv == W.F16 else W.BF16, 91)
     wl = _spread_magnitudes(W.generate(W.custom_plan(cfg, lens, qlens, 91)), 92,
-                            (-2, 2) if kv == W.BF16 else (-3, 3), (-2, 2) if kv == W.BF16 else (-3, 0))
+                            (-3, 3) if kv == W.FP8 else (-2, 2), (-3, 0) if kv == W.FP8 else (-2, 2))
     wl.scale = np.float32(wl.scale * scale_mul)
     _check(wl, _run(wl, f"magnitudes over decades kv={kv} scale x{scale_mul}"))
