@@ -180,6 +180,36 @@ int paged_attn_step(const pkv_pool* pool,
                     float scale, void* out,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* paged_append_attn_step -- the step's append and its attention in one call
+ * ("Growing During Decode" then "Attention Over Scattered Blocks"): the same
+ * results as paged_kv_append(pool, k_pool, v_pool, k_new, v_new,
+ * pool->kv_dtype, slot_mapping, total_q_tokens) followed by paged_attn_step
+ * with the remaining arguments on the same stream, provided that (as in any
+ * step a block manager produces) row r's slot is the one block_tables names
+ * for that row's position and no other row's context reaches an appended slot.
+ *   k_new, v_new    [total_q_tokens][num_kv_heads][head_dim] rows of pool->kv_dtype,
+ *                   one per query row, in query-row order.
+ *   slot_mapping    [total_q_tokens] int32, as paged_kv_append.
+ *   the rest        as paged_attn_step.
+ * Small decode-only steps (max_query_len 1, num_seqs * max_context_len <= 32768)
+ * of 16-bit KV whose rows run on the VALU decode kernel (at most two query
+ * heads per kv head) do both in the decode launch: it stores each new row into
+ * its slot and attends to it from k_new / v_new, after the pool's blocks, which
+ * saves the append kernel's launch latency; the pools come out bit for bit the
+ * same and the output the same up to that order's rounding.  Every other step
+ * enqueues the append kernel first.  Returns the first failing check of either
+ * call before anything is enqueued. */
+int paged_append_attn_step(const pkv_pool* pool, void* k_pool, void* v_pool,
+                           const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                           const void* q, int32_t q_dtype, int32_t num_q_heads,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, const int32_t* query_lens,
+                           const int32_t* shared_blocks, int32_t num_seqs,
+                           int32_t total_q_tokens, int32_t max_context_len,
+                           int32_t max_query_len, float scale, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* pkv_set_plan_override -- force parts of the launch plan that the library
  * otherwise derives from the host scalars of a step (a testing and tuning
  * hook: every choice gives the same results up to rounding order).

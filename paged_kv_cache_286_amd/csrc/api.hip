@@ -332,18 +332,24 @@ const char* pkv_kernel_name(int32_t kind) {
   }
 }
 
-int paged_kv_append(const pkv_pool* pool, void* k_pool, void* v_pool, const void* k_new,
-                    const void* v_new, int32_t new_dtype, const int32_t* slot_mapping,
-                    int32_t num_tokens, void* stream) {
-  const int st = check_pool(pool);
-  if (st != PKV_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// Host checks of an append of num_tokens rows of the pool's own element type.
+int check_append(const void* k_pool, const void* v_pool, const void* k_new, const void* v_new,
+                 const int32_t* slot_mapping, int32_t num_tokens) {
   if (num_tokens < 0) return PKV_ERR_SHAPE;
-  if (!known_dtype(new_dtype)) return PKV_ERR_DTYPE;
-  if (new_dtype != pool->kv_dtype) return PKV_ERR_DTYPE;
   if (num_tokens == 0) return PKV_OK;
   if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PKV_ERR_NULL;
   if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
     return PKV_ERR_SHAPE;
+  return PKV_OK;
+}
+
+hipError_t enqueue_append(const pkv_pool* pool, void* k_pool, void* v_pool, const void* k_new,
+                          const void* v_new, const int32_t* slot_mapping, int32_t num_tokens,
+                          hipStream_t s) {
   pkv::AppendArgs a;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
@@ -356,8 +362,25 @@ int paged_kv_append(const pkv_pool* pool, void* k_pool, void* v_pool, const void
   a.elem_bytes = elem_bytes(pool->kv_dtype);
   a.block_size = pool->block_size;
   a.num_blocks = pool->num_blocks;
-  const hipStream_t s = (hipStream_t)stream;
-  return hip_status(timed_launch(PKV_KERNEL_APPEND, s, [&] { return pkv::launch_append(a, s); }));
+  return timed_launch(PKV_KERNEL_APPEND, s, [&] { return pkv::launch_append(a, s); });
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_kv_append(const pkv_pool* pool, void* k_pool, void* v_pool, const void* k_new,
+                    const void* v_new, int32_t new_dtype, const int32_t* slot_mapping,
+                    int32_t num_tokens, void* stream) {
+  int st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) return PKV_ERR_SHAPE;
+  if (!known_dtype(new_dtype)) return PKV_ERR_DTYPE;
+  if (new_dtype != pool->kv_dtype) return PKV_ERR_DTYPE;
+  st = check_append(k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens);
+  if (st != PKV_OK || num_tokens == 0) return st;
+  return hip_status(enqueue_append(pool, k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens,
+                                   (hipStream_t)stream));
 }
 
 int paged_kv_append_quant(const pkv_pool* pool, void* k_pool, void* v_pool, float* k_scale,
@@ -403,8 +426,25 @@ size_t paged_attn_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_
   return layout_for(pool, num_seqs, num_q_heads, total_q_tokens, max_context_len, max_query_len).total;
 }
 
-// paged_attn_step and paged_attn_step_noalloc: the second takes its workspace
-// from this device's scratch array instead of the caller's.
+// The append that paged_append_attn_step enqueues with the step.
+struct FusedAppend {
+  void* k_pool;
+  void* v_pool;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slots;
+};
+
+// Decode steps of at most this many (sequence x context) tokens take their
+// append into the decode launch: there the separate append kernel's launch
+// latency is a large part of the step (the 4-sequence fp16 step: 10.2 ->
+// ~6 us); on larger steps the decode kernel grows by what the launch saves,
+// and the separate kernels keep each one's own time.
+constexpr int64_t kFuseAppendTokens = 32768;
+
+// paged_attn_step, paged_attn_step_noalloc (workspace from this device's
+// scratch array instead of the caller's) and paged_append_attn_step (fa: the
+// step's append goes first, or into the decode launch).
 static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_t num_q_heads,
                      const void* k_pool, const void* v_pool, const float* k_scale,
                      const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -412,10 +452,14 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
                      const int32_t* shared_blocks, int32_t num_seqs,
                      int32_t total_q_tokens, int32_t max_context_len, int32_t max_query_len,
                      float scale, void* out, void* workspace, size_t workspace_bytes,
-                     bool use_scratch, void* stream) {
+                     bool use_scratch, const FusedAppend* fa, void* stream) {
   int st = check_step_scalars(pool, q_dtype, num_q_heads, max_blocks_per_seq, num_seqs,
                               total_q_tokens, max_context_len, max_query_len);
   if (st != PKV_OK) return st;
+  if (fa != nullptr) {
+    st = check_append(fa->k_pool, fa->v_pool, fa->k_new, fa->v_new, fa->slots, total_q_tokens);
+    if (st != PKV_OK) return st;
+  }
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_lens || !out)
     return PKV_ERR_NULL;
@@ -458,6 +502,12 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
   p.ctx_lens = context_lens;
   p.q_lens = query_lens;
   p.shared_blocks = shared_blocks;
+  const bool fuse = fa != nullptr && !multi && !plan.decode_on_mfma && plan.heads_per_wg <= 2 &&
+                    pool->kv_dtype != PKV_FP8_E4M3 &&
+                    (int64_t)num_seqs * max_context_len <= kFuseAppendTokens;
+  p.k_new = fuse ? reinterpret_cast<const uint8_t*>(fa->k_new) : nullptr;
+  p.v_new = fuse ? reinterpret_cast<const uint8_t*>(fa->v_new) : nullptr;
+  p.slots = fuse ? fa->slots : nullptr;
   p.q_start = multi ? reinterpret_cast<const int32_t*>(ws + lay.q_start_off) : nullptr;
   p.row_seq = multi ? reinterpret_cast<const int32_t*>(ws + lay.row_seq_off) : nullptr;
   p.chunk_count = multi ? reinterpret_cast<const int32_t*>(ws + lay.chunk_count_off) : nullptr;
@@ -490,6 +540,9 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
   hipError_t e = hipSuccess;
   if (kCheckBytes > 0)
     e = pkv::launch_check(p, reinterpret_cast<int32_t*>(ws), max_context_len, max_query_len, s);
+  if (e == hipSuccess && fa != nullptr && !fuse)
+    e = enqueue_append(pool, fa->k_pool, fa->v_pool, fa->k_new, fa->v_new, fa->slots,
+                       total_q_tokens, s);
   if (e != hipSuccess) return hip_status(e);
   if (multi) {
     e = timed_launch(PKV_KERNEL_PROLOGUE, s, [&] { return pkv::launch_prologue(p, s); });
@@ -523,7 +576,23 @@ int paged_attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32_
   return attn_step(pool, q, q_dtype, num_q_heads, k_pool, v_pool, k_scale, v_scale, block_tables,
                    max_blocks_per_seq, context_lens, query_lens, shared_blocks, num_seqs,
                    total_q_tokens, max_context_len, max_query_len, scale, out, workspace,
-                   workspace_bytes, false, stream);
+                   workspace_bytes, false, nullptr, stream);
+}
+
+int paged_append_attn_step(const pkv_pool* pool, void* k_pool, void* v_pool, const void* k_new,
+                           const void* v_new, const int32_t* slot_mapping, const void* q,
+                           int32_t q_dtype, int32_t num_q_heads, const float* k_scale,
+                           const float* v_scale, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           const int32_t* query_lens, const int32_t* shared_blocks,
+                           int32_t num_seqs, int32_t total_q_tokens, int32_t max_context_len,
+                           int32_t max_query_len, float scale, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const FusedAppend fa{k_pool, v_pool, k_new, v_new, slot_mapping};
+  return attn_step(pool, q, q_dtype, num_q_heads, k_pool, v_pool, k_scale, v_scale, block_tables,
+                   max_blocks_per_seq, context_lens, query_lens, shared_blocks, num_seqs,
+                   total_q_tokens, max_context_len, max_query_len, scale, out, workspace,
+                   workspace_bytes, false, &fa, stream);
 }
 
 int paged_attn_step_noalloc(const pkv_pool* pool, const void* q, int32_t q_dtype,
@@ -537,7 +606,7 @@ int paged_attn_step_noalloc(const pkv_pool* pool, const void* q, int32_t q_dtype
   return attn_step(pool, q, q_dtype, num_q_heads, k_pool, v_pool, k_scale, v_scale, block_tables,
                    max_blocks_per_seq, context_lens, query_lens, shared_blocks, num_seqs,
                    total_q_tokens, max_context_len, max_query_len, scale, out, nullptr, 0, true,
-                   stream);
+                   nullptr, stream);
 }
 
 size_t paged_attn_scratch_bytes(void) { return kScratchBytes; }

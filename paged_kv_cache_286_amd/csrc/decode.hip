@@ -35,11 +35,12 @@
 
 namespace pkv {
 
-template <int KV, int QT, int D, int GB>
+// FUSED: the step's append goes into this launch (p.k_new set; 16-bit KV)
+template <int KV, int QT, int D, int GB, bool FUSED>
 __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) {
   const int nx = p.num_q_heads / GB;
   const int seq = blockIdx.x / nx;
-  decode_valu_wg<KV, QT, D, GB>(p, blockIdx.x - seq * nx, seq, blockIdx.y);
+  decode_valu_wg<KV, QT, D, GB, FUSED>(p, blockIdx.x - seq * nx, seq, blockIdx.y);
 }
 
 // Merge the partitions of every (row, query head) whose context was split.
@@ -255,11 +256,21 @@ static hipError_t decode_by_group(const StepParams& p, const StepPlan& plan, hip
   const dim3 grid((uint32_t)(p.num_q_heads / plan.heads_per_wg * p.num_seqs), (uint32_t)p.max_parts);
   const dim3 block(kWaves * 64);
   (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
+  if (p.k_new != nullptr) {
+    // the append in this launch: 16-bit KV, one or two query heads per kv head
+    if constexpr (KV == kFP8) return hipErrorInvalidValue;
+    else switch (plan.heads_per_wg) {
+      case 1: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 1, true>), grid, block, 0, stream, p); break;
+      case 2: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 2, true>), grid, block, 0, stream, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (plan.heads_per_wg) {
-    case 1: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 1>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 2>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 4>), grid, block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 8>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 1, false>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 2, false>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 4, false>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((decode_valu_kernel<KV, QT, D, 8, false>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -123,7 +123,7 @@ __device__ __forceinline__ void attend_block(const uint4 (&kr)[Lay<KV, D>::NL],
 // One workgroup of the decode kernel: query heads hx*GB .. hx*GB+GB-1 of
 // sequence `seq`, partition `part` (the kernel's block indices; the step
 // kernel of mixed steps runs the same workgroups among its own).
-template <int KV, int QT, int D, int GB>
+template <int KV, int QT, int D, int GB, bool FUSED = false>
 __device__ __forceinline__ void decode_valu_wg(const StepParams& p, int hx, int seq, int part) {
   using T = Lay<KV, D>;
   static_assert(T::LPR >= 1 && T::LPR <= 16 && T::NL >= 1, "unsupported shape");
@@ -143,13 +143,56 @@ __device__ __forceinline__ void decode_valu_wg(const StepParams& p, int hx, int 
     row = p.q_start[seq];
     if (row < 0 || row >= p.total_q) return;
   }
+  // Append taken into the decode launch (16-bit KV; small steps, where the
+  // launch latency of a separate append would dominate): wave 0 of the
+  // partition-0 workgroup of the first head group of each kv head (the
+  // writer) stores the row's new K and V into its slot, one 16-byte piece per
+  // lane (K on the first LPR lanes, V on the next), whatever the row's length
+  // says.  No workgroup of this launch reads that slot from the pool: the
+  // partition holding position L-1 attends to the row from k_new / v_new after
+  // the pool's blocks, in the wave the round-robin would have given the next
+  // block.  Both load their pieces before the walk and use them after it.
+  static_assert(!FUSED || KV != kFP8, "the append goes into 16-bit decode launches only");
   const int L = p.ctx_lens[seq];
   const int tok0 = part * p.part_tokens;
+  const bool bad = tok0 >= L || L > p.max_blocks * 16 || L > p.max_parts * p.part_tokens;
+  bool writer = false, has_new = false;
+  uint4 kn = make_uint4(0, 0, 0, 0), vn = make_uint4(0, 0, 0, 0);
+  if constexpr (FUSED) {
+    writer = part == 0 && hx % (group / GB) == 0 && wave == 0;
+    const int walked = max(0, min(L + 14, tok0 + p.part_tokens) / 16 - tok0 / 16);   // blocks of [tok0, L-1)
+    has_new = !bad && wave == walked % kWaves && L - 1 >= tok0 && L - 1 < tok0 + p.part_tokens;
+    // (buffer loads issued by every workgroup, moving bytes only where
+    // needed: a branch around them would leave the compiler unsure, at the
+    // block loop, which loads are still in flight)
+    const size_t roff = ((size_t)row * p.num_kv_heads + kvh) * T::ROWB;
+    const int new_bytes = __builtin_amdgcn_readfirstlane((writer || has_new) ? T::ROWB : 0);
+    kn = load_block16<false>(block_rsrc(p.k_new + roff, new_bytes), (lane % T::LPR) * 16);
+    vn = load_block16<false>(block_rsrc(p.v_new + roff, new_bytes), (lane % T::LPR) * 16);
+  }
+  // (the pieces passed by value: a lambda holding them by reference kept them
+  // in private memory)
+  auto store_new = [&](uint4 kv_k, uint4 kv_v) {
+    const int slot = p.slots[row];
+    if (lane < 2 * T::LPR && slot >= 0 && (int64_t)slot < (int64_t)p.num_blocks * 16) {
+      const size_t dst = (((size_t)(slot >> 4) * p.num_kv_heads + kvh) * 16 + (slot & 15)) * T::ROWB +
+                         (size_t)(lane % T::LPR) * 16;
+      if (lane < T::LPR) *reinterpret_cast<uint4*>(const_cast<uint8_t*>(p.k_pool) + dst) = kv_k;
+      else *reinterpret_cast<uint4*>(const_cast<uint8_t*>(p.v_pool) + dst) = kv_v;
+    }
+  };
   // rows whose length breaks the host scalars' promises are left unwritten
-  if (tok0 >= L || L > p.max_blocks * 16 || L > p.max_parts * p.part_tokens) return;
+  if (bad) {
+    if constexpr (FUSED) {
+      if (writer) store_new(kn, vn);
+    }
+    return;
+  }
   const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+  // tokens read from the pool (position L-1 comes from k_new / v_new when fused)
+  const int Lw = FUSED ? L - 1 : L;
   const int blk_begin = tok0 >> 4;
-  const int blk_end = min((L + 15) >> 4, (tok0 + p.part_tokens) >> 4);
+  const int blk_end = min((Lw + 15) >> 4, (tok0 + p.part_tokens) >> 4);
 
   // block table entries of this wave's blocks (blk_begin + wave + kWaves * i)
   const int32_t* trow = p.tables + (size_t)seq * p.max_blocks;
@@ -217,7 +260,7 @@ __device__ __forceinline__ void decode_valu_wg(const StepParams& p, int hx, int 
     const int ic = min(i, end - 1);
     const int b = blk_begin + wave + kWaves * ic;
     int phys = __builtin_amdgcn_readlane(my_tbl, ic);
-    lim = i < end ? min(16, L - b * 16) : 0;
+    lim = i < end ? min(16, Lw - b * 16) : 0;
     if ((unsigned)phys >= (unsigned)p.num_blocks) { phys = 0; lim = 0; }
     const size_t boff = ((size_t)phys * p.num_kv_heads + kvh) * T::BLKB;
     // a block with no tokens is not read (the count kept scalar: no waterfall loop)
@@ -252,6 +295,19 @@ __device__ __forceinline__ void decode_valu_wg(const StepParams& p, int hx, int 
   const int cnt_sh = min(cnt, max(0, nsh - blk_begin - wave + kWaves - 1) / kWaves);
   walk(std::false_type{}, 0, cnt_sh);
   walk(std::true_type{}, cnt_sh, cnt);
+  // the appended row, as a block of one token: every lane takes its piece of
+  // the row, and only token row 0 counts
+  if constexpr (FUSED) {
+    if (has_new) {
+#pragma unroll
+      for (int j = 0; j < T::NL; ++j) {
+        kA[j] = kn;
+        vA[j] = vn;
+      }
+      attend_block<KV, QT, D, GB>(kA, vA, 1.f, 1.f, 1, rg, qp, qf, p.scale_log2, m, l, acc);
+    }
+    if (writer) store_new(kn, vn);
+  }
 
   // merge the RPL token-row groups of this wave
 #pragma unroll

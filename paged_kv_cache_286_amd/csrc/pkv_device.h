@@ -54,6 +54,12 @@ struct StepParams {
   const int32_t* ctx_lens;   // [S]
   const int32_t* q_lens;     // [S]
   const int32_t* shared_blocks;  // [S] leading blocks other sequences also read (NULL: none)
+  // Decode steps with the append taken into the decode launch (NULL otherwise):
+  // row s's new K/V ([S][Hkv][D], pool element type) go to pool slot slots[s],
+  // and the step attends to them for position ctx_lens[s] - 1 from here.
+  const uint8_t* k_new;
+  const uint8_t* v_new;
+  const int32_t* slots;
   const int32_t* q_start;    // [S + 1] row offsets (NULL when every query_len is 1)
   const int32_t* row_seq;    // [Tq] sequence of each row (NULL when every query_len is 1)
   float* part_ml;            // [Tq][Hq][max_parts][2]  (m in log2 units, l)

@@ -60,6 +60,33 @@ def check_slots_injective(slot_mapping, num_slots: int) -> None:
         raise ValueError(f"slot_mapping names slot {int(vals[counts > 1][0])} more than once")
 
 
+def append_fusable(tables: np.ndarray, context_lens, query_lens, slot_mapping) -> bool:
+    """True when a step meets paged_append_attn_step's contract: every appended
+    row's slot is the one its table names for that row's position, and no block
+    holding an appended slot is read by another sequence (the state
+    copy-on-write keeps a step in)."""
+    lens = np.asarray(context_lens, np.int64)
+    qlens = np.asarray(query_lens, np.int64)
+    slots = np.asarray(slot_mapping, np.int64)
+    seq = np.repeat(np.arange(len(lens)), qlens)
+    if len(seq) != len(slots) or len(seq) == 0:
+        return False
+    pos = np.concatenate([np.arange(L - Q, L) for L, Q in zip(lens, qlens)])
+    blk = tables[seq, pos // 16].astype(np.int64)
+    if blk.min() < 0 or not np.array_equal(slots, blk * 16 + pos % 16):
+        return False
+    nblk = (lens + 15) // 16
+    cols = np.arange(tables.shape[1])[None, :]
+    used = tables[cols < nblk[:, None]].astype(np.int64)
+    if used.min() < 0:
+        return False
+    owners = np.repeat(np.arange(len(lens)), nblk)
+    # distinct (block, sequence) pairs; a block with two of them is shared
+    pairs = np.unique(used * len(lens) + owners)
+    readers = np.bincount(pairs // len(lens), minlength=int(blk.max()) + 1)
+    return bool((readers[blk] <= 1).all())
+
+
 # Gap between the K and the V pool when both come from one allocation.  Two
 # separate large allocations put block b's K and V slices at the same address
 # modulo 2 MiB, where they contend for the same HBM banks; starting V 4 KiB
@@ -137,6 +164,8 @@ class DeviceStep:
             plan.max_query_len)
         self.workspace = (torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
                           if self.ws_bytes else None)
+        self.fusable = append_fusable(plan.block_tables, plan.context_lens, plan.query_lens,
+                                      wl.slot_mapping)
         self._bound, self._bound_key = None, None
 
     def poison_appended_slots(self) -> None:
@@ -167,16 +196,32 @@ class DeviceStep:
             shared_blocks=self.shared_blocks)
 
     def step(self, stream=None) -> None:
-        """append, then attend, with the two calls' arguments converted once per
-        stream (replacing a buffer attribute drops the converted calls)."""
+        """The whole step, append and attention: one paged_append_attn_step call
+        where its contract holds (append_fusable), else paged_kv_append then
+        paged_attn_step; the arguments are converted once per stream (replacing
+        a buffer attribute drops the converted calls)."""
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
         key = int(s.cuda_stream) if not isinstance(s, int) else s
         if self._bound_key != key:
-            # both calls with their arguments converted once for this stream
-            self._bound = (self.bind_append(s), self.bind_attend(s))
+            self._bound = ((self.bind_step(s),) if self.fusable
+                           else (self.bind_append(s), self.bind_attend(s)))
             self._bound_key = key
-        self._bound[0]()
-        self._bound[1]()
+        for call in self._bound:
+            call()
+
+    def step_separate(self, stream=None) -> None:
+        """The same step as two calls: paged_kv_append, then paged_attn_step."""
+        self.append(stream)
+        self.attend(stream)
+
+    def bind_step(self, stream):
+        plan, cfg = self.wl.plan, self.wl.cfg
+        return pk.bind_paged_append_attn_step(
+            self.pool, self.k_pool, self.v_pool, self.k_new, self.v_new, self.slot_mapping,
+            self.q, self.q_dtype, cfg.num_q_heads, self.k_scale, self.v_scale, self.block_tables,
+            plan.max_blocks_per_seq, self.context_lens, self.query_lens, plan.num_seqs,
+            plan.total_q_tokens, plan.max_context_len, plan.max_query_len, float(self.wl.scale),
+            self.out, self.workspace, self.ws_bytes, stream, shared_blocks=self.shared_blocks)
 
     def rebind(self) -> None:
         self._bound, self._bound_key = None, None

@@ -48,7 +48,7 @@ EXPORTS = ("paged_kv_append", "paged_attn_workspace_bytes", "paged_attn_step",
            "pkv_bm_enable_prefix_cache", "pkv_bm_add_prompt", "pkv_bm_extend_tokens",
            "pkv_bm_cache_stats", "pkv_prefix_keys", "pkv_bm_shared_prefix",
            "pkv_set_plan_override", "pkv_checks_enabled", "paged_attn_step_noalloc",
-           "paged_attn_scratch_bytes")
+           "paged_attn_scratch_bytes", "paged_append_attn_step")
 
 
 class PkvPool(ctypes.Structure):
@@ -90,6 +90,10 @@ def _declare(lib):
     lib.paged_attn_step.argtypes = [_POOLP, _P, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I,
                                      _I, _I, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
     lib.paged_attn_step.restype = ctypes.c_int
+    lib.paged_append_attn_step.argtypes = [_POOLP, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _I,
+                                           _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P,
+                                           ctypes.c_size_t, _P]
+    lib.paged_append_attn_step.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_kernel_name.argtypes = [_I]
@@ -251,6 +255,50 @@ def bind_paged_attn_step(pool: PkvPool, q, q_dtype: int, num_q_heads: int, k_poo
                    int(workspace_bytes), _stream(stream)),
                   (pool, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens,
                    query_lens, shared_blocks, out, workspace, stream))
+
+
+def _append_step_args(pool, k_pool, v_pool, k_new, v_new, slot_mapping, q, q_dtype, num_q_heads,
+                      k_scale, v_scale, block_tables, max_blocks_per_seq, context_lens,
+                      query_lens, num_seqs, total_q_tokens, max_context_len, max_query_len, scale,
+                      out, workspace, workspace_bytes, stream, shared_blocks):
+    return (_poolref(pool), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+            _ptr(slot_mapping), _ptr(q), int(q_dtype), int(num_q_heads), _ptr(k_scale),
+            _ptr(v_scale), _ptr(block_tables), int(max_blocks_per_seq), _ptr(context_lens),
+            _ptr(query_lens), _ptr(shared_blocks), int(num_seqs), int(total_q_tokens),
+            int(max_context_len), int(max_query_len), float(scale), _ptr(out), _ptr(workspace),
+            int(workspace_bytes), _stream(stream))
+
+
+def paged_append_attn_step(pool: PkvPool, k_pool, v_pool, k_new, v_new, slot_mapping, q,
+                           q_dtype: int, num_q_heads: int, k_scale, v_scale, block_tables,
+                           max_blocks_per_seq: int, context_lens, query_lens, num_seqs: int,
+                           total_q_tokens: int, max_context_len: int, max_query_len: int,
+                           scale: float, out, workspace, workspace_bytes: int, stream=None,
+                           shared_blocks=None, lib=None) -> None:
+    """The step's append (rows of the pool's element type, one per query row)
+    and its attention in one call."""
+    _check("paged_append_attn_step", (lib or _lib).paged_append_attn_step(*_append_step_args(
+        pool, k_pool, v_pool, k_new, v_new, slot_mapping, q, q_dtype, num_q_heads, k_scale,
+        v_scale, block_tables, max_blocks_per_seq, context_lens, query_lens, num_seqs,
+        total_q_tokens, max_context_len, max_query_len, scale, out, workspace, workspace_bytes,
+        stream, shared_blocks)))
+
+
+def bind_paged_append_attn_step(pool: PkvPool, k_pool, v_pool, k_new, v_new, slot_mapping, q,
+                                q_dtype: int, num_q_heads: int, k_scale, v_scale, block_tables,
+                                max_blocks_per_seq: int, context_lens, query_lens, num_seqs: int,
+                                total_q_tokens: int, max_context_len: int, max_query_len: int,
+                                scale: float, out, workspace, workspace_bytes: int, stream=None,
+                                shared_blocks=None):
+    """paged_append_attn_step with its arguments converted once; see bind_paged_kv_append."""
+    return _bound("paged_append_attn_step", _lib.paged_append_attn_step,
+                  _append_step_args(pool, k_pool, v_pool, k_new, v_new, slot_mapping, q, q_dtype,
+                                    num_q_heads, k_scale, v_scale, block_tables,
+                                    max_blocks_per_seq, context_lens, query_lens, num_seqs,
+                                    total_q_tokens, max_context_len, max_query_len, scale, out,
+                                    workspace, workspace_bytes, stream, shared_blocks),
+                  (pool, k_pool, v_pool, k_new, v_new, slot_mapping, q, k_scale, v_scale,
+                   block_tables, context_lens, query_lens, shared_blocks, out, workspace, stream))
 
 
 def _bound(name: str, fn, args, keep):

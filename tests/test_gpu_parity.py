@@ -342,6 +342,64 @@ def test_gpu_shared_hint_only_changes_the_load_policy(case):
 
 
 # ----------------------------------------------------------------------------
+# the append and the step in one call
+# ----------------------------------------------------------------------------
+FUSE_CASES = {
+    # name: (Hq, Hkv, D, kv, q dtype, context lens, query lens, append kernel launches)
+    "tiny_f16_d64": (4, 4, 64, W.F16, W.F16, [10, 40, 20, 80], [1, 1, 1, 1], 0),
+    "mha_bf16_ragged_split": (8, 8, 128, W.BF16, W.BF16, [1, 16, 17, 1024, 1025, 3001, 4096, 2047],
+                              [1] * 8, 0),
+    "g2_bf16": (16, 8, 128, W.BF16, W.BF16, [33, 700, 2049, 1], [1] * 4, 0),
+    # past the size below which the append goes into the decode launch
+    "mha_bf16_large": (8, 8, 128, W.BF16, W.BF16, [4096, 17, 2500, 1] * 4, [1] * 16, 1),
+    "gqa4_bf16_mfma": (16, 4, 128, W.BF16, W.BF16, [33, 700, 2049], [1] * 3, 1),
+    "fp8_gqa8": (16, 2, 128, W.FP8, W.BF16, [3000, 200, 2047], [1] * 3, 1),
+    "mixed_step": (8, 8, 128, W.BF16, W.BF16, [50, 700, 1300, 90], [1, 1, 300, 1], 1),
+}
+
+
+@pytest.mark.parametrize("case", sorted(FUSE_CASES))
+def test_append_and_step_in_one_call(case):
+    # paged_append_attn_step: small decode steps on the VALU kernel take the
+    # append into their launch (no append kernel runs; the appended row is
+    # attended after the pool's blocks, so the last bits may differ), every
+    # other step enqueues the append kernel first (then the output is the two
+    # calls', bit for bit).  Either way both whole pools equal paged_kv_append's
+    # and the output passes the oracle.
+    from paged_kv_cache_286_amd import pagedkv as pk
+    Hq, Hkv, D, kv, qd, lens, qlens, appends = FUSE_CASES[case]
+    nb = sum(-(-L // 16) for L in lens) + 9
+    wl = W.generate(W.custom_plan(W.Config("fuse", "fuse", Hq, Hkv, D, 16, nb, kv, qd, 61),
+                                  lens, qlens, 61))
+    _say(f"[gpu] append and step in one call: {case}")
+    ds = _device_step(wl)
+    assert ds.fusable
+    ds.step_separate()
+    torch.cuda.synchronize()
+    want = (ds.out_bits().copy(), ds.k_pool.cpu().numpy(), ds.v_pool.cpu().numpy())
+    ds.poison_appended_slots()
+    ds.out.fill_(0x1234)
+    pk.pkv_timing_enable(64)
+    try:
+        ds.step()
+        torch.cuda.synchronize()
+        pk.pkv_timing_collect()
+        launched = pk.pkv_timing_get(pk.PKV_KERNEL_APPEND)[1]
+    finally:
+        pk.pkv_timing_disable()
+    assert launched == appends
+    if appends:
+        assert np.array_equal(ds.out_bits(), want[0])
+    else:
+        qd_ = wl.plan.cfg.q_dtype
+        assert oracle.tolerance_ok(oracle.decode_bits(ds.out_bits(), qd_),
+                                   oracle.decode_bits(want[0], qd_), 2e-3, 1e-2).all()
+    assert np.array_equal(ds.k_pool.cpu().numpy(), want[1])
+    assert np.array_equal(ds.v_pool.cpu().numpy(), want[2])
+    _check(wl, ds)
+
+
+# ----------------------------------------------------------------------------
 # the append, bit for bit over whole pools
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("kv", [W.BF16, W.F16, W.FP8])
