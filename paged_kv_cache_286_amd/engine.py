@@ -13,8 +13,9 @@ Does", "Chunked Prefill", "Growing During Decode", "Shared Prefixes" and
 3. if the blocks for the step's tokens are short, the most recently admitted
    sequence is preempted (its blocks released; it is recomputed later);
 4. the step runs: copy-on-write block copies, the KV append of the step's new
-   rows, then attention for every query row (``paged_kv_copy_blocks``,
-   ``paged_kv_append``, ``paged_attn_step``);
+   rows, then attention for every query row (``paged_kv_copy_blocks``, then
+   ``paged_append_attn_step``, or ``paged_kv_append`` / ``paged_kv_append_quant``
+   and ``paged_attn_step``);
 5. finished sequences leave and release their blocks in the same step.
 
 Only the attention layer is modelled: queries, keys and values of the step's
@@ -35,7 +36,7 @@ from typing import Dict, List, Optional
 import numpy as np
 
 from . import pagedkv as pk
-from .device import check_slots_injective
+from .device import append_fusable, check_slots_injective
 
 
 @dataclasses.dataclass
@@ -362,13 +363,6 @@ class DeviceEngine:
                                     self.v_scale, pairs, len(batch.copies), stream)
         check_slots_injective(batch.slot_mapping, self.b.bm.num_blocks * self.b.block_size)
         slots = torch.from_numpy(batch.slot_mapping).to(self.dev)
-        if self.fp8:
-            pk.paged_kv_append_quant(self.pool, self.k_pool, self.v_pool, self.k_scale,
-                                     self.v_scale, k_new, v_new, self.code, self.new_block_scale,
-                                     self.new_block_scale, slots, rows, stream)
-        else:
-            pk.paged_kv_append(self.pool, self.k_pool, self.v_pool, k_new, v_new, self.code, slots,
-                               rows, stream)
         tables = torch.from_numpy(batch.block_tables).to(self.dev)
         ctx = torch.from_numpy(batch.context_lens).to(self.dev)
         ql = torch.from_numpy(batch.query_lens).to(self.dev)
@@ -378,9 +372,25 @@ class DeviceEngine:
         shared = None
         if batch.shared_blocks is not None and batch.shared_blocks.any():
             shared = torch.from_numpy(batch.shared_blocks).to(self.dev)
-        pk.paged_attn_step(self.pool, q, self.code, self.Hq, self.k_pool, self.v_pool,
-                           self.k_scale, self.v_scale, tables, self.b.max_blocks, ctx, ql, S, rows,
-                           max_ctx, max_q, self.scale, out, ws, ws_bytes, stream,
-                           shared_blocks=shared)
+        if not self.fp8 and append_fusable(batch.block_tables, batch.context_lens,
+                                           batch.query_lens, batch.slot_mapping):
+            # copy-on-write left every appended slot private: append and step in one call
+            pk.paged_append_attn_step(self.pool, self.k_pool, self.v_pool, k_new, v_new, slots, q,
+                                      self.code, self.Hq, self.k_scale, self.v_scale, tables,
+                                      self.b.max_blocks, ctx, ql, S, rows, max_ctx, max_q,
+                                      self.scale, out, ws, ws_bytes, stream, shared_blocks=shared)
+        else:
+            if self.fp8:
+                pk.paged_kv_append_quant(self.pool, self.k_pool, self.v_pool, self.k_scale,
+                                         self.v_scale, k_new, v_new, self.code,
+                                         self.new_block_scale, self.new_block_scale, slots, rows,
+                                         stream)
+            else:
+                pk.paged_kv_append(self.pool, self.k_pool, self.v_pool, k_new, v_new, self.code,
+                                   slots, rows, stream)
+            pk.paged_attn_step(self.pool, q, self.code, self.Hq, self.k_pool, self.v_pool,
+                               self.k_scale, self.v_scale, tables, self.b.max_blocks, ctx, ql, S,
+                               rows, max_ctx, max_q, self.scale, out, ws, ws_bytes, stream,
+                               shared_blocks=shared)
         self.last = (q, out, ws, k_new, v_new)
         return q, out
