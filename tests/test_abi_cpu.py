@@ -96,6 +96,31 @@ def test_step_validation():
                  workspace_bytes=need - 1) == pk.PKV_ERR_WORKSPACE
 
 
+def _append_step(pool, **kw):
+    a = dict(k_pool=FAKE, v_pool=FAKE, k_new=FAKE, v_new=FAKE, slot_mapping=FAKE, q=FAKE,
+             q_dtype=pk.PKV_BF16, num_q_heads=4, k_scale=None, v_scale=None, block_tables=FAKE,
+             max_blocks_per_seq=8, context_lens=FAKE, query_lens=FAKE, num_seqs=4,
+             total_q_tokens=4, max_context_len=100, max_query_len=1, scale=0.125, out=FAKE,
+             workspace=None, workspace_bytes=0)
+    a.update(kw)
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.paged_append_attn_step(pool, **a)
+    return e.value.status
+
+
+def test_append_and_step_validation():
+    # the checks of both calls, before anything is enqueued
+    p = _pool()
+    assert _append_step(p, k_new=None) == pk.PKV_ERR_NULL
+    assert _append_step(p, slot_mapping=None) == pk.PKV_ERR_NULL
+    assert _append_step(p, v_new=FAKE + 4) == pk.PKV_ERR_SHAPE        # misaligned rows
+    assert _append_step(p, q=None) == pk.PKV_ERR_NULL
+    assert _append_step(p, scale=-1.0) == pk.PKV_ERR_SHAPE
+    assert _append_step(p, total_q_tokens=5) == pk.PKV_ERR_SHAPE
+    assert _append_step(_pool(kv_dtype=7)) == pk.PKV_ERR_DTYPE
+    assert _append_step(None) == pk.PKV_ERR_NULL
+
+
 def test_workspace_sizes():
     p = _pool()
     assert pk.paged_attn_workspace_bytes(p, 0, 4, 0, 1, 1) == 0          # invalid: no sequences
