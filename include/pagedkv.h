@@ -167,7 +167,10 @@ size_t paged_attn_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_
  *   workspace       device scratch of at least paged_attn_workspace_bytes(...) bytes
  *                   (may be NULL when that is 0); clobbered.
  * Slots of a block past context_lens[i] are never mixed into the result, whatever
- * they hold (they are masked by selection, not by multiplying with zero). */
+ * they hold (they are masked by selection, not by multiplying with zero).
+ * PKV_ERR_UNSUPPORTED when one row's split-context partials over all heads
+ * (num_q_heads * ceil(max_context_len / partition) * head_dim float32) would
+ * pass 2^31 bytes. */
 int paged_attn_step(const pkv_pool* pool,
                     const void* q, int32_t q_dtype, int32_t num_q_heads,
                     const void* k_pool, const void* v_pool,

@@ -471,6 +471,10 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
 
   const Layout lay = layout_for(pool, num_seqs, num_q_heads, total_q_tokens, max_context_len,
                                 max_query_len);
+  // a decode workgroup addresses its heads' partial rows with 32-bit byte
+  // offsets from its first head's
+  if ((int64_t)num_q_heads * lay.max_parts * pool->head_dim * 4 > INT32_MAX)
+    return PKV_ERR_UNSUPPORTED;
   if (use_scratch) {
     if (lay.total > kScratchBytes) return PKV_ERR_SCRATCH;
     st = device_scratch(stream, &workspace);
@@ -514,6 +518,9 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
   p.chunk_entries = multi ? reinterpret_cast<const int32_t*>(ws + lay.chunk_entries_off) : nullptr;
   p.part_ml = lay.max_parts > 1 ? reinterpret_cast<float*>(ws + lay.ml_off) : nullptr;
   p.part_o = lay.max_parts > 1 ? reinterpret_cast<float*>(ws + lay.o_off) : nullptr;
+  // fp8 KV: partial outputs as bfloat16 (their rounding, 2^-9 of a partition's
+  // output, is far inside what the 3-bit mantissas of the keys and values leave)
+  p.part_bf16 = pool->kv_dtype == PKV_FP8_E4M3;
   p.num_blocks = pool->num_blocks;
   p.num_kv_heads = pool->num_kv_heads;
   p.num_q_heads = num_q_heads;

@@ -74,20 +74,31 @@ __global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
   if (nparts <= 1) return;
   const size_t rh = (size_t)row * p.num_q_heads + h;
   const float* ml = p.part_ml + rh * p.max_parts * 2;
-  const float* po = p.part_o + rh * p.max_parts * D;
   float M = -__builtin_inff();
   for (int q = 0; q < nparts; ++q) M = fmaxf(M, ml[2 * q]);
   float ls = 0.f;
   float o[D / 64];
 #pragma unroll
   for (int c = 0; c < D / 64; ++c) o[c] = 0.f;
-  for (int q = 0; q < nparts; ++q) {
-    const float f = __builtin_amdgcn_exp2f(ml[2 * q] - M);
-    ls = __builtin_fmaf(ml[2 * q + 1], f, ls);
+  // partial outputs are float32, or bfloat16 for fp8 KV (one branch per row)
+  auto merge = [&](auto elem) {
+    using E = decltype(elem);
+    const E* po = reinterpret_cast<const E*>(p.part_o) + rh * p.max_parts * D;
+    for (int q = 0; q < nparts; ++q) {
+      const float f = __builtin_amdgcn_exp2f(ml[2 * q] - M);
+      ls = __builtin_fmaf(ml[2 * q + 1], f, ls);
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c)
-      o[c] = __builtin_fmaf(po[(size_t)q * D + c * 64 + lane], f, o[c]);
-  }
+      for (int c = 0; c < D / 64; ++c) {
+        const E x = po[(size_t)q * D + c * 64 + lane];
+        float v;
+        if constexpr (sizeof(E) == 2) v = __uint_as_float((uint32_t)x << 16);
+        else v = x;
+        o[c] = __builtin_fmaf(v, f, o[c]);
+      }
+    }
+  };
+  if (p.part_bf16) merge(uint16_t{});
+  else merge(float{});
 #pragma unroll
   for (int c = 0; c < D / 64; ++c)
     reinterpret_cast<uint16_t*>(p.out)[rh * D + c * 64 + lane] = to_out_bits<QT>(o[c] / ls);

@@ -263,8 +263,9 @@ __device__ __forceinline__ void decode_valu_wg(const StepParams& p, int hx, int 
     lim = i < end ? min(16, Lw - b * 16) : 0;
     if ((unsigned)phys >= (unsigned)p.num_blocks) { phys = 0; lim = 0; }
     const size_t boff = ((size_t)phys * p.num_kv_heads + kvh) * T::BLKB;
-    // a block with no tokens is not read (the count kept scalar: no waterfall loop)
-    const int bytes = __builtin_amdgcn_readfirstlane(lim > 0 ? T::BLKB : 0);
+    // only the block's rows inside the context are read (none for a block with
+    // no tokens; the count kept scalar: no waterfall loop)
+    const int bytes = __builtin_amdgcn_readfirstlane(lim * T::ROWB);
     const __amdgpu_buffer_rsrc_t kres = block_rsrc(p.k_pool + boff, bytes);
     const __amdgpu_buffer_rsrc_t vres = block_rsrc(p.v_pool + boff, bytes);
 #pragma unroll
@@ -344,6 +345,14 @@ __device__ __forceinline__ void decode_valu_wg(const StepParams& p, int hx, int 
   }
   __syncthreads();
 
+  // the GB partial rows of this workgroup lie max_parts rows apart, from the
+  // first head's; fp8 KV keeps them as bfloat16, else float32
+  constexpr int PB = KV == kFP8 ? 2 : 4;
+  const size_t idx0 = ((size_t)row * p.num_q_heads + h0) * p.max_parts + part;
+  const int64_t po_bytes = ((int64_t)(GB - 1) * p.max_parts + 1) * D * PB;
+  const __amdgpu_buffer_rsrc_t po_res =
+      block_rsrc(reinterpret_cast<const uint8_t*>(p.part_o) + idx0 * D * PB,
+                 po_bytes < INT32_MAX ? (int)po_bytes : INT32_MAX);
   for (int t = threadIdx.x; t < GB * D; t += kWaves * 64) {
     const int g = t / D;
     const int d = t - g * D;
@@ -362,7 +371,8 @@ __device__ __forceinline__ void decode_valu_wg(const StepParams& p, int hx, int 
       reinterpret_cast<uint16_t*>(p.out)[rh * D + d] = to_out_bits<QT>(o / ls);
     } else {
       const size_t idx = rh * p.max_parts + part;
-      p.part_o[idx * D + d] = o;
+      if constexpr (KV == kFP8) store_partial(po_res, (g * p.max_parts * D + d) * PB, to_out_bits<kBF16>(o));
+      else store_partial(po_res, (g * p.max_parts * D + d) * PB, o);
       if (d == 0) {
         p.part_ml[idx * 2] = M;
         p.part_ml[idx * 2 + 1] = ls;

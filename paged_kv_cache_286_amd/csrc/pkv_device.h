@@ -63,7 +63,9 @@ struct StepParams {
   const int32_t* q_start;    // [S + 1] row offsets (NULL when every query_len is 1)
   const int32_t* row_seq;    // [Tq] sequence of each row (NULL when every query_len is 1)
   float* part_ml;            // [Tq][Hq][max_parts][2]  (m in log2 units, l)
-  float* part_o;             // [Tq][Hq][max_parts][D]  unnormalised
+  float* part_o;             // [Tq][Hq][max_parts][D]  unnormalised; float32, or
+                             // bfloat16 (part_bf16: fp8 KV) in the first half
+  int32_t part_bf16;
   const int32_t* chunk_entries;  // [chunk_capacity][2] (sequence, first column) of prefill tiles
   const int32_t* chunk_count;    // number of valid chunk entries (written by the prologue)
   int32_t num_blocks;
@@ -133,6 +135,17 @@ template <bool NT>
 __device__ __forceinline__ uint4 load_block16(__amdgpu_buffer_rsrc_t r, int byte_off) {
   const u32x4_buf v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, NT ? 2 : 0);
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Stores of split-context partials (unnormalised output rows), which the
+// merge launch reads right after: with device scope (aux bit 4, sc1) rather
+// than the default policy, which measured slower in the VALU decode launch.
+constexpr int kPartialStore = 16;
+__device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t r, int byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, kPartialStore);
+}
+__device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t r, int byte_off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, byte_off, 0, kPartialStore);
 }
 
 // unpack a 16-byte load of KV elements into floats (8 for 16-bit types, 16 for fp8)

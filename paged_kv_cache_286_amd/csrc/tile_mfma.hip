@@ -960,11 +960,28 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
         for (int i4 = 0; i4 < 4; ++i4) orow[out_dim(j, i4)] = to_out_bits<QT>(o[t][j][i4] * inv);
     } else {
       const size_t idx = rh * it.max_parts + it.part;
-      float* po = p.part_o + idx * D;
+      if constexpr (KV == kFP8) {
+        // bfloat16 partials: the DT dims of (gq, i4) are consecutive, so each
+        // goes out as one DT * 2-byte store
+        static_assert(L::DT == 4 || L::DT == 8, "one 8- or 16-byte store per (gq, i4)");
+        uint16_t* po = reinterpret_cast<uint16_t*>(p.part_o) + idx * D;
 #pragma unroll
-      for (int j = 0; j < L::DT; ++j)
+        for (int i4 = 0; i4 < 4; ++i4) {
+          uint32_t w[L::DT / 2];
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) po[out_dim(j, i4)] = o[t][j][i4];
+          for (int j = 0; j < L::DT; j += 2) w[j / 2] = f32x2_to_bf16x2(o[t][j][i4], o[t][j + 1][i4]);
+          if constexpr (L::DT == 8)
+            *reinterpret_cast<uint4*>(po + out_dim(0, i4)) = make_uint4(w[0], w[1], w[2], w[3]);
+          else
+            *reinterpret_cast<uint2*>(po + out_dim(0, i4)) = make_uint2(w[0], w[1]);
+        }
+      } else {
+        float* po = p.part_o + idx * D;
+#pragma unroll
+        for (int j = 0; j < L::DT; ++j)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) po[out_dim(j, i4)] = o[t][j][i4];
+      }
       if (gq == 0) {
         p.part_ml[idx * 2] = m[t];
         p.part_ml[idx * 2 + 1] = lsum[t];

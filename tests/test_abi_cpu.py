@@ -84,6 +84,16 @@ def test_step_validation():
     assert _step(_pool(kv_dtype=7)) == pk.PKV_ERR_DTYPE
     assert _step(_pool(kv_dtype="fp8_e4m3")) == pk.PKV_ERR_NULL       # scales missing
     assert _step(None) == pk.PKV_ERR_NULL
+    # one row's partials over all heads must stay under 2^31 bytes (64 heads x
+    # 70,000 sixteen-token partitions x 128 floats: 2.29e9 bytes)
+    try:
+        pk.pkv_set_plan_override(part_tokens=16)
+        assert _step(_pool(num_kv_heads=64, head_dim=128), num_q_heads=64, max_blocks_per_seq=70000,
+                     max_context_len=16 * 70000) == pk.PKV_ERR_UNSUPPORTED
+        assert _step(_pool(num_kv_heads=64, head_dim=128), num_q_heads=64, max_blocks_per_seq=60000,
+                     max_context_len=16 * 60000) == pk.PKV_ERR_WORKSPACE
+    finally:
+        pk.pkv_set_plan_override()
     # a step this small runs unsplit: no workspace
     assert pk.paged_attn_workspace_bytes(p, 4, 4, 4, 100, 1) == 0
     # a split step needs a workspace (4 rows of up to 1000 tokens at head_dim 128
