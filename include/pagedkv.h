@@ -194,14 +194,15 @@ int paged_attn_step(const pkv_pool* pool,
  *                   one per query row, in query-row order.
  *   slot_mapping    [total_q_tokens] int32, as paged_kv_append.
  *   the rest        as paged_attn_step.
- * Small decode-only steps (max_query_len 1, num_seqs * max_context_len <= 32768)
- * of 16-bit KV whose rows run on the VALU decode kernel (at most two query
- * heads per kv head) do both in the decode launch: it stores each new row into
- * its slot and attends to it from k_new / v_new, after the pool's blocks, which
- * saves the append kernel's launch latency; the pools come out bit for bit the
- * same and the output the same up to that order's rounding.  Every other step
- * enqueues the append kernel first.  Returns the first failing check of either
- * call before anything is enqueued. */
+ * Decode-only steps (max_query_len 1) of 16-bit KV whose rows run on the VALU
+ * decode kernel (at most two query heads per kv head) take the append into the
+ * attention launches: the decode launch attends to each new row from k_new /
+ * v_new, after the pool's blocks, and the merge launch that follows it (in a
+ * step without one, the decode launch) stores the rows into their slots, which
+ * saves the append kernel's launch; the pools come out bit for bit the same and
+ * the output the same up to that order's rounding.  Every other step enqueues
+ * the append kernel first.  Returns the first failing check of either call
+ * before anything is enqueued. */
 int paged_append_attn_step(const pkv_pool* pool, void* k_pool, void* v_pool,
                            const void* k_new, const void* v_new, const int32_t* slot_mapping,
                            const void* q, int32_t q_dtype, int32_t num_q_heads,

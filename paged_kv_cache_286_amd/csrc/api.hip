@@ -435,13 +435,6 @@ struct FusedAppend {
   const int32_t* slots;
 };
 
-// Decode steps of at most this many (sequence x context) tokens take their
-// append into the decode launch: there the separate append kernel's launch
-// latency is a large part of the step (the 4-sequence fp16 step: 10.2 ->
-// ~6 us); on larger steps the decode kernel grows by what the launch saves,
-// and the separate kernels keep each one's own time.
-constexpr int64_t kFuseAppendTokens = 32768;
-
 // paged_attn_step, paged_attn_step_noalloc (workspace from this device's
 // scratch array instead of the caller's) and paged_append_attn_step (fa: the
 // step's append goes first, or into the decode launch).
@@ -506,12 +499,25 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
   p.ctx_lens = context_lens;
   p.q_lens = query_lens;
   p.shared_blocks = shared_blocks;
+  // When every sequence has max_query_len rows (total_q == num_seqs * max_q) and
+  // that exceeds small_q, every row is a prompt row; if their partition covers
+  // the whole context no row has partitions to merge and the merge launch (one
+  // workgroup per row and four heads) is skipped.
+  const bool all_prompt_rows = multi && (int64_t)num_seqs * max_query_len == total_q_tokens &&
+                               max_query_len > lay.small_q;
+  const bool merge = lay.max_parts > 1 && !(all_prompt_rows && lay.chunk_max_parts == 1);
+  // Decode steps of 16-bit KV on the VALU decode kernel take their append: the
+  // decode launch attends to the new rows from k_new / v_new, and the merge
+  // launch after it (else the decode launch itself) stores them into the pool.
+  // Stores inside the decode launch cost its read stream about what the append
+  // kernel takes, so a step with a merge launch leaves them to that one: the
+  // append kernel's launch is saved either way.
   const bool fuse = fa != nullptr && !multi && !plan.decode_on_mfma && plan.heads_per_wg <= 2 &&
-                    pool->kv_dtype != PKV_FP8_E4M3 &&
-                    (int64_t)num_seqs * max_context_len <= kFuseAppendTokens;
+                    pool->kv_dtype != PKV_FP8_E4M3;
   p.k_new = fuse ? reinterpret_cast<const uint8_t*>(fa->k_new) : nullptr;
   p.v_new = fuse ? reinterpret_cast<const uint8_t*>(fa->v_new) : nullptr;
   p.slots = fuse ? fa->slots : nullptr;
+  p.append_in_merge = fuse && merge;
   p.q_start = multi ? reinterpret_cast<const int32_t*>(ws + lay.q_start_off) : nullptr;
   p.row_seq = multi ? reinterpret_cast<const int32_t*>(ws + lay.row_seq_off) : nullptr;
   p.chunk_count = multi ? reinterpret_cast<const int32_t*>(ws + lay.chunk_count_off) : nullptr;
@@ -560,13 +566,6 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
             ? timed_launch(PKV_KERNEL_DECODE_MFMA, s, [&] { return pkv::launch_decode_mfma(p, plan, s); })
             : timed_launch(PKV_KERNEL_DECODE, s, [&] { return pkv::launch_decode(p, plan, s); });
   }
-  // When every sequence has max_query_len rows (total_q == num_seqs * max_q) and
-  // that exceeds small_q, every row is a prompt row; if their partition covers
-  // the whole context no row has partitions to merge and the merge launch (one
-  // workgroup per row and four heads) is skipped.
-  const bool all_prompt_rows = multi && (int64_t)num_seqs * max_query_len == total_q_tokens &&
-                               max_query_len > lay.small_q;
-  const bool merge = lay.max_parts > 1 && !(all_prompt_rows && lay.chunk_max_parts == 1);
   if (e == hipSuccess && merge)
     e = timed_launch(PKV_KERNEL_REDUCE, s, [&] { return pkv::launch_reduce(p, plan, s); });
   return hip_status(e);

@@ -58,6 +58,10 @@ __global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
   const int h = (blockIdx.x - row * ng) * HPW + (HPW > 1 ? (int)(threadIdx.x >> 6) : 0);
   const int lane = threadIdx.x & 63;
   if (h >= p.num_q_heads) return;
+  // the step's append when the decode launch attended to the new rows from
+  // k_new / v_new: the wave of each kv head's first query head stores the row
+  if (p.append_in_merge && h % (p.num_q_heads / p.num_kv_heads) == 0)
+    store_appended_row<D>(p, row, h / (p.num_q_heads / p.num_kv_heads), lane);
   int L, pt;
   if (p.row_seq != nullptr) {
     const int seq = p.row_seq[row];

@@ -120,6 +120,24 @@ __device__ __forceinline__ void attend_block(const uint4 (&kr)[Lay<KV, D>::NL],
   }
 }
 
+// The row's new K and V (16-bit KV, head_dim D) into its slot for kv head kvh:
+// one 16-byte piece per lane, K on the first D/8 lanes, V on the next; a slot
+// outside the pool (or -1) stores nothing, as in the append kernel.
+template <int D>
+__device__ __forceinline__ void store_appended_row(const StepParams& p, int row, int kvh, int lane) {
+  constexpr int ROWB = D * 2, LPR = ROWB / 16;
+  const int slot = p.slots[row];
+  if (lane < 2 * LPR && slot >= 0 && (int64_t)slot < (int64_t)p.num_blocks * 16) {
+    const bool is_v = lane >= LPR;
+    const int piece = lane - (is_v ? LPR : 0);
+    const size_t src = ((size_t)row * p.num_kv_heads + kvh) * ROWB + piece * 16;
+    const size_t dst =
+        (((size_t)(slot >> 4) * p.num_kv_heads + kvh) * 16 + (slot & 15)) * ROWB + piece * 16;
+    const uint4 x = *reinterpret_cast<const uint4*>((is_v ? p.v_new : p.k_new) + src);
+    *reinterpret_cast<uint4*>(const_cast<uint8_t*>(is_v ? p.v_pool : p.k_pool) + dst) = x;
+  }
+}
+
 // One workgroup of the decode kernel: query heads hx*GB .. hx*GB+GB-1 of
 // sequence `seq`, partition `part` (the kernel's block indices; the step
 // kernel of mixed steps runs the same workgroups among its own).
@@ -143,33 +161,48 @@ __device__ __forceinline__ void decode_valu_wg(const StepParams& p, int hx, int 
     row = p.q_start[seq];
     if (row < 0 || row >= p.total_q) return;
   }
-  // Append taken into the decode launch (16-bit KV; small steps, where the
-  // launch latency of a separate append would dominate): wave 0 of the
-  // partition-0 workgroup of the first head group of each kv head (the
-  // writer) stores the row's new K and V into its slot, one 16-byte piece per
-  // lane (K on the first LPR lanes, V on the next), whatever the row's length
-  // says.  No workgroup of this launch reads that slot from the pool: the
-  // partition holding position L-1 attends to the row from k_new / v_new after
-  // the pool's blocks, in the wave the round-robin would have given the next
-  // block.  Both load their pieces before the walk and use them after it.
+  // Append taken into the decode step (16-bit KV): no workgroup of this launch
+  // reads the new rows' slots from the pool; the partition holding position
+  // L-1 attends to the row from k_new / v_new after the pool's blocks, in the
+  // wave the round-robin would have given the next block.  The rows reach the
+  // pool from the merge launch that follows when there is one
+  // (append_in_merge), else from this launch: wave 0 of the partition-0
+  // workgroup of the first head group of each kv head (the writer) stores the
+  // row's new K and V into its slot, one 16-byte piece per lane (K on the
+  // first LPR lanes, V on the next), whatever the row's length says.  Both
+  // load their pieces before the walk and use them after it.
   static_assert(!FUSED || KV != kFP8, "the append goes into 16-bit decode launches only");
   const int L = p.ctx_lens[seq];
   const int tok0 = part * p.part_tokens;
   const bool bad = tok0 >= L || L > p.max_blocks * 16 || L > p.max_parts * p.part_tokens;
   bool writer = false, has_new = false;
   uint4 kn = make_uint4(0, 0, 0, 0), vn = make_uint4(0, 0, 0, 0);
+  // each wave's copy of the new row (K, then V; lane l's piece at [l]), which
+  // holds no registers across the walk
+  __shared__ uint4 sm_new[FUSED ? kWaves : 1][2][64];
   if constexpr (FUSED) {
-    writer = part == 0 && hx % (group / GB) == 0 && wave == 0;
+    writer = !p.append_in_merge && part == 0 && hx % (group / GB) == 0 && wave == 0;
     const int walked = max(0, min(L + 14, tok0 + p.part_tokens) / 16 - tok0 / 16);   // blocks of [tok0, L-1)
     has_new = !bad && wave == walked % kWaves && L - 1 >= tok0 && L - 1 < tok0 + p.part_tokens;
-    // (buffer loads issued by every workgroup, moving bytes only where
-    // needed: a branch around them would leave the compiler unsure, at the
-    // block loop, which loads are still in flight)
+    // (LDS-destination buffer loads issued by every wave, moving bytes only
+    // where needed: a branch around them would leave the compiler unsure, at
+    // the block loop, which loads are still in flight)
     const size_t roff = ((size_t)row * p.num_kv_heads + kvh) * T::ROWB;
     const int new_bytes = __builtin_amdgcn_readfirstlane((writer || has_new) ? T::ROWB : 0);
-    kn = load_block16<false>(block_rsrc(p.k_new + roff, new_bytes), (lane % T::LPR) * 16);
-    vn = load_block16<false>(block_rsrc(p.v_new + roff, new_bytes), (lane % T::LPR) * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(block_rsrc(p.k_new + roff, new_bytes),
+                                             (__attribute__((address_space(3))) void*)sm_new[wave][0],
+                                             16, (lane % T::LPR) * 16, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(block_rsrc(p.v_new + roff, new_bytes),
+                                             (__attribute__((address_space(3))) void*)sm_new[wave][1],
+                                             16, (lane % T::LPR) * 16, 0, 0, 0);
   }
+  // this wave's pieces of the new row, once its loads have landed
+  auto fetch_new = [&]() {
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    kn = sm_new[wave][0][lane];
+    vn = sm_new[wave][1][lane];
+  };
   // (the pieces passed by value: a lambda holding them by reference kept them
   // in private memory)
   auto store_new = [&](uint4 kv_k, uint4 kv_v) {
@@ -184,7 +217,10 @@ __device__ __forceinline__ void decode_valu_wg(const StepParams& p, int hx, int 
   // rows whose length breaks the host scalars' promises are left unwritten
   if (bad) {
     if constexpr (FUSED) {
-      if (writer) store_new(kn, vn);
+      if (writer) {
+        fetch_new();
+        store_new(kn, vn);
+      }
     }
     return;
   }
@@ -299,6 +335,7 @@ __device__ __forceinline__ void decode_valu_wg(const StepParams& p, int hx, int 
   // the appended row, as a block of one token: every lane takes its piece of
   // the row, and only token row 0 counts
   if constexpr (FUSED) {
+    if (has_new || writer) fetch_new();
     if (has_new) {
 #pragma unroll
       for (int j = 0; j < T::NL; ++j) {

@@ -60,6 +60,7 @@ struct StepParams {
   const uint8_t* k_new;
   const uint8_t* v_new;
   const int32_t* slots;
+  int32_t append_in_merge;   // with k_new: the merge launch, not the decode launch, stores them
   const int32_t* q_start;    // [S + 1] row offsets (NULL when every query_len is 1)
   const int32_t* row_seq;    // [Tq] sequence of each row (NULL when every query_len is 1)
   float* part_ml;            // [Tq][Hq][max_parts][2]  (m in log2 units, l)
@@ -136,6 +137,10 @@ __device__ __forceinline__ uint4 load_block16(__amdgpu_buffer_rsrc_t r, int byte
   const u32x4_buf v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, NT ? 2 : 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+
+// s_waitcnt immediate (gfx9 fields): no vector memory and no LDS/scalar
+// operation outstanding
+constexpr int kWaitAll = 0x0070;
 
 // Stores of split-context partials (unnormalised output rows), which the
 // merge launch reads right after: with device scope (aux bit 4, sc1) rather

@@ -241,7 +241,6 @@ struct StageLay {
   // LDS of one stage; stage 0 also holds the decode items' merge buffer
   static constexpr int STAGE0 = CHUNKS > 2 * 16 * D / 4 ? CHUNKS : 2 * 16 * D / 4;
 };
-constexpr int kWaitAll = 0x0070;   // vmcnt 0, lgkmcnt 0
 
 template <int KV, int D>
 struct BlockRegs {

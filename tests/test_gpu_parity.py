@@ -350,8 +350,8 @@ FUSE_CASES = {
     "mha_bf16_ragged_split": (8, 8, 128, W.BF16, W.BF16, [1, 16, 17, 1024, 1025, 3001, 4096, 2047],
                               [1] * 8, 0),
     "g2_bf16": (16, 8, 128, W.BF16, W.BF16, [33, 700, 2049, 1], [1] * 4, 0),
-    # past the size below which the append goes into the decode launch
-    "mha_bf16_large": (8, 8, 128, W.BF16, W.BF16, [4096, 17, 2500, 1] * 4, [1] * 16, 1),
+    "mha_bf16_large": (8, 8, 128, W.BF16, W.BF16, [4096, 17, 2500, 1] * 4, [1] * 16, 0),
+    # the MFMA decode, fp8 KV and mixed steps enqueue the append kernel
     "gqa4_bf16_mfma": (16, 4, 128, W.BF16, W.BF16, [33, 700, 2049], [1] * 3, 1),
     "fp8_gqa8": (16, 2, 128, W.FP8, W.BF16, [3000, 200, 2047], [1] * 3, 1),
     "mixed_step": (8, 8, 128, W.BF16, W.BF16, [50, 700, 1300, 90], [1, 1, 300, 1], 1),
@@ -360,12 +360,13 @@ FUSE_CASES = {
 
 @pytest.mark.parametrize("case", sorted(FUSE_CASES))
 def test_append_and_step_in_one_call(case):
-    # paged_append_attn_step: small decode steps on the VALU kernel take the
-    # append into their launch (no append kernel runs; the appended row is
-    # attended after the pool's blocks, so the last bits may differ), every
-    # other step enqueues the append kernel first (then the output is the two
-    # calls', bit for bit).  Either way both whole pools equal paged_kv_append's
-    # and the output passes the oracle.
+    # paged_append_attn_step: decode steps on the VALU kernel take the append
+    # into their launches (no append kernel runs; the appended row is attended
+    # after the pool's blocks, so the last bits may differ; the merge launch
+    # stores the rows of split steps, the decode launch those of the others),
+    # every other step enqueues the append kernel first (then the output is the
+    # two calls', bit for bit).  Either way both whole pools equal
+    # paged_kv_append's and the output passes the oracle.
     from paged_kv_cache_286_amd import pagedkv as pk
     Hq, Hkv, D, kv, qd, lens, qlens, appends = FUSE_CASES[case]
     nb = sum(-(-L // 16) for L in lens) + 9
