@@ -512,12 +512,17 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
   // Stores inside the decode launch cost its read stream about what the append
   // kernel takes, so a step with a merge launch leaves them to that one: the
   // append kernel's launch is saved either way.
+  // Steps with prefill chunks (16-bit KV) store the rows from the prologue
+  // launch that runs before their step kernel anyway.
   const bool fuse = fa != nullptr && !multi && !plan.decode_on_mfma && plan.heads_per_wg <= 2 &&
                     pool->kv_dtype != PKV_FP8_E4M3;
-  p.k_new = fuse ? reinterpret_cast<const uint8_t*>(fa->k_new) : nullptr;
-  p.v_new = fuse ? reinterpret_cast<const uint8_t*>(fa->v_new) : nullptr;
-  p.slots = fuse ? fa->slots : nullptr;
+  const bool fuse_prologue = fa != nullptr && multi && pool->kv_dtype != PKV_FP8_E4M3;
+  p.k_new = fuse || fuse_prologue ? reinterpret_cast<const uint8_t*>(fa->k_new) : nullptr;
+  p.v_new = fuse || fuse_prologue ? reinterpret_cast<const uint8_t*>(fa->v_new) : nullptr;
+  p.slots = fuse || fuse_prologue ? fa->slots : nullptr;
   p.append_in_merge = fuse && merge;
+  p.append_rows = fuse_prologue ? total_q_tokens : 0;
+  p.append_row_bytes = pool->head_dim * elem_bytes(pool->kv_dtype);
   p.q_start = multi ? reinterpret_cast<const int32_t*>(ws + lay.q_start_off) : nullptr;
   p.row_seq = multi ? reinterpret_cast<const int32_t*>(ws + lay.row_seq_off) : nullptr;
   p.chunk_count = multi ? reinterpret_cast<const int32_t*>(ws + lay.chunk_count_off) : nullptr;
@@ -553,7 +558,7 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
   hipError_t e = hipSuccess;
   if (kCheckBytes > 0)
     e = pkv::launch_check(p, reinterpret_cast<int32_t*>(ws), max_context_len, max_query_len, s);
-  if (e == hipSuccess && fa != nullptr && !fuse)
+  if (e == hipSuccess && fa != nullptr && !fuse && !fuse_prologue)
     e = enqueue_append(pool, fa->k_pool, fa->v_pool, fa->k_new, fa->v_new, fa->slots,
                        total_q_tokens, s);
   if (e != hipSuccess) return hip_status(e);

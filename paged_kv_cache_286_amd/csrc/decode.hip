@@ -131,7 +131,30 @@ __device__ __forceinline__ int block_scan_1024(int v, int32_t* wave_tot) {
 // query rows (shorter ones, e.g. speculative-decoding verify rows, run as
 // decode items).
 // One workgroup; only launched when some sequence has more than one row.
+// Workgroups 1 .. append_rows (16-bit KV with the step's append in this
+// launch) each store one row's new K and V into its slot first, as the append
+// kernel does: the step kernel after this launch reads them from the pool.
 __global__ __launch_bounds__(1024) void step_prologue_kernel(StepParams p) {
+  if (blockIdx.x > 0) {
+    const int row = blockIdx.x - 1;
+    const int slot = p.slots[row];
+    if (slot < 0 || (int64_t)slot >= (int64_t)p.num_blocks * 16) return;
+    const int rb = p.append_row_bytes;
+    const int pph = rb / 16;                                 // 16-byte pieces per (row, head)
+    const int per = p.num_kv_heads * pph;                    // pieces of K (then of V)
+    const size_t base = (size_t)row * p.num_kv_heads * rb;
+    const size_t blk = (size_t)(slot >> 4), off = (size_t)(slot & 15);
+    for (int j = threadIdx.x; j < 2 * per; j += blockDim.x) {
+      const bool is_v = j >= per;
+      const int jj = j - (is_v ? per : 0);
+      const int head = jj / pph;
+      const int piece = jj - head * pph;
+      const uint4 x = *reinterpret_cast<const uint4*>((is_v ? p.v_new : p.k_new) + base + (size_t)jj * 16);
+      *reinterpret_cast<uint4*>(const_cast<uint8_t*>(is_v ? p.v_pool : p.k_pool) +
+                                ((blk * p.num_kv_heads + head) * 16 + off) * rb + (size_t)piece * 16) = x;
+    }
+    return;
+  }
   constexpr int kBig = 256;                 // long sequences filled by the whole workgroup
   __shared__ int32_t wave_tot[16];
   __shared__ int32_t carry_rows, carry_tiles, n_big;
@@ -262,7 +285,7 @@ hipError_t launch_check(const StepParams& p, int32_t* record, int32_t max_ctx, i
 
 hipError_t launch_prologue(const StepParams& p, hipStream_t stream) {
   (void)hipGetLastError();   // drop an error some earlier, unrelated call left behind
-  hipLaunchKernelGGL(step_prologue_kernel, dim3(1), dim3(1024), 0, stream, p);
+  hipLaunchKernelGGL(step_prologue_kernel, dim3(1 + (uint32_t)p.append_rows), dim3(1024), 0, stream, p);
   return hipGetLastError();
 }
 

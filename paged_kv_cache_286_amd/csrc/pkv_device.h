@@ -61,6 +61,8 @@ struct StepParams {
   const uint8_t* v_new;
   const int32_t* slots;
   int32_t append_in_merge;   // with k_new: the merge launch, not the decode launch, stores them
+  int32_t append_rows;       // with k_new in a step with prefill chunks: rows the prologue launch stores
+  int32_t append_row_bytes;  // bytes of one (row, kv head) of k_new / v_new
   const int32_t* q_start;    // [S + 1] row offsets (NULL when every query_len is 1)
   const int32_t* row_seq;    // [Tq] sequence of each row (NULL when every query_len is 1)
   float* part_ml;            // [Tq][Hq][max_parts][2]  (m in log2 units, l)
