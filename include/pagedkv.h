@@ -200,12 +200,15 @@ int paged_attn_step(const pkv_pool* pool,
  * v_new, after the pool's blocks, and the merge launch that follows it (in a
  * step without one, the decode launch) stores the rows into their slots, which
  * saves the append kernel's launch; the pools come out bit for bit the same and
- * the output the same up to that order's rounding.  Steps with prefill chunks
- * (max_query_len > 1) of 16-bit KV store the rows from the launch that lists
- * the chunks, before the attention reads them (output bit for bit the two
- * calls').  Every other step (fp8 KV, decode rows on the MFMA kernel)
- * enqueues the append kernel first.  Returns the first failing check of either
- * call before anything is enqueued. */
+ * the output the same up to that order's rounding.  Split decode-only steps on
+ * the MFMA decode kernel (more query heads per kv head, or fp8 KV) leave key
+ * L-1 out of the decode launch; the merge launch adds it from k_new / v_new
+ * (fp8 rows dequantised with the scales of the block they go to) and stores the
+ * rows.  Steps with prefill chunks (max_query_len > 1) of 16-bit KV store the
+ * rows from the launch that lists the chunks, before the attention reads them
+ * (output bit for bit the two calls').  Every other step (unsplit MFMA decode
+ * steps, fp8 steps with prefill chunks) enqueues the append kernel first.
+ * Returns the first failing check of either call before anything is enqueued. */
 int paged_append_attn_step(const pkv_pool* pool, void* k_pool, void* v_pool,
                            const void* k_new, const void* v_new, const int32_t* slot_mapping,
                            const void* q, int32_t q_dtype, int32_t num_q_heads,

@@ -517,10 +517,17 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
   const bool fuse = fa != nullptr && !multi && !plan.decode_on_mfma && plan.heads_per_wg <= 2 &&
                     pool->kv_dtype != PKV_FP8_E4M3;
   const bool fuse_prologue = fa != nullptr && multi && pool->kv_dtype != PKV_FP8_E4M3;
-  p.k_new = fuse || fuse_prologue ? reinterpret_cast<const uint8_t*>(fa->k_new) : nullptr;
-  p.v_new = fuse || fuse_prologue ? reinterpret_cast<const uint8_t*>(fa->v_new) : nullptr;
-  p.slots = fuse || fuse_prologue ? fa->slots : nullptr;
-  p.append_in_merge = fuse && merge;
+  // Split decode steps on the MFMA kernel (grouped-query and fp8 KV): the
+  // decode launch leaves key L-1 out, every row writes partials, and the
+  // merge launch adds that key from k_new / v_new and stores the rows.
+  const bool fuse_merge = fa != nullptr && !multi && plan.decode_on_mfma && merge;
+  const bool any_fuse = fuse || fuse_prologue || fuse_merge;
+  p.k_new = any_fuse ? reinterpret_cast<const uint8_t*>(fa->k_new) : nullptr;
+  p.v_new = any_fuse ? reinterpret_cast<const uint8_t*>(fa->v_new) : nullptr;
+  p.slots = any_fuse ? fa->slots : nullptr;
+  p.append_in_merge = (fuse && merge) || fuse_merge;
+  p.new_in_merge = fuse_merge;
+  p.kv_fp8 = pool->kv_dtype == PKV_FP8_E4M3;
   p.append_rows = fuse_prologue ? total_q_tokens : 0;
   p.append_row_bytes = pool->head_dim * elem_bytes(pool->kv_dtype);
   p.q_start = multi ? reinterpret_cast<const int32_t*>(ws + lay.q_start_off) : nullptr;
@@ -558,7 +565,7 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
   hipError_t e = hipSuccess;
   if (kCheckBytes > 0)
     e = pkv::launch_check(p, reinterpret_cast<int32_t*>(ws), max_context_len, max_query_len, s);
-  if (e == hipSuccess && fa != nullptr && !fuse && !fuse_prologue)
+  if (e == hipSuccess && fa != nullptr && !any_fuse)
     e = enqueue_append(pool, fa->k_pool, fa->v_pool, fa->k_new, fa->v_new, fa->slots,
                        total_q_tokens, s);
   if (e != hipSuccess) return hip_status(e);

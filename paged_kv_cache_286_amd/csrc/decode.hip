@@ -58,10 +58,56 @@ __global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
   const int h = (blockIdx.x - row * ng) * HPW + (HPW > 1 ? (int)(threadIdx.x >> 6) : 0);
   const int lane = threadIdx.x & 63;
   if (h >= p.num_q_heads) return;
-  // the step's append when the decode launch attended to the new rows from
-  // k_new / v_new: the wave of each kv head's first query head stores the row
-  if (p.append_in_merge && h % (p.num_q_heads / p.num_kv_heads) == 0)
-    store_appended_row<D>(p, row, h / (p.num_q_heads / p.num_kv_heads), lane);
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int kvh = h / G;
+  // the step's append when the decode launch read no new row from the pool:
+  // the wave of each kv head's first query head stores the row
+  if (p.append_in_merge && h % G == 0) {
+    if (p.kv_fp8) store_appended_row<D>(p, row, kvh, lane);
+    else store_appended_row<2 * D>(p, row, kvh, lane);
+  }
+  // new_in_merge: the partitions cover keys 0 .. L-2 (none when L is 1) and
+  // key L-1 is this row's new K/V, merged here as one more partition
+  const bool add_new = p.new_in_merge != 0;
+  const size_t rh = (size_t)row * p.num_q_heads + h;
+  float s_new = 0.f, v_new[D / 64];
+  if (add_new) {
+    // (before the row's length is known: its loads travel with the length's)
+    // score of the new key (log2 units, as the partitions' maxima) and its
+    // value, dequantised with the scales of the block the row goes to
+    const int slot = p.slots[row];
+    const bool in_pool = slot >= 0 && (int64_t)slot < (int64_t)p.num_blocks * 16;
+    const size_t sc = in_pool ? (size_t)(slot >> 4) * p.num_kv_heads + kvh : 0;
+    const float ksc = p.kv_fp8 && in_pool ? p.k_scale[sc] : 1.f;
+    const float vsc = p.kv_fp8 && in_pool ? p.v_scale[sc] : 1.f;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + rh * D;
+    const size_t nrow = (size_t)row * p.num_kv_heads + kvh;
+    float dot = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) {
+      const int d = c * 64 + lane;
+      const uint16_t qb = qrow[d];
+      const float qv = QT == kBF16 ? __uint_as_float((uint32_t)qb << 16)
+                                   : (float)__builtin_bit_cast(_Float16, qb);
+      float kv, vv, unused;
+      if (p.kv_fp8) {
+        fp8x2_to_f32<false>(p.k_new[nrow * D + d], kv, unused);
+        fp8x2_to_f32<false>(p.v_new[nrow * D + d], vv, unused);
+        kv *= ksc;
+        vv *= vsc;
+      } else {
+        const uint16_t kb = reinterpret_cast<const uint16_t*>(p.k_new)[nrow * D + d];
+        const uint16_t vb = reinterpret_cast<const uint16_t*>(p.v_new)[nrow * D + d];
+        kv = QT == kBF16 ? __uint_as_float((uint32_t)kb << 16) : (float)__builtin_bit_cast(_Float16, kb);
+        vv = QT == kBF16 ? __uint_as_float((uint32_t)vb << 16) : (float)__builtin_bit_cast(_Float16, vb);
+      }
+      dot = __builtin_fmaf(qv, kv, dot);
+      v_new[c] = vv;
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) dot += shfl_xor_f(dot, off);
+    s_new = dot * p.scale_log2;
+  }
   int L, pt;
   if (p.row_seq != nullptr) {
     const int seq = p.row_seq[row];
@@ -74,9 +120,8 @@ __global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
     pt = p.part_tokens;
   }
   if (L < 1 || L > p.max_blocks * 16 || L > p.max_parts * pt) return;
-  const int nparts = (L + pt - 1) / pt;
-  if (nparts <= 1) return;
-  const size_t rh = (size_t)row * p.num_q_heads + h;
+  const int nparts = ((add_new ? L - 1 : L) + pt - 1) / pt;
+  if (nparts <= 1 && !add_new) return;
   const float* ml = p.part_ml + rh * p.max_parts * 2;
   float M = -__builtin_inff();
   for (int q = 0; q < nparts; ++q) M = fmaxf(M, ml[2 * q]);
@@ -84,6 +129,7 @@ __global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
   float o[D / 64];
 #pragma unroll
   for (int c = 0; c < D / 64; ++c) o[c] = 0.f;
+  if (add_new) M = fmaxf(M, s_new);
   // partial outputs are float32, or bfloat16 for fp8 KV (one branch per row)
   auto merge = [&](auto elem) {
     using E = decltype(elem);
@@ -103,6 +149,12 @@ __global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
   };
   if (p.part_bf16) merge(uint16_t{});
   else merge(float{});
+  if (add_new) {
+    const float f = __builtin_amdgcn_exp2f(s_new - M);
+    ls += f;
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) o[c] = __builtin_fmaf(v_new[c], f, o[c]);
+  }
 #pragma unroll
   for (int c = 0; c < D / 64; ++c)
     reinterpret_cast<uint16_t*>(p.out)[rh * D + c * 64 + lane] = to_out_bits<QT>(o[c] / ls);

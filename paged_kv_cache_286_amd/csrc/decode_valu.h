@@ -120,12 +120,12 @@ __device__ __forceinline__ void attend_block(const uint4 (&kr)[Lay<KV, D>::NL],
   }
 }
 
-// The row's new K and V (16-bit KV, head_dim D) into its slot for kv head kvh:
-// one 16-byte piece per lane, K on the first D/8 lanes, V on the next; a slot
-// outside the pool (or -1) stores nothing, as in the append kernel.
-template <int D>
+// The row's new K and V (ROWB bytes per (row, kv head)) into its slot for kv
+// head kvh: one 16-byte piece per lane, K on the first ROWB/16 lanes, V on the
+// next; a slot outside the pool (or -1) stores nothing, as in the append kernel.
+template <int ROWB>
 __device__ __forceinline__ void store_appended_row(const StepParams& p, int row, int kvh, int lane) {
-  constexpr int ROWB = D * 2, LPR = ROWB / 16;
+  constexpr int LPR = ROWB / 16;
   const int slot = p.slots[row];
   if (lane < 2 * LPR && slot >= 0 && (int64_t)slot < (int64_t)p.num_blocks * 16) {
     const bool is_v = lane >= LPR;

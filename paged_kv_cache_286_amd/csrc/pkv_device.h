@@ -61,6 +61,10 @@ struct StepParams {
   const uint8_t* v_new;
   const int32_t* slots;
   int32_t append_in_merge;   // with k_new: the merge launch, not the decode launch, stores them
+  int32_t new_in_merge;      // with k_new (MFMA decode steps): the decode launch walks keys
+                             // 0 .. L-2 and leaves partials for every row; the merge launch
+                             // adds key L-1 from k_new / v_new
+  int32_t kv_fp8;            // the pools hold fp8-e4m3 (k_new / v_new too)
   int32_t append_rows;       // with k_new in a step with prefill chunks: rows the prologue launch stores
   int32_t append_row_bytes;  // bytes of one (row, kv head) of k_new / v_new
   const int32_t* q_start;    // [S + 1] row offsets (NULL when every query_len is 1)

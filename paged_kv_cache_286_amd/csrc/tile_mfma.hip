@@ -950,7 +950,7 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     if (!col_ok[t] || pos[t] < tok0) continue;     // no key of this partition is visible
     const size_t rh = (size_t)row[t] * p.num_q_heads + head[t];
     const int nparts = (pos[t] + it.part_tokens) / it.part_tokens;   // ceil((pos + 1) / pt)
-    if (nparts == 1) {
+    if (nparts == 1 && !p.new_in_merge) {
       const float inv = 1.f / lsum[t];
       uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + rh * D;
 #pragma unroll
@@ -1017,9 +1017,10 @@ __device__ __forceinline__ void decode_wg(const StepParams& p, int x, int seq, i
   it.ncols = it.Q * group;
   if (it.col0 >= it.ncols) return;
   it.L = uniform_load(p.ctx_lens + it.seq);
-  if (it.Q > it.L || it.part * it.part_tokens >= it.L || it.L > p.max_blocks * 16 ||
-      it.L > p.max_parts * it.part_tokens)
-    return;
+  if (it.Q > it.L || it.L > p.max_blocks * 16 || it.L > p.max_parts * it.part_tokens) return;
+  // the merge launch adds key L-1 (this step's new row) from k_new / v_new
+  if (p.new_in_merge) it.L -= 1;
+  if (it.Q > it.L || it.part * it.part_tokens >= it.L) return;
   tile_item<KV, QT, D, true>(p, it, group, sm_o, sm_m, sm_l, nullptr, nullptr, nullptr, nullptr, kst);
 }
 

@@ -330,6 +330,11 @@ def test_gpu_shared_hint_only_changes_the_load_policy(case):
     _check(wl, ds)
     assert ds.shared_blocks is not None
     assert ds.shared_blocks.cpu().tolist() == [40, 40, 0, 0, 40]
+    # (the step may have taken its append into the attention launches, which
+    # attends to the new rows in another order: compare attention calls only)
+    ds.out.zero_()
+    ds.attend()
+    torch.cuda.synchronize()
     want = ds.out_bits()
     S = len(lens)
     dev = ds.shared_blocks.device
@@ -354,14 +359,18 @@ FUSE_CASES = {
     # steps with prefill chunks store the rows from their prologue launch
     "mixed_step": (8, 8, 128, W.BF16, W.BF16, [50, 700, 1300, 90], [1, 1, 300, 1], 0),
     "mixed_f16_d64": (4, 2, 64, W.F16, W.F16, [37, 513, 16, 260], [1, 40, 16, 1], 0),
-    # the MFMA decode and fp8 KV enqueue the append kernel
-    "gqa4_bf16_mfma": (16, 4, 128, W.BF16, W.BF16, [33, 700, 2049], [1] * 3, 1),
-    "fp8_gqa8": (16, 2, 128, W.FP8, W.BF16, [3000, 200, 2047], [1] * 3, 1),
+    # split decode steps on the MFMA kernel: the merge launch adds the new key
+    # (a length-1 sequence has nothing else) and stores the rows
+    "gqa4_bf16_mfma": (16, 4, 128, W.BF16, W.BF16, [33, 700, 2049, 1], [1] * 4, 0),
+    "fp8_gqa8": (16, 2, 128, W.FP8, W.BF16, [3000, 200, 2047, 1, 17], [1] * 5, 0),
+    "fp8_gqa8_f16q_d64": (16, 2, 64, W.FP8, W.F16, [900, 1, 4000, 65], [1] * 4, 0),
+    # unsplit MFMA decode steps and fp8 steps with prefill chunks enqueue the append kernel
+    "gqa4_unsplit": (16, 4, 128, W.BF16, W.BF16, [10, 40, 100], [1] * 3, 1),
     "fp8_mixed": (16, 2, 128, W.FP8, W.BF16, [50, 700, 1300], [1, 200, 1], 1),
 }
 # cases whose attention reads every row from the pool: the output equals the
 # separate calls' bit for bit
-FUSE_EXACT = {"mixed_step", "mixed_f16_d64", "gqa4_bf16_mfma", "fp8_gqa8", "fp8_mixed"}
+FUSE_EXACT = {"mixed_step", "mixed_f16_d64", "gqa4_unsplit", "fp8_mixed"}
 
 
 @pytest.mark.parametrize("case", sorted(FUSE_CASES))
@@ -370,8 +379,10 @@ def test_append_and_step_in_one_call(case):
     # into their launches (no append kernel runs; the appended row is attended
     # after the pool's blocks, so the last bits may differ; the merge launch
     # stores the rows of split steps, the decode launch those of the others);
-    # 16-bit steps with prefill chunks store the rows from their prologue
-    # launch; every other step enqueues the append kernel first.  Where the
+    # split decode steps on the MFMA kernel leave the new key to the merge
+    # launch, which also stores the rows; 16-bit steps with prefill chunks
+    # store the rows from their prologue launch; every other step enqueues the
+    # append kernel first.  Where the
     # attention reads every row from the pool the output is the two calls',
     # bit for bit.  Either way both whole pools equal paged_kv_append's and
     # the output passes the oracle.
@@ -558,12 +569,10 @@ def test_append_quant_bit_exact_whole_pool(new_dtype):
     assert np.array_equal(gk2.cpu().numpy(), rk2)
 
 
-@pytest.mark.parametrize("seed", [1003, 1007, 1013, 1014, 1020])
-def test_no_writes_outside_workspace_and_output(seed):
+def _guarded_step(wl, label, one_call):
     # the step writes only its output rows and the first paged_attn_workspace_bytes
-    # bytes of the workspace: guard bytes after both stay as they were
-    case = _random_case(seed)
-    wl = _small(seed=seed, **case)
+    # bytes of the workspace: guard bytes after both stay as they were (with
+    # the append and the attention as two calls, or as paged_append_attn_step)
     ds = _device_step(wl)
     guard = 1 << 16
     n = ds.ws_bytes
@@ -572,21 +581,37 @@ def test_no_writes_outside_workspace_and_output(seed):
     out_full = torch.full((ds.out.shape[0] + 4,) + tuple(ds.out.shape[1:]), 0x5A5A,
                           dtype=ds.out.dtype, device="cuda:0")
     ds.out = out_full[:ds.out.shape[0]]
-    _say(f"[gpu] guard bytes seed={seed}: workspace {n} B, {ds.out.shape[0]} rows")
-    ds.append()
-    ds.attend()
+    _say(f"[gpu] guard bytes {label} one_call={one_call}: workspace {n} B, {ds.out.shape[0]} rows")
+    if one_call:
+        assert ds.fusable
+        ds.bind_step(torch.cuda.current_stream())()
+    else:
+        ds.append()
+        ds.attend()
     torch.cuda.synchronize()
     assert bool((ws[n:] == 0xAB).all()), "a write past the workspace"
     assert bool((out_full[ds.out.shape[0]:] == 0x5A5A).all()), "a write past the output rows"
     _check(wl, ds)
 
 
+@pytest.mark.parametrize("one_call", [False, True])
+@pytest.mark.parametrize("seed", [1003, 1007, 1013, 1014, 1020])
+def test_no_writes_outside_workspace_and_output(seed, one_call):
+    _guarded_step(_small(seed=seed, **_random_case(seed)), f"seed={seed}", one_call)
+
+
+@pytest.mark.parametrize("name", ["mha_bf16_d128_ragged", "gqa4_bf16_d128", "fp8_gqa8_bf16q_d128"])
+def test_decode_steps_in_one_call_write_nothing_outside(name):
+    # decode-only steps whose append goes into the attention launches (the
+    # VALU decode, the MFMA decode of grouped-query and fp8 KV)
+    _guarded_step(_small(seed=sorted(SMALL).index(name) + 900, **SMALL[name]), name, True)
+
+
 @pytest.mark.parametrize("name", ["gqa_decode", "decode_7b", "fp8_gqa_long"])
 def test_repeated_steps_bit_identical(name):
     # the same step run again gives the same bits: every reduction has a fixed
     # order (the decode items' K regrouping through LDS included), and the
-    # partitions of a split row are merged in partition order by whichever of
-    # their workgroups arrives last, reading the others' partials coherently
+    # merge launch combines a split row's partitions in partition order
     wl = W.generate(W.make_plan(name))
     ds = _run(wl, f"{name} repeated")
     first = ds.out.clone()
