@@ -64,27 +64,42 @@ def append_fusable(tables: np.ndarray, context_lens, query_lens, slot_mapping) -
     """True when a step meets paged_append_attn_step's contract: every appended
     row's slot is the one its table names for that row's position, and no block
     holding an appended slot is read by another sequence (the state
-    copy-on-write keeps a step in)."""
+    copy-on-write keeps a step in).  Linear in the step's table entries: this
+    runs on the host before every engine step."""
+    tables = np.asarray(tables)
     lens = np.asarray(context_lens, np.int64)
     qlens = np.asarray(query_lens, np.int64)
     slots = np.asarray(slot_mapping, np.int64)
-    seq = np.repeat(np.arange(len(lens)), qlens)
+    S = len(lens)
+    seq = np.repeat(np.arange(S), qlens)
     if len(seq) != len(slots) or len(seq) == 0:
         return False
-    pos = np.concatenate([np.arange(L - Q, L) for L, Q in zip(lens, qlens)])
+    # position of every row: L - Q .. L - 1 of its sequence
+    first = np.repeat(np.cumsum(qlens) - qlens, qlens)
+    pos = np.repeat(lens - qlens, qlens) + (np.arange(len(seq)) - first)
+    if pos.min() < 0 or (pos // 16).max() >= tables.shape[1]:
+        return False
     blk = tables[seq, pos // 16].astype(np.int64)
     if blk.min() < 0 or not np.array_equal(slots, blk * 16 + pos % 16):
         return False
+    # every table entry a sequence reads, with its reader
     nblk = (lens + 15) // 16
-    cols = np.arange(tables.shape[1])[None, :]
-    used = tables[cols < nblk[:, None]].astype(np.int64)
+    if nblk.max() > tables.shape[1]:
+        return False
+    starts = np.repeat(np.cumsum(nblk) - nblk, nblk)
+    col = np.arange(int(nblk.sum())) - starts
+    reader = np.repeat(np.arange(S), nblk)
+    used = tables[reader, col].astype(np.int64)
     if used.min() < 0:
         return False
-    owners = np.repeat(np.arange(len(lens)), nblk)
-    # distinct (block, sequence) pairs; a block with two of them is shared
-    pairs = np.unique(used * len(lens) + owners)
-    readers = np.bincount(pairs // len(lens), minlength=int(blk.max()) + 1)
-    return bool((readers[blk] <= 1).all())
+    # the sequence appending into each appended block; a block appended by two
+    # sequences, or read by a sequence other than its appender, breaks it
+    owner = np.full(int(max(used.max(), blk.max())) + 1, -1, np.int64)
+    owner[blk] = seq
+    if not np.array_equal(owner[blk], seq):
+        return False
+    o = owner[used]
+    return bool(((o < 0) | (o == reader)).all())
 
 
 # Gap between the K and the V pool when both come from one allocation.  Two

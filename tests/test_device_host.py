@@ -38,3 +38,44 @@ def test_a_slot_other_than_the_tables_breaks_it():
     # one slot per query row, no more, no fewer
     assert not append_fusable(t, [40, 45], [1, 1], good[:1])
     assert not append_fusable(t, [40, 45], [1, 1], np.concatenate([good, good[:1]]))
+
+
+def _fusable_by_definition(tables, lens, qlens, slots):
+    # the contract written out row by row and block by block
+    rows = [(s, L - Q + r) for s, (L, Q) in enumerate(zip(lens, qlens)) for r in range(Q)]
+    if len(rows) != len(slots) or not rows:
+        return False
+    reads = {s: [int(b) for b in tables[s][:(L + 15) // 16]] for s, L in enumerate(lens)}
+    if any(b < 0 for bs in reads.values() for b in bs):
+        return False
+    for (s, p), slot in zip(rows, slots):
+        b = int(tables[s][p // 16])
+        if b < 0 or slot != b * 16 + p % 16:
+            return False
+        if any(b in reads[t] for t in reads if t != s):
+            return False
+    return True
+
+
+def test_fusable_check_matches_its_definition_on_random_steps():
+    rng = np.random.default_rng(17)
+    for trial in range(300):
+        S = int(rng.integers(1, 7))
+        lens = rng.integers(1, 70, S)
+        qlens = np.minimum(rng.integers(1, 4, S), lens)
+        width = int(((lens + 15) // 16).max()) + int(rng.integers(0, 2))
+        nb = 24
+        tables = np.full((S, width), -1, np.int64)
+        for s in range(S):
+            n = (int(lens[s]) + 15) // 16
+            tables[s, :n] = rng.choice(nb, n, replace=False)
+        if rng.random() < 0.4 and S > 1:               # a shared block
+            a, b = rng.choice(S, 2, replace=False)
+            tables[b, 0] = tables[a, int(rng.integers(0, (lens[a] + 15) // 16))]
+        slots = _slots(tables, lens, qlens)
+        if rng.random() < 0.2:                          # a wrong slot
+            slots[int(rng.integers(0, len(slots)))] += 1
+        if rng.random() < 0.1:                          # an invalid entry in use
+            tables[0, 0] = -1
+        want = _fusable_by_definition(tables, lens.tolist(), qlens.tolist(), slots.tolist())
+        assert append_fusable(tables, lens, qlens, slots) == want, trial
