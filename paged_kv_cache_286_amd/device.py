@@ -89,12 +89,12 @@ def append_fusable(tables: np.ndarray, context_lens, query_lens, slot_mapping) -
     starts = np.repeat(np.cumsum(nblk) - nblk, nblk)
     col = np.arange(int(nblk.sum())) - starts
     reader = np.repeat(np.arange(S), nblk)
-    used = tables[reader, col].astype(np.int64)
+    used = tables.ravel()[reader * tables.shape[1] + col].astype(np.int64)
     if used.min() < 0:
         return False
     # the sequence appending into each appended block; a block appended by two
     # sequences, or read by a sequence other than its appender, breaks it
-    owner = np.full(int(max(used.max(), blk.max())) + 1, -1, np.int64)
+    owner = np.full(int(max(used.max(), blk.max())) + 1, -1, np.int32)
     owner[blk] = seq
     if not np.array_equal(owner[blk], seq):
         return False
