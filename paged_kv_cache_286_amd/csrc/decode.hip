@@ -91,10 +91,10 @@ __global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
                                    : (float)__builtin_bit_cast(_Float16, qb);
       float kv, vv, unused;
       if (p.kv_fp8) {
+        // (the scales apply to the sum and to the weight below, so the loads
+        // of the slot and then the scales overlap the dot product)
         fp8x2_to_f32<false>(p.k_new[nrow * D + d], kv, unused);
         fp8x2_to_f32<false>(p.v_new[nrow * D + d], vv, unused);
-        kv *= ksc;
-        vv *= vsc;
       } else {
         const uint16_t kb = reinterpret_cast<const uint16_t*>(p.k_new)[nrow * D + d];
         const uint16_t vb = reinterpret_cast<const uint16_t*>(p.v_new)[nrow * D + d];
@@ -106,7 +106,9 @@ __global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) dot += shfl_xor_f(dot, off);
-    s_new = dot * p.scale_log2;
+    s_new = dot * ksc * p.scale_log2;
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) v_new[c] *= vsc;
   }
   int L, pt;
   if (p.row_seq != nullptr) {
