@@ -364,6 +364,7 @@ FUSE_CASES = {
     "gqa4_bf16_mfma": (16, 4, 128, W.BF16, W.BF16, [33, 700, 2049, 1], [1] * 4, 0),
     "fp8_gqa8": (16, 2, 128, W.FP8, W.BF16, [3000, 200, 2047, 1, 17], [1] * 5, 0),
     "fp8_gqa8_f16q_d64": (16, 2, 64, W.FP8, W.F16, [900, 1, 4000, 65], [1] * 4, 0),
+    "gqa4_f16_d64": (8, 2, 64, W.F16, W.F16, [100, 1, 2500, 777, 16, 17], [1] * 6, 0),
     # unsplit MFMA decode steps and fp8 steps with prefill chunks enqueue the append kernel
     "gqa4_unsplit": (16, 4, 128, W.BF16, W.BF16, [10, 40, 100], [1] * 3, 1),
     "fp8_mixed": (16, 2, 128, W.FP8, W.BF16, [50, 700, 1300], [1, 200, 1], 1),
