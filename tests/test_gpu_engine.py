@@ -13,8 +13,22 @@ from paged_kv_cache_286_amd.engine import ContinuousBatcher, DeviceEngine, Reque
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("case", ["mha_d128", "gqa4_d64_tight_blocks"])
-def test_engine_steps_match_oracle(case):
+def test_engine_steps_match_oracle(case, split):
+    # split: 16-token partitions forced, so decode steps merge partitions and
+    # paged_append_attn_step stores the new rows from the merge launch (and, on
+    # the MFMA decode of the grouped-query case, adds the new key there)
+    from paged_kv_cache_286_amd import pagedkv as pk
+    if split:
+        pk.pkv_set_plan_override(part_tokens=16)
+    try:
+        _engine_steps(case)
+    finally:
+        pk.pkv_set_plan_override()
+
+
+def _engine_steps(case):
     if case == "mha_d128":
         Hq, Hkv, D, nb, budget = 4, 4, 128, 96, 80
     else:
@@ -96,7 +110,19 @@ def _ideal_pools(batch, reqs, tables_kv):
     return kp, vp, tables
 
 
-def test_engine_prefix_cache_hits_hold_the_prefilled_kv():
+@pytest.mark.parametrize("split", [False, True])
+def test_engine_prefix_cache_hits_hold_the_prefilled_kv(split):
+    # (split: 16-token partitions forced, as above)
+    from paged_kv_cache_286_amd import pagedkv as pk
+    if split:
+        pk.pkv_set_plan_override(part_tokens=16)
+    try:
+        _engine_prefix_cache()
+    finally:
+        pk.pkv_set_plan_override()
+
+
+def _engine_prefix_cache():
     # a pool this small makes the cache evict and the scheduler preempt
     Hq, Hkv, D, nb = 8, 2, 128, 24
     b = ContinuousBatcher(num_blocks=nb, max_seqs=6, token_budget=96, max_blocks_per_seq=32,
