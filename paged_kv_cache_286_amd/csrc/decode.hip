@@ -51,28 +51,46 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) 
 // the workgroups that only check and leave; decode steps keep one head per
 // workgroup.  grid.x = head group (fastest), then row.
 constexpr int kMultiReduceHeads = 4;
-template <int QT, int D, int HPW>
-__global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
-  const int ng = (p.num_q_heads + HPW - 1) / HPW;
-  const int row = blockIdx.x / ng;
-  const int h = (blockIdx.x - row * ng) * HPW + (HPW > 1 ? (int)(threadIdx.x >> 6) : 0);
-  const int lane = threadIdx.x & 63;
-  if (h >= p.num_q_heads) return;
+// One wave: query head h of row `row`, partials of type E (float32, or
+// bfloat16 for fp8 KV).  Every load that does not need the row's length is
+// issued first, so the wave waits on memory about once: this wave's piece of
+// the step's append, the (max, sum) of partitions 0..63 (lane q holds
+// partition q's; every row owns max_parts entries, read whether written or
+// not and masked once the length is known), with AHEAD (decode steps) the
+// rows of partitions 0..3, and on steps whose new key is merged here that key's
+// score and value.
+template <int QT, int D, typename E, bool AHEAD>
+__device__ __forceinline__ void reduce_wave(const StepParams& p, int row, int h, int lane) {
+  constexpr int C = D / 64;
+  constexpr int kAhead = 4;
   const int G = p.num_q_heads / p.num_kv_heads;
   const int kvh = h / G;
+  const size_t rh = (size_t)row * p.num_q_heads + h;
   // the step's append when the decode launch read no new row from the pool:
-  // the wave of each kv head's first query head stores the row
-  if (p.append_in_merge && h % G == 0) {
-    if (p.kv_fp8) store_appended_row<D>(p, row, kvh, lane);
-    else store_appended_row<2 * D>(p, row, kvh, lane);
+  // the wave of each kv head's first query head stores the row (last)
+  const bool appends = p.append_in_merge && h % G == 0;
+  U32x4 app{0, 0, 0, 0};
+  if (appends) app = p.kv_fp8 ? load_appended_piece<D>(p, row, kvh, lane) : load_appended_piece<2 * D>(p, row, kvh, lane);
+  const float* ml = p.part_ml + rh * p.max_parts * 2;
+  float2 ml0 = make_float2(-__builtin_inff(), 0.f);
+  if (lane < p.max_parts) ml0 = *reinterpret_cast<const float2*>(ml + 2 * lane);
+  const E* po = reinterpret_cast<const E*>(p.part_o) + rh * p.max_parts * D + lane;
+  // (decode steps only: steps with prefill chunks have many rows with
+  // nothing to merge.  The reduce runs only where max_parts > 1; past
+  // max_parts the last partition is read again and not used.)
+  const int ahead = AHEAD ? (p.max_parts < kAhead ? p.max_parts : kAhead) : 0;
+  E x0[kAhead][C];
+#pragma unroll
+  for (int u = 0; u < kAhead; ++u) {
+    const int q = u < ahead ? u : ahead - 1;
+#pragma unroll
+    for (int c = 0; c < C; ++c) x0[u][c] = AHEAD ? po[(size_t)q * D + c * 64] : E(0);
   }
   // new_in_merge: the partitions cover keys 0 .. L-2 (none when L is 1) and
   // key L-1 is this row's new K/V, merged here as one more partition
   const bool add_new = p.new_in_merge != 0;
-  const size_t rh = (size_t)row * p.num_q_heads + h;
-  float s_new = 0.f, v_new[D / 64];
+  float s_new = 0.f, v_new[C];
   if (add_new) {
-    // (before the row's length is known: its loads travel with the length's)
     // score of the new key (log2 units, as the partitions' maxima) and its
     // value, dequantised with the scales of the block the row goes to
     const int slot = p.slots[row];
@@ -84,7 +102,7 @@ __global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
     const size_t nrow = (size_t)row * p.num_kv_heads + kvh;
     float dot = 0.f;
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c) {
+    for (int c = 0; c < C; ++c) {
       const int d = c * 64 + lane;
       const uint16_t qb = qrow[d];
       const float qv = QT == kBF16 ? __uint_as_float((uint32_t)qb << 16)
@@ -108,58 +126,112 @@ __global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
     for (int off = 1; off < 64; off <<= 1) dot += shfl_xor_f(dot, off);
     s_new = dot * ksc * p.scale_log2;
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c) v_new[c] *= vsc;
+    for (int c = 0; c < C; ++c) v_new[c] *= vsc;
   }
-  int L, pt;
+  // the row's length and partition size
+  bool merge = true;
+  int L = 0, pt = 1;
   if (p.row_seq != nullptr) {
     const int seq = p.row_seq[row];
-    if ((unsigned)seq >= (unsigned)p.num_seqs) return;
-    const int qlen = p.q_lens[seq];
-    L = p.ctx_lens[seq] - qlen + (row - p.q_start[seq]) + 1;
-    pt = qlen > p.small_q ? p.chunk_part_tokens : p.part_tokens;
+    if ((unsigned)seq < (unsigned)p.num_seqs) {
+      const int qlen = p.q_lens[seq];
+      L = p.ctx_lens[seq] - qlen + (row - p.q_start[seq]) + 1;
+      pt = qlen > p.small_q ? p.chunk_part_tokens : p.part_tokens;
+    } else {
+      merge = false;
+    }
   } else {
     L = p.ctx_lens[row];
     pt = p.part_tokens;
   }
-  if (L < 1 || L > p.max_blocks * 16 || L > p.max_parts * pt) return;
-  const int nparts = ((add_new ? L - 1 : L) + pt - 1) / pt;
-  if (nparts <= 1 && !add_new) return;
-  const float* ml = p.part_ml + rh * p.max_parts * 2;
-  float M = -__builtin_inff();
-  for (int q = 0; q < nparts; ++q) M = fmaxf(M, ml[2 * q]);
-  float ls = 0.f;
-  float o[D / 64];
+  if (L < 1 || L > p.max_blocks * 16 || L > p.max_parts * pt) merge = false;
+  const int nparts = merge ? ((add_new ? L - 1 : L) + pt - 1) / pt : 0;
+  if (nparts <= 1 && !add_new) merge = false;
+  if (merge) {
+    const float m_first = lane < nparts ? ml0.x : -__builtin_inff();
+    const float l_first = lane < nparts ? ml0.y : 0.f;
+    float M = m_first;
+    for (int q = lane + 64; q < nparts; q += 64) M = fmaxf(M, ml[2 * q]);
+    M = wave_max(M);
+    if (add_new) M = fmaxf(M, s_new);
+    float ls = 0.f;
+    float o[C];
 #pragma unroll
-  for (int c = 0; c < D / 64; ++c) o[c] = 0.f;
-  if (add_new) M = fmaxf(M, s_new);
-  // partial outputs are float32, or bfloat16 for fp8 KV (one branch per row)
-  auto merge = [&](auto elem) {
-    using E = decltype(elem);
-    const E* po = reinterpret_cast<const E*>(p.part_o) + rh * p.max_parts * D;
-    for (int q = 0; q < nparts; ++q) {
-      const float f = __builtin_amdgcn_exp2f(ml[2 * q] - M);
-      ls = __builtin_fmaf(ml[2 * q + 1], f, ls);
+    for (int c = 0; c < C; ++c) o[c] = 0.f;
+    // partitions are added in index order, 64 at a time: lane j holds the
+    // weight of partition base + j, read back with readlane, and the rows of
+    // four partitions are loaded together
+    for (int base = 0; base < nparts; base += 64) {
+      float mq = m_first, lq = l_first;
+      if (base > 0) {
+        const int q = base + lane;
+        mq = q < nparts ? ml[2 * q] : -__builtin_inff();
+        lq = q < nparts ? ml[2 * q + 1] : 0.f;
+      }
+      const float fq = __builtin_amdgcn_exp2f(mq - M);
+      const int n = nparts - base < 64 ? nparts - base : 64;
+      auto add = [&](int j, const E* x) {
+        const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fq), j));
+        const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lq), j));
+        ls = __builtin_fmaf(l, f, ls);
 #pragma unroll
-      for (int c = 0; c < D / 64; ++c) {
-        const E x = po[(size_t)q * D + c * 64 + lane];
-        float v;
-        if constexpr (sizeof(E) == 2) v = __uint_as_float((uint32_t)x << 16);
-        else v = x;
-        o[c] = __builtin_fmaf(v, f, o[c]);
+        for (int c = 0; c < C; ++c) {
+          float v;
+          if constexpr (sizeof(E) == 2) v = __uint_as_float((uint32_t)x[c] << 16);
+          else v = x[c];
+          o[c] = __builtin_fmaf(v, f, o[c]);
+        }
+      };
+      const E* pb = po + (size_t)base * D;
+      int j = 0;
+      if (base == 0) {
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u)
+          if (u < ahead && u < n) add(u, x0[u]);
+        j = ahead < n ? ahead : n;
+      }
+      for (; j + 4 <= n; j += 4) {
+        E x[4][C];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int c = 0; c < C; ++c) x[u][c] = pb[(size_t)(j + u) * D + c * 64];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) add(j + u, x[u]);
+      }
+      for (; j < n; ++j) {
+        E x[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) x[c] = pb[(size_t)j * D + c * 64];
+        add(j, x);
       }
     }
-  };
-  if (p.part_bf16) merge(uint16_t{});
-  else merge(float{});
-  if (add_new) {
-    const float f = __builtin_amdgcn_exp2f(s_new - M);
-    ls += f;
+    if (add_new) {
+      const float f = __builtin_amdgcn_exp2f(s_new - M);
+      ls += f;
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c) o[c] = __builtin_fmaf(v_new[c], f, o[c]);
+      for (int c = 0; c < C; ++c) o[c] = __builtin_fmaf(v_new[c], f, o[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      reinterpret_cast<uint16_t*>(p.out)[rh * D + c * 64 + lane] = to_out_bits<QT>(o[c] / ls);
   }
-#pragma unroll
-  for (int c = 0; c < D / 64; ++c)
-    reinterpret_cast<uint16_t*>(p.out)[rh * D + c * 64 + lane] = to_out_bits<QT>(o[c] / ls);
+  if (appends) {
+    if (p.kv_fp8) store_appended_piece<D>(p, row, kvh, lane, app);
+    else store_appended_piece<2 * D>(p, row, kvh, lane, app);
+  }
+}
+
+template <int QT, int D, int HPW>
+__global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
+  const int ng = (p.num_q_heads + HPW - 1) / HPW;
+  const int row = blockIdx.x / ng;
+  const int h = (blockIdx.x - row * ng) * HPW + (HPW > 1 ? (int)(threadIdx.x >> 6) : 0);
+  const int lane = threadIdx.x & 63;
+  if (h >= p.num_q_heads) return;
+  // one head per workgroup on decode steps, which read partitions ahead
+  if (p.part_bf16) reduce_wave<QT, D, uint16_t, HPW == 1>(p, row, h, lane);
+  else reduce_wave<QT, D, float, HPW == 1>(p, row, h, lane);
 }
 
 // inclusive scan of v over the 1024 threads of the workgroup

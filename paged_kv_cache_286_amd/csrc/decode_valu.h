@@ -138,6 +138,47 @@ __device__ __forceinline__ void store_appended_row(const StepParams& p, int row,
   }
 }
 
+// The same piece in two halves, so that other loads can go between them:
+// load_appended_piece reads the lane's piece of the new row (whatever the
+// slot: the step's new rows all exist), store_appended_piece writes it to the
+// row's slot.  The pointers are taken into scalar registers and accessed as
+// global memory: a per-lane choice between two kernel arguments otherwise
+// becomes a vector load of the chosen pointer, and a flat access would also
+// hold back every later wait on scalar loads.
+typedef uint32_t U32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) U32x4 GlobalU32x4;
+__device__ __forceinline__ GlobalU32x4* global_uniform(const void* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (GlobalU32x4*)(((uint64_t)hi << 32) | lo);
+}
+template <int ROWB>
+__device__ __forceinline__ U32x4 load_appended_piece(const StepParams& p, int row, int kvh, int lane) {
+  constexpr int LPR = ROWB / 16;
+  U32x4 x{0, 0, 0, 0};
+  GlobalU32x4* src_k = global_uniform(p.k_new);
+  GlobalU32x4* src_v = global_uniform(p.v_new);
+  if (lane < 2 * LPR) {
+    const bool is_v = lane >= LPR;
+    const int piece = lane - (is_v ? LPR : 0);
+    x = (is_v ? src_v : src_k)[((size_t)row * p.num_kv_heads + kvh) * LPR + piece];
+  }
+  return x;
+}
+template <int ROWB>
+__device__ __forceinline__ void store_appended_piece(const StepParams& p, int row, int kvh, int lane, U32x4 x) {
+  constexpr int LPR = ROWB / 16;
+  GlobalU32x4* dst_k = global_uniform(p.k_pool);
+  GlobalU32x4* dst_v = global_uniform(p.v_pool);
+  const int slot = uniform_load(p.slots + row);
+  if (lane < 2 * LPR && slot >= 0 && (int64_t)slot < (int64_t)p.num_blocks * 16) {
+    const bool is_v = lane >= LPR;
+    const int piece = lane - (is_v ? LPR : 0);
+    (is_v ? dst_v : dst_k)[(((size_t)(slot >> 4) * p.num_kv_heads + kvh) * 16 + (slot & 15)) * LPR + piece] = x;
+  }
+}
+
 // One workgroup of the decode kernel: query heads hx*GB .. hx*GB+GB-1 of
 // sequence `seq`, partition `part` (the kernel's block indices; the step
 // kernel of mixed steps runs the same workgroups among its own).

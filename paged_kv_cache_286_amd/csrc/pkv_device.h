@@ -118,6 +118,14 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& a, float& b) {
 __device__ __forceinline__ int uniform_load(const int32_t* ptr) {
   return __builtin_amdgcn_readfirstlane(*ptr);
 }
+// a pointer every lane holds alike, in scalar registers
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
 
 // Buffer-resource loads of one K or V block.  The resource's record count
 // covers the block's existing token rows only (0 for a block that counts no
@@ -244,6 +252,14 @@ __device__ __forceinline__ float max_xor16(float v) {
 __device__ __forceinline__ float max_xor32(float v) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
   return fmaxf(__int_as_float(p[0]), __int_as_float(p[1]));
+}
+// maximum over the 64 lanes of a fully active wave, in every lane
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+  return max_xor32(max_xor16(v));
 }
 __device__ __forceinline__ float sum_xor16(float v) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
