@@ -63,6 +63,7 @@ template <int QT, int D, typename E, bool AHEAD>
 __device__ __forceinline__ void reduce_wave(const StepParams& p, int row, int h, int lane) {
   constexpr int C = D / 64;
   constexpr int kAhead = 4;
+  constexpr bool FP8 = sizeof(E) == 2;   // bfloat16 partials exactly when the KV is fp8
   const int G = p.num_q_heads / p.num_kv_heads;
   const int kvh = h / G;
   const size_t rh = (size_t)row * p.num_q_heads + h;
@@ -70,7 +71,7 @@ __device__ __forceinline__ void reduce_wave(const StepParams& p, int row, int h,
   // the wave of each kv head's first query head stores the row (last)
   const bool appends = p.append_in_merge && h % G == 0;
   U32x4 app{0, 0, 0, 0};
-  if (appends) app = p.kv_fp8 ? load_appended_piece<D>(p, row, kvh, lane) : load_appended_piece<2 * D>(p, row, kvh, lane);
+  if (appends) app = load_appended_piece<FP8 ? D : 2 * D>(p, row, kvh, lane);
   const float* ml = p.part_ml + rh * p.max_parts * 2;
   float2 ml0 = make_float2(-__builtin_inff(), 0.f);
   if (lane < p.max_parts) ml0 = *reinterpret_cast<const float2*>(ml + 2 * lane);
@@ -86,18 +87,32 @@ __device__ __forceinline__ void reduce_wave(const StepParams& p, int row, int h,
 #pragma unroll
     for (int c = 0; c < C; ++c) x0[u][c] = AHEAD ? po[(size_t)q * D + c * 64] : E(0);
   }
+  // the row's length and partition size
+  bool merge = true;
+  int L = 0, pt = 1;
+  if (p.row_seq != nullptr) {
+    const int seq = const_load(p.row_seq + row);
+    if ((unsigned)seq < (unsigned)p.num_seqs) {
+      const int qlen = const_load(p.q_lens + seq);
+      L = const_load(p.ctx_lens + seq) - qlen + (row - const_load(p.q_start + seq)) + 1;
+      pt = qlen > p.small_q ? p.chunk_part_tokens : p.part_tokens;
+    } else {
+      merge = false;
+    }
+  } else {
+    L = const_load(p.ctx_lens + row);
+    pt = p.part_tokens;
+  }
   // new_in_merge: the partitions cover keys 0 .. L-2 (none when L is 1) and
   // key L-1 is this row's new K/V, merged here as one more partition
   const bool add_new = p.new_in_merge != 0;
   float s_new = 0.f, v_new[C];
   if (add_new) {
     // score of the new key (log2 units, as the partitions' maxima) and its
-    // value, dequantised with the scales of the block the row goes to
-    const int slot = p.slots[row];
-    const bool in_pool = slot >= 0 && (int64_t)slot < (int64_t)p.num_blocks * 16;
-    const size_t sc = in_pool ? (size_t)(slot >> 4) * p.num_kv_heads + kvh : 0;
-    const float ksc = p.kv_fp8 && in_pool ? p.k_scale[sc] : 1.f;
-    const float vsc = p.kv_fp8 && in_pool ? p.v_scale[sc] : 1.f;
+    // value, dequantised with the scales of the block the row goes to (the
+    // scales apply to the sum and to the weight, so their loads, after the
+    // slot's, overlap the row's)
+    const int slot = const_load(p.slots + row);
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + rh * D;
     const size_t nrow = (size_t)row * p.num_kv_heads + kvh;
     float dot = 0.f;
@@ -108,9 +123,7 @@ __device__ __forceinline__ void reduce_wave(const StepParams& p, int row, int h,
       const float qv = QT == kBF16 ? __uint_as_float((uint32_t)qb << 16)
                                    : (float)__builtin_bit_cast(_Float16, qb);
       float kv, vv, unused;
-      if (p.kv_fp8) {
-        // (the scales apply to the sum and to the weight below, so the loads
-        // of the slot and then the scales overlap the dot product)
+      if constexpr (FP8) {
         fp8x2_to_f32<false>(p.k_new[nrow * D + d], kv, unused);
         fp8x2_to_f32<false>(p.v_new[nrow * D + d], vv, unused);
       } else {
@@ -122,27 +135,17 @@ __device__ __forceinline__ void reduce_wave(const StepParams& p, int row, int h,
       dot = __builtin_fmaf(qv, kv, dot);
       v_new[c] = vv;
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) dot += shfl_xor_f(dot, off);
-    s_new = dot * ksc * p.scale_log2;
+    float ksc = 1.f, vsc = 1.f;
+    if constexpr (FP8) {
+      if (slot >= 0 && (int64_t)slot < (int64_t)p.num_blocks * 16) {
+        const size_t sc = (size_t)(slot >> 4) * p.num_kv_heads + kvh;
+        ksc = p.k_scale[sc];
+        vsc = p.v_scale[sc];
+      }
+    }
+    s_new = wave_sum(dot) * ksc * p.scale_log2;
 #pragma unroll
     for (int c = 0; c < C; ++c) v_new[c] *= vsc;
-  }
-  // the row's length and partition size
-  bool merge = true;
-  int L = 0, pt = 1;
-  if (p.row_seq != nullptr) {
-    const int seq = p.row_seq[row];
-    if ((unsigned)seq < (unsigned)p.num_seqs) {
-      const int qlen = p.q_lens[seq];
-      L = p.ctx_lens[seq] - qlen + (row - p.q_start[seq]) + 1;
-      pt = qlen > p.small_q ? p.chunk_part_tokens : p.part_tokens;
-    } else {
-      merge = false;
-    }
-  } else {
-    L = p.ctx_lens[row];
-    pt = p.part_tokens;
   }
   if (L < 1 || L > p.max_blocks * 16 || L > p.max_parts * pt) merge = false;
   const int nparts = merge ? ((add_new ? L - 1 : L) + pt - 1) / pt : 0;
@@ -216,13 +219,11 @@ __device__ __forceinline__ void reduce_wave(const StepParams& p, int row, int h,
     for (int c = 0; c < C; ++c)
       reinterpret_cast<uint16_t*>(p.out)[rh * D + c * 64 + lane] = to_out_bits<QT>(o[c] / ls);
   }
-  if (appends) {
-    if (p.kv_fp8) store_appended_piece<D>(p, row, kvh, lane, app);
-    else store_appended_piece<2 * D>(p, row, kvh, lane, app);
-  }
+  if (appends) store_appended_piece<FP8 ? D : 2 * D>(p, row, kvh, lane, app);
 }
 
-template <int QT, int D, int HPW>
+// E: the partials' type (bfloat16 for fp8 KV, else float32), one kernel each
+template <int QT, int D, int HPW, typename E>
 __global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
   const int ng = (p.num_q_heads + HPW - 1) / HPW;
   const int row = blockIdx.x / ng;
@@ -230,8 +231,7 @@ __global__ __launch_bounds__(64 * HPW) void split_reduce_kernel(StepParams p) {
   const int lane = threadIdx.x & 63;
   if (h >= p.num_q_heads) return;
   // one head per workgroup on decode steps, which read partitions ahead
-  if (p.part_bf16) reduce_wave<QT, D, uint16_t, HPW == 1>(p, row, h, lane);
-  else reduce_wave<QT, D, float, HPW == 1>(p, row, h, lane);
+  reduce_wave<QT, D, E, HPW == 1>(p, row, h, lane);
 }
 
 // inclusive scan of v over the 1024 threads of the workgroup
@@ -467,16 +467,22 @@ hipError_t launch_decode(const StepParams& p, const StepPlan& plan, hipStream_t 
   return hipErrorInvalidValue;
 }
 
+template <int HPW, typename E>
+void reduce_launch(const StepParams& p, const StepPlan& plan, dim3 grid, dim3 block, hipStream_t stream) {
+  if (plan.q_dtype == kBF16) {
+    if (plan.head_dim == 128) hipLaunchKernelGGL((split_reduce_kernel<kBF16, 128, HPW, E>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((split_reduce_kernel<kBF16, 64, HPW, E>), grid, block, 0, stream, p);
+  } else {
+    if (plan.head_dim == 128) hipLaunchKernelGGL((split_reduce_kernel<kF16, 128, HPW, E>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((split_reduce_kernel<kF16, 64, HPW, E>), grid, block, 0, stream, p);
+  }
+}
+
 template <int HPW>
 void reduce_typed(const StepParams& p, const StepPlan& plan, dim3 grid, hipStream_t stream) {
   const dim3 block(64 * HPW);
-  if (plan.q_dtype == kBF16) {
-    if (plan.head_dim == 128) hipLaunchKernelGGL((split_reduce_kernel<kBF16, 128, HPW>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((split_reduce_kernel<kBF16, 64, HPW>), grid, block, 0, stream, p);
-  } else {
-    if (plan.head_dim == 128) hipLaunchKernelGGL((split_reduce_kernel<kF16, 128, HPW>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((split_reduce_kernel<kF16, 64, HPW>), grid, block, 0, stream, p);
-  }
+  if (p.part_bf16) reduce_launch<HPW, uint16_t>(p, plan, grid, block, stream);
+  else reduce_launch<HPW, float>(p, plan, grid, block, stream);
 }
 
 hipError_t launch_reduce(const StepParams& p, const StepPlan& plan, hipStream_t stream) {

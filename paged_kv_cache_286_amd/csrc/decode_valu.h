@@ -171,7 +171,7 @@ __device__ __forceinline__ void store_appended_piece(const StepParams& p, int ro
   constexpr int LPR = ROWB / 16;
   GlobalU32x4* dst_k = global_uniform(p.k_pool);
   GlobalU32x4* dst_v = global_uniform(p.v_pool);
-  const int slot = uniform_load(p.slots + row);
+  const int slot = const_load(p.slots + row);
   if (lane < 2 * LPR && slot >= 0 && (int64_t)slot < (int64_t)p.num_blocks * 16) {
     const bool is_v = lane >= LPR;
     const int piece = lane - (is_v ? LPR : 0);

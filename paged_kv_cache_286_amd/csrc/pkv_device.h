@@ -118,6 +118,13 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& a, float& b) {
 __device__ __forceinline__ int uniform_load(const int32_t* ptr) {
   return __builtin_amdgcn_readfirstlane(*ptr);
 }
+// An int that no running kernel writes, at an address every lane holds alike:
+// read through the constant address space, so it is a scalar load whatever
+// the kernel stores elsewhere (a vector load would be waited for together
+// with every vector load in flight)
+__device__ __forceinline__ int const_load(const int32_t* ptr) {
+  return *(const __attribute__((address_space(4))) int32_t*)ptr;
+}
 // a pointer every lane holds alike, in scalar registers
 template <typename T>
 __device__ __forceinline__ T* uniform_ptr(T* ptr) {
@@ -268,6 +275,11 @@ __device__ __forceinline__ float sum_xor16(float v) {
 __device__ __forceinline__ float sum_xor32(float v) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
   return __int_as_float(p[0]) + __int_as_float(p[1]);
+}
+// sum over the 64 lanes of a fully active wave, in every lane (the same
+// order of additions in every lane)
+__device__ __forceinline__ float wave_sum(float v) {
+  return sum_xor32(sum_xor16(group_sum<16>(v)));
 }
 
 }  // namespace pkv
