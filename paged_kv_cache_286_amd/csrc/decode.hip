@@ -13,12 +13,11 @@
 //           sequence (only sequences with one query row; prefill chunks go to
 //           the MFMA chunk kernel) -- one dimension, so the sequence count is
 //           not held to grid.y's 65,535,
-//   grid.y  split-context partition of part_tokens tokens.
+//   grid.y  split-context partition of part_tokens tokens, in the order
+//           set by dispatch_part.
 // The hardware deals workgroups to the 8 XCDs round-robin by linear id, so the
 // fastest grid dimension must not be one along which the work per workgroup
-// changes: heads (equal work) go first and partitions (the last ones are often
-// empty) go last, which also dispatches every row's heavy first partitions
-// before the light tail ones.
+// changes: heads (equal work) go first and partitions go last.
 // Inside a workgroup wave w takes blocks w, w+NW, ... of the partition.  A
 // (block, kv head) of K is block_size * head_dim contiguous elements, so one
 // wave-wide 16-byte load covers RPL whole token rows with no gaps: lane l
@@ -40,7 +39,7 @@ template <int KV, int QT, int D, int GB, bool FUSED>
 __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(StepParams p) {
   const int nx = p.num_q_heads / GB;
   const int seq = blockIdx.x / nx;
-  decode_valu_wg<KV, QT, D, GB, FUSED>(p, blockIdx.x - seq * nx, seq, blockIdx.y);
+  decode_valu_wg<KV, QT, D, GB, FUSED>(p, blockIdx.x - seq * nx, seq, dispatch_part(p));
 }
 
 // Merge the partitions of every (row, query head) whose context was split.

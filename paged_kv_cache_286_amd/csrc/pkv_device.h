@@ -118,6 +118,17 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& a, float& b) {
 __device__ __forceinline__ int uniform_load(const int32_t* ptr) {
   return __builtin_amdgcn_readfirstlane(*ptr);
 }
+// The split-context partition a decode launch's workgroup takes from its
+// grid.y.  Partition q exists only for rows longer than q partitions, so the
+// work per partition index falls as the index grows: dispatched last-first,
+// the launch ends on partition 0, which every row has, and the chip stays
+// filled to the end (dispatched first-first it ended on the few longest rows'
+// last partitions, most slots idle).  Steps with a shared-prefix hint keep
+// first-first, which measured faster for them.
+__device__ __forceinline__ int dispatch_part(const StepParams& p) {
+  return p.shared_blocks != nullptr ? (int)blockIdx.y : (int)(gridDim.y - 1 - blockIdx.y);
+}
+
 // An int that no running kernel writes, at an address every lane holds alike:
 // read through the constant address space, so it is a scalar load whatever
 // the kernel stores elsewhere (a vector load would be waited for together

@@ -1065,7 +1065,7 @@ __device__ __forceinline__ void chunk_wgs(const StepParams& p, int wg, int nwg, 
 }
 
 // Decode rows only: grid.x = kv head x column tile (fastest), then sequence;
-// grid.y = partition.
+// grid.y = partition, in the order set by dispatch_part.
 template <int KV, int QT, int D>
 __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(StepParams p) {
   __shared__ float sm_o[2 * 16 * D];
@@ -1076,7 +1076,7 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nx = p.num_kv_heads * ((p.small_q * (p.num_q_heads / p.num_kv_heads) + 15) / 16);
   const int seq = blockIdx.x / nx;
-  decode_wg<KV, QT, D>(p, blockIdx.x - seq * nx, seq, blockIdx.y, sm_o, sm_m, sm_l,
+  decode_wg<KV, QT, D>(p, blockIdx.x - seq * nx, seq, dispatch_part(p), sm_o, sm_m, sm_l,
                        sm_k + wave * 2 * TileLay<KV, D>::BLKB / 16);
 }
 
