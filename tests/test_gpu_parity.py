@@ -316,8 +316,10 @@ def test_gpu_shared_prefix_equals_copies_bitwise():
 
 @pytest.mark.parametrize("case", ["mha_bf16_valu", "gqa8_fp8_mfma", "mixed_step"])
 def test_gpu_shared_hint_only_changes_the_load_policy(case):
-    # the shared_blocks hint picks cached or streaming loads; whatever it says
-    # (right, absent, negative, past the table) the output bits stay the same
+    # the shared_blocks hint picks cached or streaming loads, and whether it is
+    # passed at all picks the order the decode launch deals the split
+    # partitions in; whatever it says (right, absent, negative, past the
+    # table) the output bits stay the same
     Hq, Hkv, kv, qd = {"mha_bf16_valu": (8, 8, W.BF16, W.BF16),
                        "gqa8_fp8_mfma": (16, 2, W.FP8, W.BF16),
                        "mixed_step": (8, 8, W.BF16, W.BF16)}[case]
