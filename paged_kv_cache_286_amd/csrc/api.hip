@@ -127,7 +127,7 @@ constexpr size_t kCheckBytes = 0;
 struct Layout {
   size_t q_start_off = 0, row_seq_off = 0, chunk_count_off = 0, chunk_entries_off = 0;
   size_t ml_off = 0, o_off = 0, total = 0;
-  int32_t part_tokens = 0, chunk_part_tokens = 0, max_parts = 0, chunk_max_parts = 0;
+  int32_t part_tokens = 0, part_head = 0, chunk_part_tokens = 0, max_parts = 0, chunk_max_parts = 0;
   int32_t chunk_capacity = 0, chunk_cols = 64, heads_per_wg = 1, small_q = 1;
   bool decode_on_mfma = false;
 };
@@ -194,7 +194,15 @@ Layout layout_for(const pkv_pool* pool, int32_t num_seqs, int32_t num_q_heads, i
       lay.decode_on_mfma ? pool->num_kv_heads * ((group + 15) / 16) : num_q_heads / lay.heads_per_wg;
   // (the tiles per kv head of small-query sequences only add columns, not blocks)
   lay.part_tokens = part_tokens_for(pool, num_seqs, wg_per_row, max_ctx);
-  lay.max_parts = (max_ctx + lay.part_tokens - 1) / lay.part_tokens;
+  // split steps whose decode rows run as MFMA tiles: a row's partition 0 is
+  // half a partition short, so the last items a decode launch deals
+  // (partition 0 of every row) are short ones and the launch's tail is short.
+  // The MFMA items are long (fp8: 4,096 tokens) on half the VALU kernel's
+  // slots; the VALU decode's items are short already, and there the extra
+  // partition of each row cost more than the shorter tail saved.  Unsplit
+  // steps stay unsplit.
+  lay.part_head = lay.decode_on_mfma && max_ctx > lay.part_tokens ? (lay.part_tokens / 2) & ~15 : 0;
+  lay.max_parts = (max_ctx + lay.part_head + lay.part_tokens - 1) / lay.part_tokens;
   size_t off = kCheckBytes;
   if (max_q > 1) {
     lay.small_q = lay.decode_on_mfma ? small_q_for(group) : 1;
@@ -547,6 +555,7 @@ static int attn_step(const pkv_pool* pool, const void* q, int32_t q_dtype, int32
   p.total_q = total_q_tokens;
   p.max_parts = lay.max_parts;
   p.part_tokens = lay.part_tokens;
+  p.part_head = lay.part_head;
   p.chunk_part_tokens = multi ? lay.chunk_part_tokens : lay.part_tokens;
   p.chunk_max_parts = lay.chunk_max_parts;
   p.chunk_capacity = lay.chunk_capacity;

@@ -88,19 +88,21 @@ __device__ __forceinline__ void reduce_wave(const StepParams& p, int row, int h,
   }
   // the row's length and partition size
   bool merge = true;
-  int L = 0, pt = 1;
+  int L = 0, pt = 1, ph = 0;
   if (p.row_seq != nullptr) {
     const int seq = const_load(p.row_seq + row);
     if ((unsigned)seq < (unsigned)p.num_seqs) {
       const int qlen = const_load(p.q_lens + seq);
       L = const_load(p.ctx_lens + seq) - qlen + (row - const_load(p.q_start + seq)) + 1;
       pt = qlen > p.small_q ? p.chunk_part_tokens : p.part_tokens;
+      ph = qlen > p.small_q ? 0 : p.part_head;
     } else {
       merge = false;
     }
   } else {
     L = const_load(p.ctx_lens + row);
     pt = p.part_tokens;
+    ph = p.part_head;
   }
   // new_in_merge: the partitions cover keys 0 .. L-2 (none when L is 1) and
   // key L-1 is this row's new K/V, merged here as one more partition
@@ -146,8 +148,8 @@ __device__ __forceinline__ void reduce_wave(const StepParams& p, int row, int h,
 #pragma unroll
     for (int c = 0; c < C; ++c) v_new[c] *= vsc;
   }
-  if (L < 1 || L > p.max_blocks * 16 || L > p.max_parts * pt) merge = false;
-  const int nparts = merge ? ((add_new ? L - 1 : L) + pt - 1) / pt : 0;
+  if (L < 1 || L > p.max_blocks * 16 || L + ph > p.max_parts * pt) merge = false;
+  const int nparts = merge ? part_count(add_new ? L - 1 : L, pt, ph) : 0;
   if (nparts <= 1 && !add_new) merge = false;
   if (merge) {
     const float m_first = lane < nparts ? ml0.x : -__builtin_inff();

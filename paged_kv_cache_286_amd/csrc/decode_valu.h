@@ -214,8 +214,9 @@ __device__ __forceinline__ void decode_valu_wg(const StepParams& p, int hx, int 
   // load their pieces before the walk and use them after it.
   static_assert(!FUSED || KV != kFP8, "the append goes into 16-bit decode launches only");
   const int L = p.ctx_lens[seq];
-  const int tok0 = part * p.part_tokens;
-  const bool bad = tok0 >= L || L > p.max_blocks * 16 || L > p.max_parts * p.part_tokens;
+  const int tok0 = part_begin(part, p.part_tokens, p.part_head);
+  const int tok_end = part_end(part, p.part_tokens, p.part_head);
+  const bool bad = tok0 >= L || L > p.max_blocks * 16 || L + p.part_head > p.max_parts * p.part_tokens;
   bool writer = false, has_new = false;
   uint4 kn = make_uint4(0, 0, 0, 0), vn = make_uint4(0, 0, 0, 0);
   // each wave's copy of the new row (K, then V; lane l's piece at [l]), which
@@ -223,8 +224,8 @@ __device__ __forceinline__ void decode_valu_wg(const StepParams& p, int hx, int 
   __shared__ uint4 sm_new[FUSED ? kWaves : 1][2][64];
   if constexpr (FUSED) {
     writer = !p.append_in_merge && part == 0 && hx % (group / GB) == 0 && wave == 0;
-    const int walked = max(0, min(L + 14, tok0 + p.part_tokens) / 16 - tok0 / 16);   // blocks of [tok0, L-1)
-    has_new = !bad && wave == walked % kWaves && L - 1 >= tok0 && L - 1 < tok0 + p.part_tokens;
+    const int walked = max(0, min(L + 14, tok_end) / 16 - tok0 / 16);   // blocks of [tok0, L-1)
+    has_new = !bad && wave == walked % kWaves && L - 1 >= tok0 && L - 1 < tok_end;
     // (LDS-destination buffer loads issued by every wave, moving bytes only
     // where needed: a branch around them would leave the compiler unsure, at
     // the block loop, which loads are still in flight)
@@ -265,11 +266,11 @@ __device__ __forceinline__ void decode_valu_wg(const StepParams& p, int hx, int 
     }
     return;
   }
-  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+  const int nparts = part_count(L, p.part_tokens, p.part_head);
   // tokens read from the pool (position L-1 comes from k_new / v_new when fused)
   const int Lw = FUSED ? L - 1 : L;
   const int blk_begin = tok0 >> 4;
-  const int blk_end = min((Lw + 15) >> 4, (tok0 + p.part_tokens) >> 4);
+  const int blk_end = min((Lw + 15) >> 4, tok_end >> 4);
 
   // block table entries of this wave's blocks (blk_begin + wave + kWaves * i)
   const int32_t* trow = p.tables + (size_t)seq * p.max_blocks;

@@ -83,6 +83,7 @@ struct StepParams {
   int32_t total_q;
   int32_t max_parts;         // partition slots per (row, head) in the partial buffers
   int32_t part_tokens;       // tokens per split-context partition of a decode row (multiple of 16)
+  int32_t part_head;         // tokens a decode row's partition 0 is short by (multiple of 16, < part_tokens)
   int32_t chunk_part_tokens; // tokens per partition of a prefill-chunk row (multiple of 16)
   int32_t chunk_max_parts;   // partitions the chunk kernel walks per entry and kv head
   int32_t chunk_capacity;    // room for chunk entries in the workspace
@@ -118,6 +119,17 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& a, float& b) {
 __device__ __forceinline__ int uniform_load(const int32_t* ptr) {
   return __builtin_amdgcn_readfirstlane(*ptr);
 }
+// Split-context partition q of a row covers keys [part_begin, part_end) of
+// its context: partitions of pt keys, the first h keys short (h = part_head
+// for decode rows, 0 for prefill-chunk rows), so that the partitions a decode
+// launch deals last (partition 0, which every row has) are the short ones.
+__device__ __forceinline__ int part_begin(int q, int pt, int h) { return q == 0 ? 0 : q * pt - h; }
+__device__ __forceinline__ int part_end(int q, int pt, int h) { return (q + 1) * pt - h; }
+// partitions of a row whose partitions cover `keys` keys (none for none)
+__device__ __forceinline__ int part_count(int keys, int pt, int h) {
+  return keys > 0 ? (keys + h + pt - 1) / pt : 0;
+}
+
 // The split-context partition a decode launch's workgroup takes from its
 // grid.y.  Partition q exists only for rows longer than q partitions, so the
 // work per partition index falls as the index grows: dispatched last-first,

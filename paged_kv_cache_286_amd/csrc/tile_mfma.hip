@@ -253,7 +253,7 @@ struct BlockRegs {
 };
 
 struct TileItem {
-  int seq, kvh, col0, ncols, part, part_tokens, L, Q, row0, max_parts;
+  int seq, kvh, col0, ncols, part, part_tokens, part_head, L, Q, row0, max_parts;
 };
 
 // One work item for the whole workgroup.  SPLIT (decode rows): the item is
@@ -294,8 +294,8 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   const int min_pos = it.L - it.Q + wcol0 / group;        // positions rise with the column
   const int last_col = min(wcol0 + 16 * TPW - 1, it.ncols - 1);
   const int max_pos = it.L - it.Q + last_col / group;
-  const int tok0 = it.part * it.part_tokens;
-  const int tok1 = min(tok0 + it.part_tokens, max_pos + 1);
+  const int tok0 = part_begin(it.part, it.part_tokens, it.part_head);
+  const int tok1 = min(part_end(it.part, it.part_tokens, it.part_head), max_pos + 1);
   const int blk_begin = tok0 >> 4;
   const int blk_end = (tok1 + 15) >> 4;
 
@@ -361,7 +361,8 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
   const int cnt = nb > first ? (nb - first + stride - 1) / stride : 0;   // <= 256 (partition <= 4096)
   // prefill items: the blocks the workgroup stages, up to its last column's limit
   const int item_max_pos = it.L - it.Q + (it.ncols - 1) / group;
-  const int cnt_item = max(0, ((min(tok0 + it.part_tokens, item_max_pos + 1) + 15) >> 4) - blk_begin);
+  const int cnt_item =
+      max(0, ((min(part_end(it.part, it.part_tokens, it.part_head), item_max_pos + 1) + 15) >> 4) - blk_begin);
   const int tbl_cnt = SPLIT ? cnt : cnt_item;
   // Table entries (and fp8 scales) of the wave's blocks, read per block with
   // readlane.  Loading them up front keeps scalar loads out of the block loop:
@@ -949,7 +950,7 @@ __device__ __forceinline__ void tile_item(const StepParams& p, const TileItem& i
     // this wave holds its columns' result over the partition: write it out
     if (!col_ok[t] || pos[t] < tok0) continue;     // no key of this partition is visible
     const size_t rh = (size_t)row[t] * p.num_q_heads + head[t];
-    const int nparts = (pos[t] + it.part_tokens) / it.part_tokens;   // ceil((pos + 1) / pt)
+    const int nparts = part_count(pos[t] + 1, it.part_tokens, it.part_head);
     if (nparts == 1 && !p.new_in_merge) {
       const float inv = 1.f / lsum[t];
       uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + rh * D;
@@ -1004,6 +1005,7 @@ __device__ __forceinline__ void decode_wg(const StepParams& p, int x, int seq, i
   it.col0 = (x % tiles) * 16;
   it.part = part;
   it.part_tokens = p.part_tokens;
+  it.part_head = p.part_head;
   it.max_parts = p.max_parts;
   it.Q = 1;
   if (p.q_start != nullptr) {
@@ -1017,10 +1019,10 @@ __device__ __forceinline__ void decode_wg(const StepParams& p, int x, int seq, i
   it.ncols = it.Q * group;
   if (it.col0 >= it.ncols) return;
   it.L = uniform_load(p.ctx_lens + it.seq);
-  if (it.Q > it.L || it.L > p.max_blocks * 16 || it.L > p.max_parts * it.part_tokens) return;
+  if (it.Q > it.L || it.L > p.max_blocks * 16 || it.L + it.part_head > p.max_parts * it.part_tokens) return;
   // the merge launch adds key L-1 (this step's new row) from k_new / v_new
   if (p.new_in_merge) it.L -= 1;
-  if (it.Q > it.L || it.part * it.part_tokens >= it.L) return;
+  if (it.Q > it.L || part_begin(it.part, it.part_tokens, it.part_head) >= it.L) return;
   tile_item<KV, QT, D, true>(p, it, group, sm_o, sm_m, sm_l, nullptr, nullptr, nullptr, nullptr, kst);
 }
 
@@ -1048,6 +1050,7 @@ __device__ __forceinline__ void chunk_wgs(const StepParams& p, int wg, int nwg, 
     it.kvh = rem / p.chunk_max_parts;
     it.part = rem - it.kvh * p.chunk_max_parts;
     it.part_tokens = p.chunk_part_tokens;
+    it.part_head = 0;
     it.max_parts = p.max_parts;
     if ((unsigned)it.seq >= (unsigned)p.num_seqs) continue;
     it.Q = uniform_load(p.q_lens + it.seq);
