@@ -169,8 +169,10 @@ size_t paged_attn_workspace_bytes(const pkv_pool* pool, int32_t num_seqs, int32_
  * Slots of a block past context_lens[i] are never mixed into the result, whatever
  * they hold (they are masked by selection, not by multiplying with zero).
  * PKV_ERR_UNSUPPORTED when one row's split-context partials over all heads
- * (num_q_heads * ceil(max_context_len / partition) * head_dim float32) would
- * pass 2^31 bytes. */
+ * (num_q_heads * partitions * head_dim float32, partitions =
+ * ceil(max_context_len / partition), one more where split decode rows run as
+ * MFMA tiles, whose partition 0 is half a partition long) would pass 2^31
+ * bytes. */
 int paged_attn_step(const pkv_pool* pool,
                     const void* q, int32_t q_dtype, int32_t num_q_heads,
                     const void* k_pool, const void* v_pool,
@@ -223,7 +225,9 @@ int paged_append_attn_step(const pkv_pool* pool, void* k_pool, void* v_pool,
 /* pkv_set_plan_override -- force parts of the launch plan that the library
  * otherwise derives from the host scalars of a step (a testing and tuning
  * hook: every choice gives the same results up to rounding order).
- *   part_tokens        tokens per split-context partition of decode rows;
+ *   part_tokens        tokens per split-context partition of decode rows (where
+ *                      split decode rows run as MFMA tiles, partition 0 holds
+ *                      half that, rounded down to a multiple of 16);
  *   chunk_part_tokens  tokens per partition of prefill-chunk rows;
  *                      each 0 (library's choice) or a multiple of 16 in [16, 4096];
  *   small_q            sequences with query_len <= small_q run as decode items
